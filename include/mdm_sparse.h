@@ -1,0 +1,198 @@
+/*
+ * mdm_sparse.h - C ABI of the sparse masked-diffusion sampling step (HIP, gfx950).
+ *
+ * One sampling step of Sparse-LaViDa (arXiv 2512.14008) processes only a small
+ * query set: the tokens decoded at the previous step (they enter the KV cache
+ * now), the masked positions chosen for decoding at this step, and R register
+ * tokens placed after the end of the sequence; logits are produced only for
+ * the decoded subset (papernotes.org reading notes, page 1: overall framework,
+ * key designs 1-3 and the worked example = the paper's Figure 3; paperlayer.ai
+ * summary, section 3.2).
+ *
+ * The model behind these calls is one attention layer whose query/key/value
+ * rows are looked up by token id in folded tables (embedding times projection),
+ * rotated by RoPE at each row's explicit position id; h is the concatenation of
+ * the head outputs and the logits are h W^T.  Token ids: 0..V-1 vocabulary,
+ * V = the mask token, V+1..V+R the registers.  Positions are 0-indexed; the
+ * registers sit at seq_len .. seq_len+R-1.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees device memory and keeps no pointer beyond the
+ *    buffers registered at init.  It allocates only the host-side context.
+ *  - Every compute call is an asynchronous enqueue on the context's stream and
+ *    returns after validating its arguments on the host; results are valid
+ *    once that stream has been synchronised.  On any error nothing is enqueued.
+ *  - "bf16" arrays hold bfloat16 bit patterns (uint16); "elem" means bf16 in
+ *    MDM_BF16 precision and fp32 in MDM_FP32 precision.
+ *  - A context is not thread-safe; use one context per stream.
+ *  - Token ids and positions in device arrays are range-checked by the
+ *    kernels: an out-of-range value is replaced by 0 for addressing and sets a
+ *    sticky flag that mdm_device_status() reports as MDM_E_DEVICE.
+ */
+#ifndef MDM_SPARSE_H
+#define MDM_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MDM_OK = 0,
+  MDM_E_ARG = -1,          /* null pointer, bad enum or out-of-range scalar           */
+  MDM_E_SHAPE = -2,        /* sizes inconsistent with the config or the buffers      */
+  MDM_E_CAPACITY = -3,     /* the KV cache (or the transient tail) would overflow     */
+  MDM_E_HIP = -4,          /* a HIP runtime call failed (see mdm_last_error)          */
+  MDM_E_UNSUPPORTED = -5,  /* a shape this build does not implement                   */
+  MDM_E_DEVICE = -6        /* a kernel met an out-of-range token id or position       */
+} mdm_status;
+
+typedef enum {
+  MDM_BF16 = 0,            /* bf16 storage, bf16 MFMA with fp32 accumulation          */
+  MDM_FP32 = 1             /* fp32 storage and arithmetic (validation mode)           */
+} mdm_precision;
+
+typedef enum {
+  MDM_SELECT_ORDER = 0,       /* pre-generated order: unmask every candidate           */
+  MDM_SELECT_CONFIDENCE = 1   /* unmask the n_select most confident candidates         */
+} mdm_select_mode;
+
+typedef struct mdm_ctx mdm_ctx;   /* opaque host-side context */
+
+typedef struct {
+  int32_t batch;          /* B independent sequences, same per-step counts           */
+  int32_t n_heads;        /* H query heads                                            */
+  int32_t n_kv_heads;     /* H_kv key/value heads; H % H_kv == 0; query head h uses   */
+                          /* key/value head h / (H / H_kv)                            */
+  int32_t head_dim;       /* d: 64 or 128                                             */
+  int32_t vocab;          /* V                                                        */
+  int32_t seq_len;        /* total length of the sequence (prompt + generated)       */
+  int32_t n_registers;    /* R, 0..256                                                */
+  int32_t max_decode;     /* upper bound on n_decode per step (sizes the workspace)  */
+  int32_t precision;      /* mdm_precision                                            */
+  int32_t accurate_conf;  /* bf16 only: nonzero splits h into bf16 hi + lo for the    */
+                          /* vocab screening, so confidences are accurate enough to   */
+                          /* rank; zero screens with bf16(h) (argmax still exact)     */
+  double rope_theta;      /* RoPE base (10000)                                        */
+} mdm_config;
+
+typedef struct {
+  const void* tq;         /* elem [V+1+R][H*d]    folded query table, row = token id  */
+  const void* tk;         /* elem [V+1+R][H_kv*d] folded key table                    */
+  const void* tv;         /* elem [V+1+R][H_kv*d] folded value table                  */
+  const void* w_vocab;    /* elem [V][H*d]        vocabulary head                     */
+  void* k_cache;          /* elem [B][H_kv][slots][d]   RoPE'd keys, append order     */
+  void* v_cache;          /* elem [B][H_kv][d][slots]   values, transposed            */
+  int32_t* cache_pos;     /* [B][slots] position id of each cached slot               */
+  int32_t* cache_tok;     /* [B][slots] token id of each cached slot                  */
+  void* workspace;        /* scratch, at least mdm_workspace_bytes() bytes, 256-aligned */
+  size_t workspace_bytes;
+} mdm_buffers;
+
+/* Slots per (sequence, key/value head) in the cache buffers: seq_len + R rounded
+ * up to a multiple of 64.  Returns 0 for an invalid config. */
+size_t mdm_cache_slots(const mdm_config* cfg);
+
+/* Bytes of workspace the context needs (RoPE table, partial results).  0 if invalid. */
+size_t mdm_workspace_bytes(const mdm_config* cfg);
+
+/* Bytes per element of tables, caches and the vocab head (2 or 4).  0 if invalid. */
+size_t mdm_element_bytes(const mdm_config* cfg);
+
+/* Create a context (page 3, section 3.2: the cache starts empty and the prompt
+ * is prefetched into it by mdm_kv_append).  Validates cfg and the buffers,
+ * builds the fp32 RoPE table (cos/sin of pos * base^(-2i/d) evaluated in double,
+ * rounded to fp32) on the host and uploads it to the workspace, clears the
+ * device error flag, and synchronises the stream once.  `stream` is a
+ * hipStream_t (NULL = the default stream).  On success *ctx owns a host
+ * allocation released by mdm_sparse_step_destroy. */
+mdm_status mdm_sparse_step_init(mdm_ctx** ctx, const mdm_config* cfg, const mdm_buffers* buf,
+                                void* stream);
+
+/* Change the stream later calls enqueue on (e.g. a graph-capture stream). */
+mdm_status mdm_set_stream(mdm_ctx* ctx, void* stream);
+
+/* Append n rows to every sequence's KV cache (page 3, section 3.2: the prompt is
+ * prefetched; the tokens decoded at step k-1 enter the cache before step k).
+ * Row r of sequence b has token id tok[b*stride + r] and position pos[b*stride + r];
+ * its key is Tk[id] rotated by RoPE at pos, its value Tv[id]; both are written
+ * to slot len+r, with (pos, id) recorded in cache_pos / cache_tok.  The host
+ * cache length becomes len + n.  stride 0 means n.  MDM_E_CAPACITY if
+ * len + n > seq_len.  n == 0 is a no-op. */
+mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, int64_t stride,
+                         int32_t n);
+
+/* Step attention under the step-causal mask (page 1, worked example = Figure 3;
+ * page 1, key design 3).  The query set of every sequence is, in this order:
+ *   n_new_cached rows D (token d_tok, position d_pos) - the rows the preceding
+ *     mdm_kv_append committed; they see the cache (which includes themselves);
+ *   n_decode rows C (the mask token at positions c_pos[b*c_stride + i]);
+ *   R register rows (ids V+1.., positions seq_len..);
+ * C and R rows see the cache plus all C and R rows.  Keys/values of the C and R
+ * rows are written to the transient slots [len, len+n_decode+R), never
+ * committed.  Queries are rotated at their own positions.  Output
+ * out[b][i][h*d + j] (fp32, [B][n_q][H*d], n_q = n_new_cached + n_decode + R) is
+ * the attention output of row i, head h.  Strides of 0 mean compact.
+ * MDM_E_CAPACITY if len + n_decode > seq_len; MDM_E_ARG if n_new_cached > len
+ * or n_decode > max_decode. */
+mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t* d_pos,
+                              int64_t d_stride, int32_t n_new_cached, const int32_t* c_pos,
+                              int64_t c_stride, int32_t n_decode, float* out);
+
+/* Logits for the decoded subset only, with confidence and argmax (page 1, key
+ * design 1: only the positions being decoded need logits; page 3, section 3.2).
+ * Row c of sequence b is h[b*h_batch_stride + c*H*d .. +H*d) (fp32).  For every
+ * row: token = the lowest index of the largest logit, conf = the largest
+ * softmax probability (temperature 1).  The bf16 path screens all logits with a
+ * bf16 MFMA product, keeps the 4 best candidates per row and re-scores them
+ * exactly in fp32 from the fp32 h; the fp32 path computes all logits in fp32.
+ * conf, token: [B][n_decode].  logits_or_null: if non-NULL, receives the
+ * screened logits [B][n_decode][V] (fp32). */
+mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_batch_stride,
+                                        int32_t n_decode, float* conf, int32_t* token,
+                                        float* logits_or_null);
+
+/* Unmasking after a step (page 3, section 3.2).  Candidates i of sequence b:
+ * position cand_pos[b*cand_stride + i], decided token token[b*n_cand + i],
+ * confidence conf[b*n_cand + i].
+ *   MDM_SELECT_ORDER: n_select must equal n_cand; all candidates are unmasked
+ *     in the given order.
+ *   MDM_SELECT_CONFIDENCE: the n_select candidates with the largest conf (ties:
+ *     lower position first) are unmasked; they are listed in ascending
+ *     position order, and the others (still masked) are written in ascending
+ *     position order to rem_pos[b][n_cand - n_select] (may be NULL).
+ * out_tok/out_pos [B][n_select] receive the unmasked tokens and positions (the
+ * rows entering the cache at the next step); seq_tokens[b][pos] = token for
+ * each unmasked position if seq_tokens is non-NULL ([B][seq_len]). */
+mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand_stride,
+                             const float* conf, const int32_t* token, int32_t n_cand,
+                             int32_t n_select, int32_t mode, int32_t* out_tok, int32_t* out_pos,
+                             int32_t* rem_pos, int32_t* seq_tokens);
+
+/* Start a new generation: cache length 0 (the buffers are reused). */
+mdm_status mdm_sparse_step_reset(mdm_ctx* ctx);
+
+/* Current cache length (host bookkeeping), -1 for NULL. */
+int32_t mdm_cache_len(const mdm_ctx* ctx);
+
+/* Synchronise the stream, read and clear the kernels' sticky range-check flag.
+ * MDM_E_DEVICE if any kernel met an out-of-range token id or position. */
+mdm_status mdm_device_status(mdm_ctx* ctx);
+
+/* Release the host context (device buffers stay the caller's). */
+void mdm_sparse_step_destroy(mdm_ctx* ctx);
+
+/* Message of the last error on ctx ("" if none); valid until the next call. */
+const char* mdm_last_error(const mdm_ctx* ctx);
+
+/* Static name of a status code. */
+const char* mdm_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDM_SPARSE_H */

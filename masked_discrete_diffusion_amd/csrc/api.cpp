@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/mdm_sparse.h: argument and
+// capacity validation, workspace layout, cache-length bookkeeping, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mdm_sparse.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace mdm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRegisters = 256;
+constexpr int kMaxSelectCand = 1024;
+
+thread_local std::string g_last_error;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  size_t err, rope_cos, rope_sin, hhi, hlo, partials, total;
+  int m_pad, n_vt;
+};
+
+bool config_ok(const mdm_config* c, std::string* why) {
+  auto fail = [&](const char* m) { if (why) *why = m; return false; };
+  if (!c) return fail("config is NULL");
+  if (c->batch <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0) return fail("batch and head counts must be positive");
+  if (c->n_heads % c->n_kv_heads) return fail("n_heads must be a multiple of n_kv_heads");
+  if (c->vocab <= 0 || c->seq_len <= 0) return fail("vocab and seq_len must be positive");
+  if (c->n_registers < 0 || c->n_registers > kMaxRegisters) return fail("n_registers out of range");
+  if (c->max_decode <= 0 || c->max_decode > c->seq_len) return fail("max_decode out of range");
+  if (c->precision != MDM_BF16 && c->precision != MDM_FP32) return fail("unknown precision");
+  if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta)) return fail("rope_theta must be finite and > 1");
+  return true;
+}
+
+bool shape_supported(const mdm_config* c, std::string* why) {
+  if (c->head_dim != 64 && c->head_dim != 128) { if (why) *why = "head_dim must be 64 or 128"; return false; }
+  const int64_t hidden = (int64_t)c->n_heads * c->head_dim;
+  if (hidden % 64) { if (why) *why = "n_heads * head_dim must be a multiple of 64"; return false; }
+  if ((int64_t)c->vocab + 1 + c->n_registers > INT32_MAX / 2) { if (why) *why = "vocab too large"; return false; }
+  return true;
+}
+
+size_t slots_of(const mdm_config* c) { return align_up((size_t)c->seq_len + c->n_registers, kKeyTile); }
+
+Layout layout_of(const mdm_config* c) {
+  Layout L{};
+  const int hidden = c->n_heads * c->head_dim;
+  const size_t max_pos = (size_t)c->seq_len + c->n_registers;
+  L.n_vt = (c->vocab + kVocabTile - 1) / kVocabTile;
+  L.m_pad = (int)align_up((size_t)c->batch * c->max_decode, 64);
+  size_t off = 0;
+  L.err = off; off += kAlign;
+  L.rope_cos = off; off = align_up(off + max_pos * (c->head_dim / 2) * sizeof(float), kAlign);
+  L.rope_sin = off; off = align_up(off + max_pos * (c->head_dim / 2) * sizeof(float), kAlign);
+  const bool bf16 = c->precision == MDM_BF16;
+  const size_t hbytes = bf16 ? (size_t)L.m_pad * hidden * sizeof(uint16_t) : 0;
+  L.hhi = off; off = align_up(off + hbytes, kAlign);
+  L.hlo = off; off = align_up(off + ((bf16 && c->accurate_conf) ? hbytes : 0), kAlign);
+  L.partials = off; off = align_up(off + (size_t)L.m_pad * L.n_vt * 8 * sizeof(float), kAlign);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct mdm_ctx {
+  mdm_config cfg;
+  mdm_buffers buf;
+  hipStream_t stream;
+  Geometry g;
+  Layout L;
+  int len;
+  std::string err;
+  char* ws() const { return static_cast<char*>(buf.workspace); }
+};
+
+namespace {
+
+mdm_status fail(mdm_ctx* ctx, mdm_status st, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  if (ctx) ctx->err = msg;
+  g_last_error = msg;
+  return st;
+}
+
+mdm_status hip_check(mdm_ctx* ctx, hipError_t e, const char* what) {
+  if (e == hipSuccess) return MDM_OK;
+  return fail(ctx, MDM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int* err_word(mdm_ctx* c) { return reinterpret_cast<int*>(c->ws() + c->L.err); }
+const float* rope_cos(mdm_ctx* c) { return reinterpret_cast<const float*>(c->ws() + c->L.rope_cos); }
+const float* rope_sin(mdm_ctx* c) { return reinterpret_cast<const float*>(c->ws() + c->L.rope_sin); }
+
+}  // namespace
+
+extern "C" {
+
+size_t mdm_cache_slots(const mdm_config* cfg) {
+  if (!config_ok(cfg, nullptr) || !shape_supported(cfg, nullptr)) return 0;
+  return slots_of(cfg);
+}
+
+size_t mdm_workspace_bytes(const mdm_config* cfg) {
+  if (!config_ok(cfg, nullptr) || !shape_supported(cfg, nullptr)) return 0;
+  return layout_of(cfg).total;
+}
+
+size_t mdm_element_bytes(const mdm_config* cfg) {
+  if (!config_ok(cfg, nullptr)) return 0;
+  return cfg->precision == MDM_BF16 ? 2 : 4;
+}
+
+mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_buffers* buf, void* stream) {
+  if (!out) return fail(nullptr, MDM_E_ARG, "ctx out-pointer is NULL");
+  *out = nullptr;
+  std::string why;
+  if (!config_ok(cfg, &why)) return fail(nullptr, MDM_E_ARG, "invalid config: %s", why.c_str());
+  if (!shape_supported(cfg, &why)) return fail(nullptr, MDM_E_UNSUPPORTED, "unsupported shape: %s", why.c_str());
+  if (!buf) return fail(nullptr, MDM_E_ARG, "buffers are NULL");
+  if (!buf->tq || !buf->tk || !buf->tv || !buf->w_vocab || !buf->k_cache || !buf->v_cache ||
+      !buf->cache_pos || !buf->cache_tok || !buf->workspace)
+    return fail(nullptr, MDM_E_ARG, "a required buffer pointer is NULL");
+  const Layout L = layout_of(cfg);
+  if (buf->workspace_bytes < L.total)
+    return fail(nullptr, MDM_E_SHAPE, "workspace has %zu bytes, needs %zu", buf->workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(buf->workspace) % kAlign)
+    return fail(nullptr, MDM_E_ARG, "workspace must be 256-byte aligned");
+  const uintptr_t a16 = reinterpret_cast<uintptr_t>(buf->tq) | reinterpret_cast<uintptr_t>(buf->tk) |
+                        reinterpret_cast<uintptr_t>(buf->tv) | reinterpret_cast<uintptr_t>(buf->w_vocab) |
+                        reinterpret_cast<uintptr_t>(buf->k_cache) | reinterpret_cast<uintptr_t>(buf->v_cache);
+  if (a16 % 16) return fail(nullptr, MDM_E_ARG, "tables and caches must be 16-byte aligned");
+
+  mdm_ctx* ctx = new (std::nothrow) mdm_ctx();
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "out of host memory");
+  ctx->cfg = *cfg;
+  ctx->buf = *buf;
+  ctx->stream = static_cast<hipStream_t>(stream);
+  ctx->L = L;
+  ctx->len = 0;
+  Geometry& g = ctx->g;
+  g.B = cfg->batch; g.H = cfg->n_heads; g.Hkv = cfg->n_kv_heads; g.D = cfg->head_dim; g.V = cfg->vocab;
+  g.seq_len = cfg->seq_len; g.R = cfg->n_registers; g.slots = (int)slots_of(cfg);
+  g.table_rows = cfg->vocab + 1 + cfg->n_registers; g.max_pos = cfg->seq_len + cfg->n_registers;
+  g.hidden = cfg->n_heads * cfg->head_dim; g.fp32 = cfg->precision == MDM_FP32;
+
+  // RoPE table: theta_i = base^(-2i/d), angle = pos * theta_i, cos/sin in double, rounded to fp32.
+  const int half = g.D / 2;
+  std::vector<float> cs((size_t)g.max_pos * half), sn((size_t)g.max_pos * half);
+  std::vector<double> theta(half);
+  for (int i = 0; i < half; ++i) theta[i] = std::pow(cfg->rope_theta, -2.0 * i / g.D);
+  for (int p = 0; p < g.max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * theta[i];
+      cs[(size_t)p * half + i] = (float)std::cos(ang);
+      sn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+  mdm_status st = hip_check(ctx, hipMemcpyAsync(ctx->ws() + L.rope_cos, cs.data(), cs.size() * sizeof(float),
+                                                hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
+  if (st == MDM_OK)
+    st = hip_check(ctx, hipMemcpyAsync(ctx->ws() + L.rope_sin, sn.data(), sn.size() * sizeof(float),
+                                       hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
+  if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 1, ctx->stream), "clear error flag");
+  if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "init synchronize");
+  if (st != MDM_OK) {
+    delete ctx;
+    return st;
+  }
+  *out = ctx;
+  return MDM_OK;
+}
+
+mdm_status mdm_set_stream(mdm_ctx* ctx, void* stream) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  ctx->stream = static_cast<hipStream_t>(stream);
+  return MDM_OK;
+}
+
+mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, int64_t stride, int32_t n) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (n < 0) return fail(ctx, MDM_E_ARG, "n must be >= 0");
+  if (n == 0) return MDM_OK;
+  if (!tok || !pos) return fail(ctx, MDM_E_ARG, "tok and pos must be non-NULL");
+  if (stride == 0) stride = n;
+  if (stride < n) return fail(ctx, MDM_E_ARG, "stride %lld < n %d", (long long)stride, n);
+  if ((int64_t)ctx->len + n > ctx->cfg.seq_len)
+    return fail(ctx, MDM_E_CAPACITY, "cache length %d + %d exceeds seq_len %d", ctx->len, n, ctx->cfg.seq_len);
+  AppendArgs a{};
+  a.tk = ctx->buf.tk; a.tv = ctx->buf.tv; a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
+  a.cache_pos = ctx->buf.cache_pos; a.cache_tok = ctx->buf.cache_tok;
+  a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
+  a.tok = tok; a.pos = pos; a.stride = stride; a.n_a = n; a.n_reg = 0; a.slot0 = ctx->len;
+  a.err = err_word(ctx);
+  mdm_status st = hip_check(ctx, launch_append(ctx->g, a, ctx->stream), "kv_append launch");
+  if (st == MDM_OK) ctx->len += n;
+  return st;
+}
+
+mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t* d_pos, int64_t d_stride,
+                              int32_t n_new_cached, const int32_t* c_pos, int64_t c_stride, int32_t n_decode,
+                              float* out) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (!out) return fail(ctx, MDM_E_ARG, "out is NULL");
+  if (n_new_cached < 0 || n_decode < 0) return fail(ctx, MDM_E_ARG, "row counts must be >= 0");
+  if (n_new_cached > ctx->len)
+    return fail(ctx, MDM_E_ARG, "n_new_cached %d exceeds the cache length %d", n_new_cached, ctx->len);
+  if (n_decode > ctx->cfg.max_decode)
+    return fail(ctx, MDM_E_ARG, "n_decode %d exceeds max_decode %d", n_decode, ctx->cfg.max_decode);
+  if (n_new_cached > 0 && (!d_tok || !d_pos)) return fail(ctx, MDM_E_ARG, "d_tok/d_pos are NULL");
+  if (n_decode > 0 && !c_pos) return fail(ctx, MDM_E_ARG, "c_pos is NULL");
+  if (d_stride == 0) d_stride = n_new_cached;
+  if (c_stride == 0) c_stride = n_decode;
+  if (d_stride < n_new_cached || c_stride < n_decode) return fail(ctx, MDM_E_ARG, "stride smaller than row count");
+  if ((int64_t)ctx->len + n_decode > ctx->cfg.seq_len)
+    return fail(ctx, MDM_E_CAPACITY, "cache length %d + n_decode %d exceeds seq_len %d", ctx->len, n_decode,
+                ctx->cfg.seq_len);
+  const int n_r = ctx->cfg.n_registers;
+  if (n_new_cached + n_decode + n_r == 0) return MDM_OK;
+  // transient keys/values of the decoded rows and the registers
+  AppendArgs ta{};
+  ta.tk = ctx->buf.tk; ta.tv = ctx->buf.tv; ta.kc = ctx->buf.k_cache; ta.vc = ctx->buf.v_cache;
+  ta.cache_pos = nullptr; ta.cache_tok = nullptr;
+  ta.rope_cos = rope_cos(ctx); ta.rope_sin = rope_sin(ctx);
+  ta.tok = nullptr; ta.pos = c_pos; ta.stride = c_stride; ta.n_a = n_decode; ta.n_reg = n_r;
+  ta.slot0 = ctx->len; ta.err = err_word(ctx);
+  mdm_status st = hip_check(ctx, launch_append(ctx->g, ta, ctx->stream), "transient append launch");
+  if (st != MDM_OK) return st;
+  AttnArgs a{};
+  a.tq = ctx->buf.tq; a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
+  a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
+  a.d_tok = d_tok; a.d_pos = d_pos; a.d_stride = d_stride; a.c_pos = c_pos; a.c_stride = c_stride;
+  a.out = out; a.err = err_word(ctx);
+  a.n_d = n_new_cached; a.n_c = n_decode; a.n_r = n_r; a.S = ctx->len;
+  return hip_check(ctx, launch_attention(ctx->g, a, ctx->stream), "attention launch");
+}
+
+mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_batch_stride, int32_t n_decode,
+                                        float* conf, int32_t* token, float* logits_or_null) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (n_decode < 0 || n_decode > ctx->cfg.max_decode)
+    return fail(ctx, MDM_E_ARG, "n_decode %d outside [0, max_decode %d]", n_decode, ctx->cfg.max_decode);
+  if (n_decode == 0) return MDM_OK;
+  if (!h || !conf || !token) return fail(ctx, MDM_E_ARG, "h, conf and token must be non-NULL");
+  const int hidden = ctx->g.hidden;
+  if (h_batch_stride == 0) h_batch_stride = (int64_t)n_decode * hidden;
+  if (h_batch_stride < (int64_t)n_decode * hidden) return fail(ctx, MDM_E_ARG, "h_batch_stride too small");
+  if (h_batch_stride % 4 || reinterpret_cast<uintptr_t>(h) % 16)
+    return fail(ctx, MDM_E_ARG, "h must be 16-byte aligned with a stride that is a multiple of 4");
+  VocabArgs a{};
+  a.w = ctx->buf.w_vocab; a.h = h; a.h_stride = h_batch_stride; a.n_c = n_decode;
+  a.hhi = reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hhi);
+  a.hlo = (ctx->cfg.precision == MDM_BF16 && ctx->cfg.accurate_conf)
+              ? reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hlo) : nullptr;
+  a.partials = reinterpret_cast<float*>(ctx->ws() + ctx->L.partials);
+  a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
+  return hip_check(ctx, launch_vocab(ctx->g, a, ctx->stream), "vocab launch");
+}
+
+mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand_stride, const float* conf,
+                             const int32_t* token, int32_t n_cand, int32_t n_select, int32_t mode, int32_t* out_tok,
+                             int32_t* out_pos, int32_t* rem_pos, int32_t* seq_tokens) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (n_cand < 0 || n_cand > kMaxSelectCand) return fail(ctx, MDM_E_ARG, "n_cand outside [0, %d]", kMaxSelectCand);
+  if (n_select < 0 || n_select > n_cand) return fail(ctx, MDM_E_ARG, "n_select outside [0, n_cand]");
+  if (mode != MDM_SELECT_ORDER && mode != MDM_SELECT_CONFIDENCE) return fail(ctx, MDM_E_ARG, "unknown mode");
+  if (mode == MDM_SELECT_ORDER && n_select != n_cand)
+    return fail(ctx, MDM_E_ARG, "order mode unmasks every candidate (n_select must equal n_cand)");
+  if (n_cand == 0) return MDM_OK;
+  if (!cand_pos || !token || !out_tok || !out_pos) return fail(ctx, MDM_E_ARG, "a required pointer is NULL");
+  if (mode == MDM_SELECT_CONFIDENCE && !conf) return fail(ctx, MDM_E_ARG, "conf is NULL");
+  if (cand_stride == 0) cand_stride = n_cand;
+  if (cand_stride < n_cand) return fail(ctx, MDM_E_ARG, "cand_stride < n_cand");
+  SelectArgs a{};
+  a.cand_pos = cand_pos; a.cand_stride = cand_stride; a.conf = conf; a.token = token;
+  a.n_cand = n_cand; a.n_select = n_select; a.by_conf = mode == MDM_SELECT_CONFIDENCE;
+  a.out_tok = out_tok; a.out_pos = out_pos; a.rem_pos = rem_pos; a.seq_tokens = seq_tokens;
+  a.err = err_word(ctx);
+  return hip_check(ctx, launch_select(ctx->g, a, ctx->stream), "select launch");
+}
+
+mdm_status mdm_sparse_step_reset(mdm_ctx* ctx) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  ctx->len = 0;
+  return MDM_OK;
+}
+
+int32_t mdm_cache_len(const mdm_ctx* ctx) { return ctx ? ctx->len : -1; }
+
+mdm_status mdm_device_status(mdm_ctx* ctx) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  int flag = 0;
+  mdm_status st = hip_check(ctx, hipMemcpyAsync(&flag, err_word(ctx), sizeof(int), hipMemcpyDeviceToHost, ctx->stream),
+                            "read error flag");
+  if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "synchronize");
+  if (st != MDM_OK) return st;
+  if (flag) {
+    st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 1, ctx->stream), "clear error flag");
+    if (st != MDM_OK) return st;
+    return fail(ctx, MDM_E_DEVICE, "kernels met an out-of-range %s%s", (flag & kErrTok) ? "token id " : "",
+                (flag & kErrPos) ? "position" : "");
+  }
+  return MDM_OK;
+}
+
+void mdm_sparse_step_destroy(mdm_ctx* ctx) { delete ctx; }
+
+const char* mdm_last_error(const mdm_ctx* ctx) { return ctx ? ctx->err.c_str() : g_last_error.c_str(); }
+
+const char* mdm_status_string(int32_t s) {
+  switch (s) {
+    case MDM_OK: return "MDM_OK";
+    case MDM_E_ARG: return "MDM_E_ARG";
+    case MDM_E_SHAPE: return "MDM_E_SHAPE";
+    case MDM_E_CAPACITY: return "MDM_E_CAPACITY";
+    case MDM_E_HIP: return "MDM_E_HIP";
+    case MDM_E_UNSUPPORTED: return "MDM_E_UNSUPPORTED";
+    case MDM_E_DEVICE: return "MDM_E_DEVICE";
+    default: return "MDM_E_UNKNOWN";
+  }
+}
+
+}  // extern "C"

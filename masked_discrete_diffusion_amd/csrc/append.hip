@@ -1,0 +1,119 @@
+// KV append: gather key/value rows from the folded tables by token id, rotate
+// keys by RoPE at each row's explicit position id, and store them into the
+// cache (keys [slot][d]; values transposed [d][slot] so the attention kernel
+// streams them key-contiguous).  Used for committed rows (the prompt prefetch
+// and the tokens decoded at the previous step) and for the transient rows of
+// this step's masked tokens and registers (page 3, section 3.2; page 1,
+// worked example = the paper's Figure 3).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mdm {
+
+namespace {
+
+constexpr int kRowsPerBlock = 32;
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+  static __device__ float load(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+  static __device__ uint16_t from_f64(double x) { return f64_to_bf16(x); }
+};
+template <>
+struct Elem<float> {
+  static __device__ float load(const float* p, int i) { return p[i]; }
+  static __device__ float from_f64(double x) { return (float)x; }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
+  constexpr int kEpt = D / 8;                 // elements per thread (8 threads per row)
+  __shared__ T vs[kRowsPerBlock][D + 2];
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int n_rows = a.n_a + a.n_reg;
+  const int t = threadIdx.x;
+  const int lr = t / 8, part = t % 8;
+  const int r = r0 + lr;
+  const bool valid = r < n_rows;
+
+  int id = 0, pos = 0;
+  if (valid) {
+    if (r < a.n_a) {
+      id = a.tok ? a.tok[(int64_t)b * a.stride + r] : g.V;
+      pos = a.pos[(int64_t)b * a.stride + r];
+    } else {
+      const int j = r - a.n_a;
+      id = g.V + 1 + j;
+      pos = g.seq_len + j;
+    }
+    if (id < 0 || id >= g.table_rows) { flag_error(a.err, kErrTok); id = 0; }
+    if (pos < 0 || pos >= g.max_pos) { flag_error(a.err, kErrPos); pos = 0; }
+  }
+
+  const T* tk = static_cast<const T*>(a.tk);
+  const T* tv = static_cast<const T*>(a.tv);
+  T* kc = static_cast<T*>(a.kc);
+  T* vc = static_cast<T*>(a.vc);
+  const int64_t head_base = ((int64_t)b * g.Hkv + kvh) * g.slots;
+  const int slot = a.slot0 + r;
+
+  if (valid) {
+    const T* ksrc = tk + (int64_t)id * g.Hkv * D + kvh * D + part * kEpt;
+    const T* vsrc = tv + (int64_t)id * g.Hkv * D + kvh * D + part * kEpt;
+    T* kdst = kc + (head_base + slot) * D + part * kEpt;
+    const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+    const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+#pragma unroll
+    for (int p = 0; p < kEpt / 2; ++p) {
+      double r0d, r1d;
+      rope_pair(Elem<T>::load(ksrc, 2 * p), Elem<T>::load(ksrc, 2 * p + 1), cs[p], sn[p], r0d, r1d);
+      kdst[2 * p] = Elem<T>::from_f64(r0d);
+      kdst[2 * p + 1] = Elem<T>::from_f64(r1d);
+    }
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) vs[lr][part * kEpt + e] = vsrc[e];
+    if (a.cache_pos && kvh == 0 && part == 0) {
+      a.cache_pos[(int64_t)b * g.slots + slot] = pos;
+      a.cache_tok[(int64_t)b * g.slots + slot] = id;
+    }
+  }
+  __syncthreads();
+  // transposed value store: for each d, the block's rows are consecutive slots
+  const int rows_here = min(kRowsPerBlock, n_rows - r0);
+  for (int e = t; e < D * kRowsPerBlock; e += blockDim.x) {
+    const int dd = e / kRowsPerBlock, rr = e % kRowsPerBlock;
+    if (rr < rows_here) vc[((int64_t)b * g.Hkv + kvh) * D * g.slots + (int64_t)dd * g.slots + a.slot0 + r0 + rr] = vs[rr][dd];
+  }
+}
+
+__global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s) {
+  const int n_rows = a.n_a + a.n_reg;
+  if (n_rows <= 0) return hipSuccess;
+  dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, g.Hkv, g.B);
+  if (g.fp32) {
+    if (g.D == 128) hipLaunchKernelGGL((k_append<float, 128>), grid, dim3(256), 0, s, g, a);
+    else hipLaunchKernelGGL((k_append<float, 64>), grid, dim3(256), 0, s, g, a);
+  } else {
+    if (g.D == 128) hipLaunchKernelGGL((k_append<uint16_t, 128>), grid, dim3(256), 0, s, g, a);
+    else hipLaunchKernelGGL((k_append<uint16_t, 64>), grid, dim3(256), 0, s, g, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace mdm

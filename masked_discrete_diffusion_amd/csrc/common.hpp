@@ -1,0 +1,66 @@
+// Device helpers shared by the sparse-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mdm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kKeyTile = 64;       // keys per LDS stage in attention; cache slots are a multiple
+constexpr int kVocabTile = 128;    // vocab columns per screening tile (one partial per tile)
+constexpr int kTopK = 4;           // candidates re-scored exactly per row
+
+// Error bits of the device flag word.
+constexpr int kErrTok = 1;
+constexpr int kErrPos = 2;
+
+__device__ inline void flag_error(int* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// bf16 bit pattern -> float (exact).
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16 bit pattern, round to nearest even (hardware conversion on gfx950).
+__device__ inline uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// double -> bf16 bit pattern, round to nearest even in ONE step (no detour via
+// fp32, which could round twice).  Keeps the top 7 of the 52 stored mantissa
+// bits: add just under half of the dropped 45 bits plus the kept lsb, then
+// truncate; a carry into the exponent is the correct result.  Inputs are
+// finite and in the normal range of bf16 (O(1) activations); the truncated
+// double is then exactly representable in fp32 and in bf16.
+__device__ inline uint16_t f64_to_bf16(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t lsb = (u >> 45) & 1ull;
+  u += ((1ull << 44) - 1ull) + lsb;
+  u &= ~((1ull << 45) - 1ull);
+  float f = (float)__longlong_as_double((long long)u);
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// RoPE of one interleaved pair (x0, x1) by the angle whose fp32 cos/sin are c, s.
+// Evaluated in double: x (bf16 or fp32) times c or s (fp32) is exact in double,
+// so each component rounds once; contraction into fma cannot change it.
+__device__ inline void rope_pair(float x0, float x1, float c, float s, double& r0, double& r1) {
+  const double dx0 = x0, dx1 = x1, dc = c, ds = s;
+  r0 = dx0 * dc - dx1 * ds;
+  r1 = dx0 * ds + dx1 * dc;
+}
+
+// Strict "a ranks before b" for (value, index) candidates: larger value first,
+// lower index on equal values.
+__device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+}  // namespace mdm

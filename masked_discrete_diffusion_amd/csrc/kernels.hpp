@@ -1,0 +1,88 @@
+// Launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mdm {
+
+struct Geometry {
+  int B, H, Hkv, D, V, seq_len, R;
+  int slots;        // cache slots per (sequence, kv head), multiple of kKeyTile
+  int table_rows;   // V + 1 + R
+  int max_pos;      // seq_len + R
+  int hidden;       // H * D
+  bool fp32;        // MDM_FP32 storage
+};
+
+// Rows [0, n_a): token tok[b*stride + r] (or the mask token V when tok == NULL),
+// position pos[b*stride + r].  Rows [n_a, n_a + n_reg): register r - n_a
+// (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) and transposed values to
+// slots slot0 + r; records (pos, id) when cache_pos != NULL.
+struct AppendArgs {
+  const void* tk;
+  const void* tv;
+  void* kc;
+  void* vc;
+  int32_t* cache_pos;
+  int32_t* cache_tok;
+  const float* rope_cos;
+  const float* rope_sin;
+  const int32_t* tok;
+  const int32_t* pos;
+  int64_t stride;
+  int n_a, n_reg, slot0;
+  int* err;
+};
+hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* tq;
+  const void* kc;
+  const void* vc;
+  const float* rope_cos;
+  const float* rope_sin;
+  const int32_t* d_tok;
+  const int32_t* d_pos;
+  int64_t d_stride;
+  const int32_t* c_pos;
+  int64_t c_stride;
+  float* out;
+  int* err;
+  int n_d, n_c, n_r;   // query rows: D | C | R
+  int S;               // cache length including D
+};
+hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s);
+
+struct VocabArgs {
+  const void* w;            // [V][hidden] elem
+  const float* h;           // fp32 rows: row m = (b, c) at h + b*h_stride + c*hidden
+  int64_t h_stride;
+  int n_c;                  // rows per sequence
+  uint16_t* hhi;            // [m_pad][hidden] bf16 workspace (bf16 mode)
+  uint16_t* hlo;            // [m_pad][hidden] bf16 workspace (accurate mode), or NULL
+  float* partials;          // [m_pad][n_vt][8]
+  float* logits;            // optional [M][V]
+  float* conf;              // [M]
+  int32_t* token;           // [M]
+  int m_pad;
+};
+hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
+
+struct SelectArgs {
+  const int32_t* cand_pos;
+  int64_t cand_stride;
+  const float* conf;
+  const int32_t* token;
+  int n_cand, n_select, by_conf;
+  int32_t* out_tok;
+  int32_t* out_pos;
+  int32_t* rem_pos;
+  int32_t* seq_tokens;
+  int* err;
+};
+hipError_t launch_select(const Geometry& g, const SelectArgs& a, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
+
+}  // namespace mdm

@@ -1,0 +1,413 @@
+// Logits for the decoded subset only, with max-probability confidence and
+// argmax (page 1, key design 1; page 3, section 3.2).
+//
+// 1. pack:   fp32 h rows of the decoded subset -> bf16 hi (and lo = bf16(h - hi))
+//            in a dense [m_pad][hidden] operand, zero rows past M.
+// 2. screen: z^T = W h^T on bf16 MFMA (32x32x16), one 128-column vocab tile by
+//            64 rows per block; the epilogue keeps per (row, tile) the maximum,
+//            the sum of exp(z - max) and the two best (value, index) pairs, and
+//            never writes the logits (unless asked to, for validation).
+//            fp32 mode: the same tile and epilogue with fp32 VALU products.
+// 3. merge:  per row, combine the tiles (max, sum of exp), take the kTopK best
+//            candidates, recompute their logits exactly in fp32 from the fp32 h,
+//            decide the argmax among them (lowest index on ties) and the
+//            confidence exp(z_best - M) / sum exp(z - M), with the candidates'
+//            screened terms replaced by their exact ones.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mdm {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kRowTile = 64;       // rows per screening block
+constexpr int kKChunk = 64;        // hidden elements per LDS stage
+
+struct Top2 {
+  float m;      // running maximum
+  float se;     // sum of exp(z - m)
+  float v1, v2;
+  int i1, i2;
+};
+
+__device__ inline void top2_push(Top2& t, float v, int i) {
+  if (ranks_before(v, i, t.v1, t.i1)) {
+    t.v2 = t.v1; t.i2 = t.i1; t.v1 = v; t.i1 = i;
+  } else if (ranks_before(v, i, t.v2, t.i2)) {
+    t.v2 = v; t.i2 = i;
+  }
+}
+
+__device__ inline Top2 top2_merge(const Top2& a, const Top2& b) {
+  Top2 r;
+  r.m = fmaxf(a.m, b.m);
+  r.se = (a.m == kNegInf ? 0.f : a.se * __expf(a.m - r.m)) + (b.m == kNegInf ? 0.f : b.se * __expf(b.m - r.m));
+  r.v1 = a.v1; r.i1 = a.i1; r.v2 = a.v2; r.i2 = a.i2;
+  top2_push(r, b.v1, b.i1);
+  top2_push(r, b.v2, b.i2);
+  return r;
+}
+
+__device__ inline Top2 top2_shfl_xor(const Top2& t, int mask) {
+  Top2 o;
+  o.m = __shfl_xor(t.m, mask);
+  o.se = __shfl_xor(t.se, mask);
+  o.v1 = __shfl_xor(t.v1, mask);
+  o.v2 = __shfl_xor(t.v2, mask);
+  o.i1 = __shfl_xor(t.i1, mask);
+  o.i2 = __shfl_xor(t.i2, mask);
+  return o;
+}
+
+// Fold a lane's logits into (max, sumexp, top2): values[n] with indices idx[n].
+template <int N>
+__device__ inline Top2 summarize(const float* vals, const int* idx) {
+  Top2 t;
+  t.m = kNegInf; t.se = 0.f; t.v1 = kNegInf; t.v2 = kNegInf; t.i1 = 0x7fffffff; t.i2 = 0x7fffffff;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    t.m = fmaxf(t.m, vals[e]);
+    top2_push(t, vals[e], idx[e]);
+  }
+  if (t.m != kNegInf) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) t.se += __expf(vals[e] - t.m);
+  }
+  return t;
+}
+
+__device__ inline void store_partial(float* p, const Top2& t) {
+  floatx4 a = {t.m, t.se, t.v1, __int_as_float(t.i1)};
+  floatx4 c = {t.v2, __int_as_float(t.i2), 0.f, 0.f};
+  reinterpret_cast<floatx4*>(p)[0] = a;
+  reinterpret_cast<floatx4*>(p)[1] = c;
+}
+
+// ------------------------------------------------------------------ pack --
+__global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
+  const int64_t n8 = (int64_t)a.m_pad * g.hidden / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t e0 = i * 8;
+  const int m = (int)(e0 / g.hidden);
+  const int k = (int)(e0 % g.hidden);
+  u16x8 hi = {0, 0, 0, 0, 0, 0, 0, 0}, lo = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (m < M) {
+    const int b = m / a.n_c, c = m % a.n_c;
+    const float* src = a.h + (int64_t)b * a.h_stride + (int64_t)c * g.hidden + k;
+    const floatx4 x0 = reinterpret_cast<const floatx4*>(src)[0];
+    const floatx4 x1 = reinterpret_cast<const floatx4*>(src)[1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < 4 ? x0[e] : x1[e - 4];
+      const uint16_t hb = f32_to_bf16(x);
+      hi[e] = hb;
+      lo[e] = f32_to_bf16(x - bf16_to_f32(hb));
+    }
+  }
+  reinterpret_cast<u16x8*>(a.hhi)[i] = hi;
+  if (a.hlo) reinterpret_cast<u16x8*>(a.hlo)[i] = lo;
+}
+
+// ------------------------------------------------------- screen, bf16 MFMA --
+// Block: 4 wavefronts; wave w owns vocab columns [32w, 32w+32) of the tile and
+// all 64 rows (two 32-row blocks).
+template <bool kLo>
+__global__ __launch_bounds__(256) void k_screen_bf16(Geometry g, VocabArgs a, int M) {
+  constexpr int WPAD = kKChunk + 8;
+  __shared__ __align__(16) uint16_t ws[kVocabTile * WPAD];
+  __shared__ __align__(16) uint16_t hs[kRowTile * WPAD];
+  __shared__ __align__(16) uint16_t ls[kLo ? kRowTile * WPAD : 8];
+  __shared__ Top2 red[4][kRowTile];
+
+  const int vt = blockIdx.x;
+  const int mt = blockIdx.y;
+  const int v0 = vt * kVocabTile;
+  const int m0 = mt * kRowTile;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int half = lane / 32, l32 = lane % 32;
+  const uint16_t* w = static_cast<const uint16_t*>(a.w);
+
+  floatx16 acc[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+
+  for (int k0 = 0; k0 < g.hidden; k0 += kKChunk) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < kVocabTile * kKChunk / 8; c += blockDim.x) {
+      const int vr = c / (kKChunk / 8), kc = c % (kKChunk / 8);
+      const int v = min(v0 + vr, g.V - 1);
+      *reinterpret_cast<u16x8*>(ws + vr * WPAD + kc * 8) =
+          *reinterpret_cast<const u16x8*>(w + (int64_t)v * g.hidden + k0 + kc * 8);
+    }
+    for (int c = threadIdx.x; c < kRowTile * kKChunk / 8; c += blockDim.x) {
+      const int r = c / (kKChunk / 8), kc = c % (kKChunk / 8);
+      const int64_t off = (int64_t)(m0 + r) * g.hidden + k0 + kc * 8;
+      *reinterpret_cast<u16x8*>(hs + r * WPAD + kc * 8) = *reinterpret_cast<const u16x8*>(a.hhi + off);
+      if (kLo) *reinterpret_cast<u16x8*>(ls + r * WPAD + kc * 8) = *reinterpret_cast<const u16x8*>(a.hlo + off);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kKChunk / 16; ++t) {
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(ws + (32 * wave + l32) * WPAD + 16 * t + 8 * half);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(hs + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
+        if (kLo) {
+          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(ls + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lf, acc[rb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds z for row 32rb + l32 and vocab v0 + 32w + 8jj + 4half + ii
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float vals[16];
+    int idx[16];
+    const int r = m0 + 32 * rb + l32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int jj = e / 4, ii = e % 4;
+      const int v = v0 + 32 * wave + 8 * jj + 4 * half + ii;
+      idx[e] = v;
+      vals[e] = v < g.V ? acc[rb][e] : kNegInf;
+      if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[rb][e];
+    }
+    Top2 t = summarize<16>(vals, idx);
+    t = top2_merge(t, top2_shfl_xor(t, 32));
+    if (half == 0) red[wave][32 * rb + l32] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < kRowTile) {
+    const int r = threadIdx.x;
+    Top2 t = red[0][r];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) t = top2_merge(t, red[wv][r]);
+    const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+    store_partial(a.partials + ((int64_t)(m0 + r) * n_vt + vt) * 8, t);
+  }
+}
+
+// ------------------------------------------------------------ screen, fp32 --
+// Block: 128 vocab x 32 rows; thread t owns vocab {t%32 + 32q} and rows 4(t/32)+0..3.
+__global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int M) {
+  constexpr int KC = 32;
+  constexpr int RT = 32;
+  __shared__ float ws[kVocabTile][KC + 1];
+  __shared__ float hs[RT][KC + 1];
+  const int vt = blockIdx.x, mt = blockIdx.y;
+  const int v0 = vt * kVocabTile, m0 = mt * RT;
+  const int t = threadIdx.x;
+  const int tv = t % 32, tr = t / 32;
+  const float* w = static_cast<const float*>(a.w);
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < g.hidden; k0 += KC) {
+    __syncthreads();
+    for (int c = t; c < kVocabTile * KC; c += blockDim.x) {
+      const int vr = c / KC, kk = c % KC;
+      const int v = min(v0 + vr, g.V - 1);
+      ws[vr][kk] = w[(int64_t)v * g.hidden + k0 + kk];
+    }
+    for (int c = t; c < RT * KC; c += blockDim.x) {
+      const int r = c / KC, kk = c % KC;
+      const int m = m0 + r;
+      float x = 0.f;
+      if (m < M) {
+        const int b = m / a.n_c, cc = m % a.n_c;
+        x = a.h[(int64_t)b * a.h_stride + (int64_t)cc * g.hidden + k0 + kk];
+      }
+      hs[r][kk] = x;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < KC; ++kk) {
+      float wv[4], hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[q] = ws[tv + 32 * q][kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = hs[4 * tr + i][kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(hv[i], wv[q], acc[i][q]);
+    }
+  }
+  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + 4 * tr + i;
+    float vals[4];
+    int idx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = v0 + tv + 32 * q;
+      idx[q] = v;
+      vals[q] = v < g.V ? acc[i][q] : kNegInf;
+      if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[i][q];
+    }
+    Top2 tt = summarize<4>(vals, idx);
+#pragma unroll
+    for (int mask = 1; mask < 32; mask <<= 1) tt = top2_merge(tt, top2_shfl_xor(tt, mask));
+    if (tv == 0 && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, tt);
+  }
+}
+
+// ----------------------------------------------------- merge and re-score --
+struct Cand {
+  float v;
+  int i;
+};
+
+template <typename WT>
+__device__ inline float w_elem(const WT* w, int64_t i);
+template <>
+__device__ inline float w_elem<uint16_t>(const uint16_t* w, int64_t i) { return bf16_to_f32(w[i]); }
+template <>
+__device__ inline float w_elem<float>(const float* w, int64_t i) { return w[i]; }
+
+template <typename WT>
+__global__ __launch_bounds__(64) void k_merge(Geometry g, VocabArgs a, int M) {
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+  const float* part = a.partials + (int64_t)m * n_vt * 8;
+
+  // per-lane running (max, sumexp) in double and top-K candidates
+  double lm = -1e300, lse = 0.0;
+  Cand c[kTopK];
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
+  for (int tile = lane; tile < n_vt; tile += kWave) {
+    const floatx4 p0 = reinterpret_cast<const floatx4*>(part + tile * 8)[0];
+    const floatx4 p1 = reinterpret_cast<const floatx4*>(part + tile * 8)[1];
+    const double tm = p0[0], tse = p0[1];
+    if (tm > lm) { lse = lse * exp(lm - tm) + tse; lm = tm; }
+    else lse += tse * exp(tm - lm);
+    const float cv[2] = {p0[2], p1[0]};
+    const int ci[2] = {__float_as_int(p0[3]), __float_as_int(p1[1])};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float v = cv[q];
+      int i = ci[q];
+#pragma unroll
+      for (int k = 0; k < kTopK; ++k) {
+        if (ranks_before(v, i, c[k].v, c[k].i)) {
+          const float tv = c[k].v; const int ti = c[k].i;
+          c[k].v = v; c[k].i = i; v = tv; i = ti;
+        }
+      }
+    }
+  }
+  // wave reduce (max, sumexp)
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) {
+    const double om = __shfl_xor(lm, mask), ose = __shfl_xor(lse, mask);
+    const double nm = fmax(lm, om);
+    lse = lse * exp(lm - nm) + ose * exp(om - nm);
+    lm = nm;
+  }
+  // wave top-K: K rounds of a (value desc, index asc) argmax; the winner pops.
+  Cand best[kTopK];
+  int head = 0;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    float v = head < kTopK ? c[0].v : kNegInf;
+    int i = head < kTopK ? c[0].i : 0x7fffffff;
+    // c[0] is always this lane's current best (popped entries shift down)
+    float bv = v;
+    int bi = i;
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+      const float ov = __shfl_xor(bv, mask);
+      const int oi = __shfl_xor(bi, mask);
+      if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    best[k].v = bv;
+    best[k].i = bi;
+    if (bi == i && bv == v && i != 0x7fffffff) {   // this lane held the winner: pop it
+#pragma unroll
+      for (int q = 0; q < kTopK - 1; ++q) c[q] = c[q + 1];
+      c[kTopK - 1].v = kNegInf;
+      c[kTopK - 1].i = 0x7fffffff;
+      ++head;
+    }
+  }
+  // exact fp32 re-score of the candidates from the fp32 h
+  const int b = m / a.n_c, cc = m % a.n_c;
+  const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
+  const WT* w = static_cast<const WT*>(a.w);
+  float ze[kTopK];
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    const int v = best[k].i;
+    float s = 0.f;
+    if (v >= 0 && v < g.V) {
+      const WT* wr = w + (int64_t)v * g.hidden;
+      for (int e = lane; e < g.hidden; e += kWave) s = fmaf(hrow[e], w_elem<WT>(wr, e), s);
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
+    ze[k] = (v >= 0 && v < g.V) ? s : kNegInf;
+  }
+  if (lane == 0) {
+    int tb = 0;
+#pragma unroll
+    for (int k = 1; k < kTopK; ++k)
+      if (ranks_before(ze[k], best[k].i, ze[tb], best[tb].i)) tb = k;
+    double mx = lm;
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k)
+      if (ze[k] != kNegInf) mx = fmax(mx, (double)ze[k]);
+    double tot = lse * exp(lm - mx);
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+      if (ze[k] == kNegInf) continue;
+      tot += exp((double)ze[k] - mx) - exp((double)best[k].v - mx);
+    }
+    const double conf = exp((double)ze[tb] - mx) / tot;
+    a.conf[m] = (float)conf;
+    a.token[m] = best[tb].i;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
+  const int M = g.B * a.n_c;
+  if (M <= 0) return hipSuccess;
+  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+  if (g.fp32) {
+    dim3 grid(n_vt, (M + 31) / 32);
+    hipLaunchKernelGGL(k_screen_f32, grid, dim3(256), 0, s, g, a, M);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_merge<float>), dim3(M), dim3(kWave), 0, s, g, a, M);
+    return hipGetLastError();
+  }
+  const int m_tiles = (M + kRowTile - 1) / kRowTile;
+  VocabArgs pa = a;
+  pa.m_pad = m_tiles * kRowTile;
+  const int64_t n8 = (int64_t)pa.m_pad * g.hidden / 8;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, g, pa, M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(n_vt, m_tiles);
+  if (a.hlo) hipLaunchKernelGGL((k_screen_bf16<true>), grid, dim3(256), 0, s, g, pa, M);
+  else hipLaunchKernelGGL((k_screen_bf16<false>), grid, dim3(256), 0, s, g, pa, M);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_merge<uint16_t>), dim3(M), dim3(kWave), 0, s, g, pa, M);
+  return hipGetLastError();
+}
+
+}  // namespace mdm

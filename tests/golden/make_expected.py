@@ -1,0 +1,85 @@
+"""Write the oracle's expected results for the five workloads.
+
+    python tests/golden/make_expected.py [config ...]
+
+Calls only ``oracle`` (and the shared input generator ``mdm_inputs``); the
+HIP path plays no part.  For each workload it stores, in
+``tests/golden/expected_<name>.npz``:
+
+  tokens    [B][seq_len] final sequences
+  sel_pos   [B][L] positions in the order they were unmasked
+  dec_tok   [B][sum n_C] decided token of every decoded row, step by step
+  conf      [B][sum n_C] fp32 confidence of every decoded row
+  margin    [B][sum n_C] top-1 minus top-2 logit (float64)
+  conf_gap  [steps][B] fp32 confidence gap at the top-n cut (semi-AR only)
+  o_steps   steps whose attention output rows were sampled
+  o_rows    [len(o_steps)][n_rows] sampled query-row indices (sequence 0)
+  o_vals    [len(o_steps)][n_rows][hidden] attention output (float32)
+"""
+
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from mdm_inputs import CONFIGS, get_config, make_workload  # noqa: E402
+from oracle.step import run_workload  # noqa: E402
+
+
+def sample_rows(n_d, n_c, n_r):
+    rows = [0, n_d - 1, n_d, n_d + n_c - 1, n_d + n_c, n_d + n_c + n_r - 1]
+    return sorted({r for r in rows if 0 <= r < n_d + n_c + n_r})
+
+
+def o_steps_of(cfg):
+    n = cfg.n_steps
+    return sorted({1, n // 2, n - 1})
+
+
+def expected(cfg):
+    wl = make_workload(cfg)
+    steps = o_steps_of(cfg)
+    t = time.time()
+    res = run_workload(wl, keep_steps=steps)
+    dt = time.time() - t
+    B = cfg.batch
+    sel_pos = [np.concatenate([r.c_pos[b][r.selected[b]] for r in res.records]) for b in range(B)]
+    dec_tok = [np.concatenate([r.token[b] for r in res.records]) for b in range(B)]
+    conf = [np.concatenate([r.conf32[b] for r in res.records]) for b in range(B)]
+    margin = [np.concatenate([r.margin[b] for r in res.records]) for b in range(B)]
+    gaps = np.array([[r.conf_gap[b] for b in range(B)] for r in res.records], dtype=np.float64)
+    o_rows, o_vals = [], []
+    for k in steps:
+        r = res.records[k]
+        n_d, n_c = r.d_pos[0].size, r.c_pos[0].size
+        rows = sample_rows(n_d, n_c, cfg.n_registers)
+        rows = (rows + [rows[-1]] * 6)[:6]
+        o_rows.append(rows)
+        o_vals.append(r.o[0][rows].astype(np.float32))
+    out = dict(tokens=res.tokens.astype(np.int32), sel_pos=np.stack(sel_pos).astype(np.int32),
+               dec_tok=np.stack(dec_tok).astype(np.int32), conf=np.stack(conf).astype(np.float32),
+               margin=np.stack(margin), conf_gap=gaps, o_steps=np.array(steps, dtype=np.int32),
+               o_rows=np.array(o_rows, dtype=np.int32), o_vals=np.stack(o_vals))
+    return out, dt
+
+
+def main(names):
+    cfgs = [get_config(n) for n in names] if names else list(CONFIGS)
+    for cfg in cfgs:
+        out, dt = expected(cfg)
+        path = os.path.join(HERE, f"expected_{cfg.name}.npz")
+        np.savez_compressed(path, **out)
+        print(f"{cfg.name}: oracle {dt:.1f}s, min margin {out['margin'].min():.3g}, "
+              f"min conf gap {np.nanmin(out['conf_gap']) if np.isfinite(out['conf_gap']).any() else float('nan'):.3g}"
+              f" -> {os.path.relpath(path, ROOT)}", flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -28,3 +28,33 @@ def reduced(name, **kw):
 
 def workload(cfg, tables=True):
     return make_workload(cfg, tables=tables)
+
+
+# Shapes the HIP path supports (head_dim 64/128), small enough for a live oracle,
+# ragged on purpose: key counts and row counts are not multiples of the tiles.
+def gpu_small_bf16(index=110, **kw):
+    base = dict(name="gpu_small_bf16", index=index, batch=2, n_heads=4, n_kv_heads=2, head_dim=64,
+                vocab=1000, prompt_len=40, gen_len=96, n_registers=8, n_steps=6,
+                schedule="fixed", per_step=16, order="random", precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+def gpu_small_d128(index=111, **kw):
+    base = dict(name="gpu_small_d128", index=index, batch=2, n_heads=8, n_kv_heads=8, head_dim=128,
+                vocab=700, prompt_len=70, gen_len=144, n_registers=64, n_steps=8,
+                schedule="cosine", order="stratified2d", grid=12, precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+def gpu_small_semi_ar(index=112, **kw):
+    base = dict(name="gpu_small_semi_ar", index=index, batch=3, n_heads=8, n_kv_heads=2, head_dim=128,
+                vocab=3000, prompt_len=33, gen_len=64, n_registers=5, n_steps=16,
+                schedule="semi_ar", block=16, steps_per_block=4, order="confidence", precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+def gpu_small_fp32(index=113, **kw):
+    return gpu_small_d128(index=index, name="gpu_small_fp32", precision="fp32", **kw)

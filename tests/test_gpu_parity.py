@@ -1,0 +1,205 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bars (written here, applied element by element):
+* decoded tokens, unmasked positions and their order: bit-exact;
+* bf16 path: attention outputs, confidences and screened logits within
+  2e-2 relative + 1e-2 absolute; fp32 path: 1e-5 relative + 1e-5 absolute;
+* a tighter diagnostic on attention outputs (max |err| / max |ref|) that a
+  mask bug would break even where the loose bar would not;
+* keys written to the cache: bit-exact (the RoPE rule rounds once from an
+  exact double).
+"""
+
+import numpy as np
+import pytest
+
+from mdm_inputs import make_workload
+from oracle.numerics import table_values
+from oracle.step import Model, SequenceOracle, run_workload
+from small_workloads import gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar
+from mdm_inputs import get_config
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
+TIGHT = {"bf16": 2e-4, "fp32": 1e-5}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def assert_close(got, ref, rtol, atol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    bad = ~(err <= atol + rtol * np.abs(ref))
+    assert not bad.any(), (f"{what}: {int(bad.sum())}/{bad.size} outside tolerance, "
+                           f"max abs err {np.nanmax(err):.3g}")
+    return float(np.nanmax(err)) if err.size else 0.0
+
+
+def _runner(cfg, **kw):
+    import torch
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    wl = make_workload(cfg)
+    return wl, SparseStepRunner(wl, device="cuda", **kw)
+
+
+SMALL = [gpu_small_bf16, gpu_small_d128, gpu_small_semi_ar, gpu_small_fp32,
+         lambda: get_config("c1_tiny")]
+
+
+@pytest.mark.parametrize("cfgfn", SMALL, ids=["bf16_d64", "bf16_d128", "semi_ar", "fp32_d128", "c1_tiny"])
+def test_append_keys_bit_exact(cfgfn):
+    cfg = cfgfn()
+    _say(f"append parity: {cfg.name}")
+    wl, run = _runner(cfg)
+    run.prefill()
+    import torch
+    torch.cuda.synchronize()
+    P, d, S = cfg.prompt_len, cfg.head_dim, run.slots
+    kc = run.k_cache.cpu().numpy().reshape(cfg.batch, cfg.n_kv_heads, S, d)
+    vc = run.v_cache.cpu().numpy().reshape(cfg.batch, cfg.n_kv_heads, d, S)
+    model = Model.from_workload(wl)
+    for b in range(cfg.batch):
+        seq = SequenceOracle(model, wl.prompt_ids[b])
+        seq.prefill()
+        k_ref = seq.k[0][:P]                                  # [P, Hkv, d] float64 storage values
+        v_ref = seq.v[0][:P]
+        k_gpu = table_values(kc[b].view(np.uint16) if cfg.precision == "bf16" else kc[b])[:, :P]
+        v_gpu = table_values(vc[b].view(np.uint16) if cfg.precision == "bf16" else vc[b])[:, :, :P]
+        assert np.array_equal(k_gpu.transpose(1, 0, 2), k_ref), f"keys differ (b={b})"
+        assert np.array_equal(v_gpu.transpose(2, 0, 1), v_ref), f"values differ (b={b})"
+        pos = run.cache_pos.cpu().numpy().reshape(cfg.batch, S)[b, :P]
+        tok = run.cache_tok.cpu().numpy().reshape(cfg.batch, S)[b, :P]
+        assert np.array_equal(pos, np.arange(P)) and np.array_equal(tok, wl.prompt_ids[b])
+    run.close()
+
+
+@pytest.mark.parametrize("cfgfn", SMALL, ids=["bf16_d64", "bf16_d128", "semi_ar", "fp32_d128", "c1_tiny"])
+def test_generation_matches_oracle(cfgfn):
+    cfg = cfgfn()
+    _say(f"generation parity: {cfg.name}")
+    wl, run = _runner(cfg)
+    steps = list(range(cfg.n_steps))
+    recs, seq = run.generate_recorded(keep_o=steps, keep_logits=steps)
+    run.close()
+    res = run_workload(wl, keep_steps=steps)
+    rtol, atol = TOL[cfg.precision]
+    accurate = cfg.schedule == "semi_ar"
+    worst = {"o": 0.0, "conf": 0.0, "logits": 0.0}
+    for k, (g, r) in enumerate(zip(recs, res.records)):
+        for b in range(cfg.batch):
+            assert np.array_equal(g["token"][b], r.token[b]), f"step {k} b {b}: decoded tokens differ"
+            sel = r.selected[b]
+            assert np.array_equal(g["sel_pos"][b], r.c_pos[b][sel]), f"step {k} b {b}: unmask order differs"
+            assert np.array_equal(g["sel_tok"][b], r.token[b][sel])
+            worst["conf"] = max(worst["conf"], assert_close(g["conf"][b], r.conf64[b], rtol, atol, f"conf step {k}"))
+            o_ref = r.o[b]
+            worst["o"] = max(worst["o"], assert_close(g["o"][b], o_ref, rtol, atol, f"O step {k} b {b}"))
+            rel = np.max(np.abs(g["o"][b] - o_ref)) / np.max(np.abs(o_ref))
+            assert rel <= TIGHT[cfg.precision], f"O step {k} b {b}: max err / max ref = {rel:.3g}"
+        zref = r.z if (cfg.precision == "fp32" or accurate) else r.z_mirror
+        worst["logits"] = max(worst["logits"], assert_close(
+            g["logits"].reshape(-1, cfg.vocab), zref, rtol, atol, f"logits step {k}"))
+    assert np.array_equal(seq, res.tokens), "final sequences differ"
+    _say(f"  worst abs errors: {worst}")
+
+
+def test_forbidden_keys_nan_poison():
+    """Invariant (c) on the GPU: NaN in every key/value a new row may not see
+    (this step's masked and register rows, and every slot past the visible
+    prefix) leaves the new rows' outputs finite and bit-identical."""
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    cfg = gpu_small_d128()
+    _say("nan poison: gpu_small_d128")
+    wl, run = _runner(cfg)
+    run.prefill()
+    for k in range(3):
+        run.step(k)
+    st = run.plan[3]
+    L.mdm_kv_append(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d)
+    c_ptr, c_stride = run._c_src(st)
+    n_q = st.n_d + st.n_c + cfg.n_registers
+
+    def attend():
+        L.mdm_step_attention(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d,
+                             c_ptr, c_stride, st.n_c, run.out)
+        torch.cuda.synchronize()
+        return run.out[:cfg.batch * n_q * cfg.hidden].view(cfg.batch, n_q, cfg.hidden).clone()
+
+    ref = attend()
+    nan = torch.tensor(0x7FC0, dtype=torch.int32).to(torch.int16).item()
+    forbidden = [cfg.vocab] + list(range(cfg.vocab + 1, cfg.vocab + 1 + cfg.n_registers))
+    run.tk.view(cfg.table_rows, -1)[forbidden] = nan
+    run.tv.view(cfg.table_rows, -1)[forbidden] = nan
+    s_tot = L.mdm_cache_len(run.ctx) + st.n_c + cfg.n_registers
+    kc = run.k_cache.view(cfg.batch, cfg.n_kv_heads, run.slots, cfg.head_dim)
+    vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, cfg.head_dim, run.slots)
+    kc[:, :, s_tot:] = nan
+    vc[:, :, :, s_tot:] = nan
+    got = attend()
+    n_d = st.n_d
+    assert torch.isfinite(got[:, :n_d]).all()
+    assert torch.equal(got[:, :n_d], ref[:, :n_d])
+    assert torch.isnan(got[:, n_d:]).any()          # the others do see the poisoned rows
+    run.close()
+
+
+def test_rerun_is_bitwise_deterministic():
+    cfg = gpu_small_semi_ar()
+    _say("determinism: gpu_small_semi_ar")
+    wl, run = _runner(cfg)
+    a, sa = run.generate_recorded(keep_o=[3, 9])
+    b, sb = run.generate_recorded(keep_o=[3, 9])
+    run.close()
+    assert np.array_equal(sa, sb)
+    for x, y in zip(a, b):
+        assert np.array_equal(x["conf"], y["conf"]) and np.array_equal(x["token"], y["token"])
+        if "o" in x:
+            assert np.array_equal(x["o"], y["o"])
+
+
+def test_graph_replays_match_eager():
+    import torch
+    cfg = gpu_small_d128()
+    _say("graph replay: gpu_small_d128")
+    wl, run = _runner(cfg)
+    _, eager = run.generate_recorded()
+    graph = run.capture_graph()
+    for rep in range(3):
+        run.seq_tokens.copy_(run.seq0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(run.seq_tokens.cpu().numpy(), eager), f"replay {rep}"
+        _, again = run.generate_recorded(n_steps=2)          # eager work between replays
+    run.close()
+
+
+def test_device_range_check_and_capacity():
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    cfg = gpu_small_bf16()
+    _say("range checks: gpu_small_bf16")
+    wl, run = _runner(cfg)
+    run.prefill()
+    bad_tok = torch.full((cfg.batch, 2), cfg.table_rows + 5, dtype=torch.int32, device="cuda")
+    pos = torch.full((cfg.batch, 2), cfg.prompt_len, dtype=torch.int32, device="cuda")
+    L.mdm_kv_append(run.ctx, bad_tok, pos, 2, 2)
+    with pytest.raises(L.MdmError) as e:
+        L.mdm_device_status(run.ctx)
+    assert e.value.status == L.MDM_E_DEVICE
+    L.mdm_device_status(run.ctx)                       # the flag was cleared
+    with pytest.raises(L.MdmError) as e:
+        L.mdm_kv_append(run.ctx, pos, pos, 2, cfg.seq_len)
+    assert e.value.status in (L.MDM_E_CAPACITY, L.MDM_E_ARG)
+    n_left = cfg.seq_len - L.mdm_cache_len(run.ctx)
+    with pytest.raises(L.MdmError) as e:
+        big = torch.zeros(cfg.batch * (n_left + 1), dtype=torch.int32, device="cuda")
+        L.mdm_kv_append(run.ctx, big, big, n_left + 1, n_left + 1)
+    assert e.value.status == L.MDM_E_CAPACITY
+    run.close()
