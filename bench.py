@@ -1,0 +1,247 @@
+"""Benchmark of the sparse sampling step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3_t2i_4k] [--no-cpu-baseline]
+
+A bench "step" is one whole generation of the workload: the prompt prefetch
+and all sampling steps (every step runs the full hot path: KV append, step
+attention, subset logits with confidence/argmax, unmask selection) over the
+batch.  The generation is captured once as a HIP graph; W replays warm up,
+then K replays are timed between device synchronisations.
+
+value  = tokens unmasked per second = batch * generated length * K / seconds.
+roofline: the dominant kernel is the step attention; its average launch
+          duration comes from HIP events recorded around every attention
+          launch of an eager generation on the stream the kernel runs on, and
+          its achieved TFLOP/s counts only algorithmic work (4*d per visible
+          (query, key) pair per head).  `traffic` is read from the committed
+          hardware-counter summary when it was taken on the current kernel
+          source, else null.
+cpu_baseline: the CPU oracle (float64 NumPy) timed on this host on a bounded
+          sample: sequence 0 of the same workload, from the prompt through as
+          many sampling steps as fit in the time budget.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+METRIC = "tokens unmasked/sec at 4096-tok T2I; step-attn+logits % of MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_c3_t2i_4k_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "masked_discrete_diffusion_amd", "csrc", "attention.hip")
+
+
+def attention_work(cfg, plan):
+    """Algorithmic FLOPs and HBM bytes of every attention launch."""
+    flops, nbytes = [], []
+    d, H, Hkv, B, R = cfg.head_dim, cfg.n_heads, cfg.n_kv_heads, cfg.batch, cfg.n_registers
+    esz = 2 if cfg.precision == "bf16" else 4
+    S = cfg.prompt_len
+    for st in plan:
+        S += st.n_d
+        s_tot = S + st.n_c + R
+        pairs = st.n_d * S + (st.n_c + R) * s_tot
+        flops.append(4.0 * d * pairs * H * B)
+        n_q = st.n_d + st.n_c + R
+        kv = 2.0 * S * Hkv * d * esz                      # cached K and V read once per (b, kv head)
+        tables = (n_q * H * d + 2 * (st.n_c + R) * Hkv * d) * esz
+        out = 4.0 * n_q * H * d
+        nbytes.append(B * (kv + tables + out))
+    return np.array(flops), np.array(nbytes)
+
+
+def logits_work(cfg, plan):
+    hidden, V = cfg.hidden, cfg.vocab
+    esz = 2 if cfg.precision == "bf16" else 4
+    flops = np.array([2.0 * cfg.batch * st.n_c * hidden * V for st in plan])
+    nbytes = np.array([V * hidden * esz + cfg.batch * st.n_c * hidden * 4.0 for st in plan])
+    return flops, nbytes
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(n_launch_units):
+    """Counter-derived HBM bytes per attention launch, if measured on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attention_source_sha") != source_sha(ATTN_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s):
+    from threadpoolctl import threadpool_info
+    from mdm_inputs import make_workload
+    from oracle.step import Model, SequenceOracle, step_candidates
+    from oracle.logits import decide, subset_logits
+
+    wl = make_workload(cfg)
+    model = Model.from_workload(wl)
+    t0 = time.perf_counter()
+    seq = SequenceOracle(model, wl.prompt_ids[0])
+    seq.prefill()
+    d = (np.empty(0, np.int64), np.empty(0, np.int64))
+    tokens = 0
+    steps = 0
+    for k in range(cfg.n_steps):
+        c_pos = step_candidates(wl, k, 0, {0: None})
+        out = seq.forward(d[0], d[1], c_pos)
+        tok = decide(subset_logits(out.h, model.w))[0]
+        seq.write_tokens(c_pos, tok)
+        d = (tok, c_pos)
+        tokens += c_pos.size
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence 0 of {cfg.name}: prompt prefetch + sampling steps 1..{steps} of "
+                      f"{cfg.n_steps} ({tokens} tokens) in {dt:.1f} s, float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3_t2i_4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run only this many eager generations (for profilers) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              f"(sequences shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    from mdm_inputs import get_config, make_workload
+
+    cfg = get_config(args.workload)
+    wl = make_workload(cfg)
+    run = SparseStepRunner(wl, device="cuda:0")
+    print(f"[bench] {cfg.name}: batch {cfg.batch}, {cfg.n_steps} steps, workload ready", file=sys.stderr, flush=True)
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            run.generate()
+        torch.cuda.synchronize()
+        L.mdm_device_status(run.ctx)
+        print(f"[bench] profiled {args.profile_steps} eager generations", file=sys.stderr, flush=True)
+        return
+
+    run.generate()
+    torch.cuda.synchronize()
+    L.mdm_device_status(run.ctx)
+    graph = run.capture_graph()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tokens = cfg.batch * cfg.gen_len * args.steps
+    print(f"[bench] {args.steps} graph replays in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    # per-kernel durations: HIP events around every attention / logits launch of
+    # eager generations, on the stream the kernels run on
+    stream = run.stream
+    n = len(run.plan)
+    reps = 3
+    att_ms = np.zeros(n)
+    log_ms = np.zeros(n)
+    for _ in range(reps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        run.prefill()
+        for k, st in enumerate(run.plan):
+            if st.n_d:
+                L.mdm_kv_append(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d)
+            c_ptr, c_stride = run._c_src(st)
+            ev[k][0].record(stream)
+            L.mdm_step_attention(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d,
+                                 c_ptr, c_stride, st.n_c, run.out)
+            ev[k][1].record(stream)
+            n_q = st.n_d + st.n_c + cfg.n_registers
+            h_ptr = run.out.data_ptr() + 4 * st.n_d * cfg.hidden
+            ev[k][2].record(stream)
+            L.mdm_subset_logits_confidence(run.ctx, h_ptr, n_q * cfg.hidden, st.n_c, run.conf, run.token, None)
+            ev[k][3].record(stream)
+            rem = run.rem[st.rem_out] if st.rem_out >= 0 else None
+            L.mdm_unmask_select(run.ctx, c_ptr, c_stride, run.conf, run.token, st.n_c, st.n_sel, st.mode,
+                                run.d_tok[st.out_buf], run.d_pos[st.out_buf], rem, run.seq_tokens)
+        torch.cuda.synchronize()
+        att_ms += np.array([e[0].elapsed_time(e[1]) for e in ev])
+        log_ms += np.array([e[2].elapsed_time(e[3]) for e in ev])
+    att_ms /= reps
+    log_ms /= reps
+    L.mdm_device_status(run.ctx)
+
+    a_flops, a_bytes = attention_work(cfg, run.plan)
+    l_flops, l_bytes = logits_work(cfg, run.plan)
+    att_s = att_ms.sum() / 1e3
+    achieved = a_flops.sum() / att_s / 1e12               # = mean flops per launch / mean launch time
+    traffic = load_traffic(n)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic,
+                "kernel": "k_attn_bf16<128>", "launches": n,
+                "avg_launch_us": round(att_ms.mean() * 1e3, 2),
+                "algorithmic_gflop_per_launch": round(a_flops.mean() / 1e9, 3),
+                "hbm_gbs_algorithmic": round(a_bytes.sum() / att_s / 1e9, 1)}
+    both_s = att_s + log_ms.sum() / 1e3
+    step_frac = (a_flops.sum() + l_flops.sum()) / both_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.precision == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "prompt_tokens": cfg.prompt_len,
+                   "image_tokens": cfg.gen_len, "registers": cfg.n_registers, "sampling_steps": cfg.n_steps,
+                   "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "vocab": cfg.vocab, "schedule": cfg.schedule, "order": cfg.order, "parallelism": "none"},
+        "roofline": roofline,
+        "step_attn_logits_mfma_frac": round(step_frac, 4),
+        "kernel_ms_per_generation": {"attention": round(att_ms.sum(), 4), "logits": round(log_ms.sum(), 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    run.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -92,8 +92,8 @@ typedef struct {
   size_t workspace_bytes;
 } mdm_buffers;
 
-/* Slots per (sequence, key/value head) in the cache buffers: seq_len + R rounded
- * up to a multiple of 64.  Returns 0 for an invalid config. */
+/* Slots per (sequence, key/value head) in the cache buffers: seq_len rounded up
+ * to a multiple of 64.  Returns 0 for an invalid config. */
 size_t mdm_cache_slots(const mdm_config* cfg);
 
 /* Bytes of workspace the context needs (RoPE table, partial results).  0 if invalid. */
@@ -132,8 +132,9 @@ mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, i
  *   n_decode rows C (the mask token at positions c_pos[b*c_stride + i]);
  *   R register rows (ids V+1.., positions seq_len..);
  * C and R rows see the cache plus all C and R rows.  Keys/values of the C and R
- * rows are written to the transient slots [len, len+n_decode+R), never
- * committed.  Queries are rotated at their own positions.  Output
+ * rows are gathered from the tables and rotated inside the kernel; they are
+ * never written to the cache.  Queries are rotated at their own positions.
+ * One kernel launch.  Output
  * out[b][i][h*d + j] (fp32, [B][n_q][H*d], n_q = n_new_cached + n_decode + R) is
  * the attention output of row i, head h.  Strides of 0 mean compact.
  * MDM_E_CAPACITY if len + n_decode > seq_len; MDM_E_ARG if n_new_cached > len

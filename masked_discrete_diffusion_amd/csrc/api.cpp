@@ -2,6 +2,7 @@
 // capacity validation, workspace layout, cache-length bookkeeping, launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -27,8 +28,10 @@ thread_local std::string g_last_error;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-  size_t err, rope_cos, rope_sin, hhi, hlo, partials, total;
-  int m_pad, n_vt;
+  size_t err, rope_cos, rope_sin, ktab, hhi, hlo, partials, zpart, tickets, total;
+  int ktab_rows;
+  size_t zpart_bytes;
+  int m_pad, n_vt, v_pad;
 };
 
 bool config_ok(const mdm_config* c, std::string* why) {
@@ -52,23 +55,34 @@ bool shape_supported(const mdm_config* c, std::string* why) {
   return true;
 }
 
-size_t slots_of(const mdm_config* c) { return align_up((size_t)c->seq_len + c->n_registers, kKeyTile); }
+size_t slots_of(const mdm_config* c) { return align_up((size_t)c->seq_len, kKeyTile); }
 
 Layout layout_of(const mdm_config* c) {
   Layout L{};
   const int hidden = c->n_heads * c->head_dim;
   const size_t max_pos = (size_t)c->seq_len + c->n_registers;
   L.n_vt = (c->vocab + kVocabTile - 1) / kVocabTile;
-  L.m_pad = (int)align_up((size_t)c->batch * c->max_decode, 64);
+  L.v_pad = L.n_vt * kVocabTile;
+  L.m_pad = (int)align_up((size_t)c->batch * c->max_decode, 128);
   size_t off = 0;
   L.err = off; off += kAlign;
   L.rope_cos = off; off = align_up(off + max_pos * (c->head_dim / 2) * sizeof(float), kAlign);
   L.rope_sin = off; off = align_up(off + max_pos * (c->head_dim / 2) * sizeof(float), kAlign);
   const bool bf16 = c->precision == MDM_BF16;
+  const size_t esz = bf16 ? 2 : 4;
+  // keys of the mask token at every position, then of the registers, per kv head
+  L.ktab_rows = (int)align_up((size_t)c->seq_len + c->n_registers, kKeyTile);
+  L.ktab = off; off = align_up(off + (size_t)c->n_kv_heads * L.ktab_rows * c->head_dim * esz, kAlign);
   const size_t hbytes = bf16 ? (size_t)L.m_pad * hidden * sizeof(uint16_t) : 0;
   L.hhi = off; off = align_up(off + hbytes, kAlign);
   L.hlo = off; off = align_up(off + ((bf16 && c->accurate_conf) ? hbytes : 0), kAlign);
   L.partials = off; off = align_up(off + (size_t)L.m_pad * L.n_vt * 8 * sizeof(float), kAlign);
+  // split-hidden partial logits: at most 8 splits, capped at 32 MiB (splitting
+  // is only chosen when few vocab tiles exist, i.e. for small vocabularies)
+  const size_t zfull = 8 * (size_t)c->batch * c->max_decode * L.v_pad * sizeof(float);
+  L.zpart_bytes = bf16 ? std::min(zfull, (size_t)32 << 20) : 0;
+  L.zpart = off; off = align_up(off + L.zpart_bytes, kAlign);
+  L.tickets = off; off = align_up(off + (size_t)L.n_vt * (L.m_pad / 32) * sizeof(int), kAlign);
   L.total = off;
   return L;
 }
@@ -177,6 +191,23 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
     st = hip_check(ctx, hipMemcpyAsync(ctx->ws() + L.rope_sin, sn.data(), sn.size() * sizeof(float),
                                        hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
   if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 1, ctx->stream), "clear error flag");
+  if (st == MDM_OK) {
+    // Key table: the mask token rotated at every position 0..seq_len-1, then the
+    // registers at seq_len..seq_len+R-1 (their keys never change).
+    Geometry gt = g;
+    gt.B = 1;
+    gt.slots = L.ktab_rows;
+    AppendArgs ka{};
+    ka.tk = buf->tk; ka.tv = buf->tv; ka.kc = ctx->ws() + L.ktab; ka.vc = nullptr;
+    ka.cache_pos = nullptr; ka.cache_tok = nullptr;
+    ka.rope_cos = rope_cos(ctx); ka.rope_sin = rope_sin(ctx);
+    ka.tok = nullptr; ka.pos = nullptr; ka.stride = 0; ka.n_a = cfg->seq_len; ka.n_reg = cfg->n_registers;
+    ka.slot0 = 0; ka.err = err_word(ctx);
+    st = hip_check(ctx, launch_append(gt, ka, ctx->stream), "key table");
+  }
+  if (st == MDM_OK)
+    st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.tickets), 0,
+                                        L.n_vt * (L.m_pad / 32), ctx->stream), "clear tickets");
   if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "init synchronize");
   if (st != MDM_OK) {
     delete ctx;
@@ -232,17 +263,10 @@ mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t*
                 ctx->cfg.seq_len);
   const int n_r = ctx->cfg.n_registers;
   if (n_new_cached + n_decode + n_r == 0) return MDM_OK;
-  // transient keys/values of the decoded rows and the registers
-  AppendArgs ta{};
-  ta.tk = ctx->buf.tk; ta.tv = ctx->buf.tv; ta.kc = ctx->buf.k_cache; ta.vc = ctx->buf.v_cache;
-  ta.cache_pos = nullptr; ta.cache_tok = nullptr;
-  ta.rope_cos = rope_cos(ctx); ta.rope_sin = rope_sin(ctx);
-  ta.tok = nullptr; ta.pos = c_pos; ta.stride = c_stride; ta.n_a = n_decode; ta.n_reg = n_r;
-  ta.slot0 = ctx->len; ta.err = err_word(ctx);
-  mdm_status st = hip_check(ctx, launch_append(ctx->g, ta, ctx->stream), "transient append launch");
-  if (st != MDM_OK) return st;
   AttnArgs a{};
-  a.tq = ctx->buf.tq; a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
+  a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
+  a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
+  a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
   a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
   a.d_tok = d_tok; a.d_pos = d_pos; a.d_stride = d_stride; a.c_pos = c_pos; a.c_stride = c_stride;
   a.out = out; a.err = err_word(ctx);
@@ -269,6 +293,8 @@ mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_
               ? reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hlo) : nullptr;
   a.partials = reinterpret_cast<float*>(ctx->ws() + ctx->L.partials);
   a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
+  a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
+  a.tickets = reinterpret_cast<int*>(ctx->ws() + ctx->L.tickets); a.v_pad = ctx->L.v_pad;
   return hip_check(ctx, launch_vocab(ctx->g, a, ctx->stream), "vocab launch");
 }
 

@@ -2,9 +2,9 @@
 // keys by RoPE at each row's explicit position id, and store them into the
 // cache (keys [slot][d]; values transposed [d][slot] so the attention kernel
 // streams them key-contiguous).  Used for committed rows (the prompt prefetch
-// and the tokens decoded at the previous step) and for the transient rows of
-// this step's masked tokens and registers (page 3, section 3.2; page 1,
-// worked example = the paper's Figure 3).
+// and the tokens decoded at the previous step) and, once at init, for the keys
+// of the mask token at every position and of the registers (page 3, section
+// 3.2; page 1, worked example = the paper's Figure 3).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   if (valid) {
     if (r < a.n_a) {
       id = a.tok ? a.tok[(int64_t)b * a.stride + r] : g.V;
-      pos = a.pos[(int64_t)b * a.stride + r];
+      pos = a.pos ? a.pos[(int64_t)b * a.stride + r] : r;
     } else {
       const int j = r - a.n_a;
       id = g.V + 1 + j;
@@ -73,13 +73,16 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
       kdst[2 * p] = Elem<T>::from_f64(r0d);
       kdst[2 * p + 1] = Elem<T>::from_f64(r1d);
     }
+    if (vc) {
 #pragma unroll
-    for (int e = 0; e < kEpt; ++e) vs[lr][part * kEpt + e] = vsrc[e];
+      for (int e = 0; e < kEpt; ++e) vs[lr][part * kEpt + e] = vsrc[e];
+    }
     if (a.cache_pos && kvh == 0 && part == 0) {
       a.cache_pos[(int64_t)b * g.slots + slot] = pos;
       a.cache_tok[(int64_t)b * g.slots + slot] = id;
     }
   }
+  if (!vc) return;
   __syncthreads();
   // transposed value store: for each d, the block's rows are consecutive slots
   const int rows_here = min(kRowsPerBlock, n_rows - r0);

@@ -10,6 +10,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kKeyTile = 64;       // keys per LDS stage in attention; cache slots are a multiple
@@ -31,6 +33,12 @@ __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint3
 __device__ inline uint16_t f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
+}
+
+// Two floats -> packed bf16 pair (first in the low half), round to nearest even.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const floatx2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // double -> bf16 bit pattern, round to nearest even in ONE step (no detour via

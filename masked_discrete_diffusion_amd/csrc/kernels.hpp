@@ -16,9 +16,10 @@ struct Geometry {
 };
 
 // Rows [0, n_a): token tok[b*stride + r] (or the mask token V when tok == NULL),
-// position pos[b*stride + r].  Rows [n_a, n_a + n_reg): register r - n_a
-// (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) and transposed values to
-// slots slot0 + r; records (pos, id) when cache_pos != NULL.
+// position pos[b*stride + r] (or r when pos == NULL).  Rows [n_a, n_a + n_reg):
+// register r - n_a (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) and,
+// when vc != NULL, transposed values to slots slot0 + r; records (pos, id) when
+// cache_pos != NULL.
 struct AppendArgs {
   const void* tk;
   const void* tv;
@@ -38,6 +39,10 @@ hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const void* tq;
+  const void* tv;           // value table (transient C and R values)
+  const void* ktab;         // [H_kv][ktab_rows][d] keys of the mask token at every
+                            // position, then of the registers (built at init)
+  int ktab_rows;
   const void* kc;
   const void* vc;
   const float* rope_cos;
@@ -62,6 +67,10 @@ struct VocabArgs {
   uint16_t* hhi;            // [m_pad][hidden] bf16 workspace (bf16 mode)
   uint16_t* hlo;            // [m_pad][hidden] bf16 workspace (accurate mode), or NULL
   float* partials;          // [m_pad][n_vt][8]
+  float* zpart;             // split partial logits [n_split][M][v_pad] (bf16 path)
+  int64_t zpart_bytes;
+  int* tickets;             // [m_tiles][n_vt] arrival counters, zero between launches
+  int v_pad;                // V rounded up to the vocab tile
   float* logits;            // optional [M][V]
   float* conf;              // [M]
   int32_t* token;           // [M]

@@ -4,7 +4,7 @@
 // 1. pack:   fp32 h rows of the decoded subset -> bf16 hi (and lo = bf16(h - hi))
 //            in a dense [m_pad][hidden] operand, zero rows past M.
 // 2. screen: z^T = W h^T on bf16 MFMA (32x32x16), one 128-column vocab tile by
-//            64 rows per block; the epilogue keeps per (row, tile) the maximum,
+//            32/64/128 rows per block; the epilogue keeps per (row, tile) the maximum,
 //            the sum of exp(z - max) and the two best (value, index) pairs, and
 //            never writes the logits (unless asked to, for validation).
 //            fp32 mode: the same tile and epilogue with fp32 VALU products.
@@ -21,8 +21,8 @@ namespace mdm {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kRowTile = 64;       // rows per screening block
 constexpr int kKChunk = 64;        // hidden elements per LDS stage
+constexpr int kScreenTargetBlocks = 256;   // split hidden until about this many blocks
 
 struct Top2 {
   float m;      // running maximum
@@ -42,7 +42,7 @@ __device__ inline void top2_push(Top2& t, float v, int i) {
 __device__ inline Top2 top2_merge(const Top2& a, const Top2& b) {
   Top2 r;
   r.m = fmaxf(a.m, b.m);
-  r.se = (a.m == kNegInf ? 0.f : a.se * __expf(a.m - r.m)) + (b.m == kNegInf ? 0.f : b.se * __expf(b.m - r.m));
+  r.se = (a.m == kNegInf ? 0.f : a.se * expf(a.m - r.m)) + (b.m == kNegInf ? 0.f : b.se * expf(b.m - r.m));
   r.v1 = a.v1; r.i1 = a.i1; r.v2 = a.v2; r.i2 = a.i2;
   top2_push(r, b.v1, b.i1);
   top2_push(r, b.v2, b.i2);
@@ -72,7 +72,7 @@ __device__ inline Top2 summarize(const float* vals, const int* idx) {
   }
   if (t.m != kNegInf) {
 #pragma unroll
-    for (int e = 0; e < N; ++e) t.se += __expf(vals[e] - t.m);
+    for (int e = 0; e < N; ++e) t.se += expf(vals[e] - t.m);
   }
   return t;
 }
@@ -111,63 +111,163 @@ __global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
 }
 
 // ------------------------------------------------------- screen, bf16 MFMA --
-// Block: 4 wavefronts; wave w owns vocab columns [32w, 32w+32) of the tile and
-// all 64 rows (two 32-row blocks).
-template <bool kLo>
-__global__ __launch_bounds__(256) void k_screen_bf16(Geometry g, VocabArgs a, int M) {
+// Block: 4 wavefronts; wave w owns vocab columns [32w, 32w+32) of a 128-column
+// tile and all 32*RB rows of the row tile.  Hidden is consumed in 64-wide
+// chunks, double-buffered in LDS with the next chunk's global loads in flight
+// while the current one is multiplied.  With n_split > 1 the hidden dimension
+// is split over blockIdx.z: every split writes its partial tile, and the last
+// split to arrive (ticket per tile) sums the partials in split order and runs
+// the epilogue, so the result does not depend on arrival order.
+constexpr int kScreenThreads = 256;
+
+template <int RB, bool kLo>
+struct ScreenRegs {
+  u16x8 w[4];
+  u16x8 h[RB];
+  u16x8 l[kLo ? RB : 1];
+};
+
+template <int RB, bool kLo>
+__device__ inline void screen_load(ScreenRegs<RB, kLo>& r, const uint16_t* w, const uint16_t* hhi,
+                                   const uint16_t* hlo, int hidden, int V, int v0, int m0, int k0) {
+  constexpr int CPR = kKChunk / 8;   // 16-byte chunks per row of a chunk
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + i * kScreenThreads;
+    const int v = min(v0 + c / CPR, V - 1);
+    r.w[i] = *reinterpret_cast<const u16x8*>(w + (int64_t)v * hidden + k0 + (c % CPR) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int c = threadIdx.x + i * kScreenThreads;
+    const int64_t off = (int64_t)(m0 + c / CPR) * hidden + k0 + (c % CPR) * 8;
+    r.h[i] = *reinterpret_cast<const u16x8*>(hhi + off);
+    if (kLo) r.l[i] = *reinterpret_cast<const u16x8*>(hlo + off);
+  }
+}
+
+template <int RB, bool kLo>
+__device__ inline void screen_store(const ScreenRegs<RB, kLo>& r, uint16_t* ws, uint16_t* hs, uint16_t* ls) {
   constexpr int WPAD = kKChunk + 8;
-  __shared__ __align__(16) uint16_t ws[kVocabTile * WPAD];
-  __shared__ __align__(16) uint16_t hs[kRowTile * WPAD];
-  __shared__ __align__(16) uint16_t ls[kLo ? kRowTile * WPAD : 8];
-  __shared__ Top2 red[4][kRowTile];
+  constexpr int CPR = kKChunk / 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + i * kScreenThreads;
+    *reinterpret_cast<u16x8*>(ws + (c / CPR) * WPAD + (c % CPR) * 8) = r.w[i];
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int c = threadIdx.x + i * kScreenThreads;
+    *reinterpret_cast<u16x8*>(hs + (c / CPR) * WPAD + (c % CPR) * 8) = r.h[i];
+    if (kLo) *reinterpret_cast<u16x8*>(ls + (c / CPR) * WPAD + (c % CPR) * 8) = r.l[i];
+  }
+}
+
+template <int RB, bool kLo>
+__global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, VocabArgs a, int M, int n_split) {
+  constexpr int WPAD = kKChunk + 8;
+  constexpr int MT = 32 * RB;
+  __shared__ __align__(16) uint16_t ws[2][kVocabTile * WPAD];
+  __shared__ __align__(16) uint16_t hs[2][MT * WPAD];
+  __shared__ __align__(16) uint16_t ls[kLo ? 2 : 1][kLo ? MT * WPAD : 8];
+  __shared__ Top2 red[4][MT];
+  __shared__ int last_flag;
 
   const int vt = blockIdx.x;
   const int mt = blockIdx.y;
+  const int split = blockIdx.z;
   const int v0 = vt * kVocabTile;
-  const int m0 = mt * kRowTile;
+  const int m0 = mt * MT;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int half = lane / 32, l32 = lane % 32;
   const uint16_t* w = static_cast<const uint16_t*>(a.w);
+  const int k_len = g.hidden / n_split;
+  const int k_beg = split * k_len;
+  const int n_chunks = k_len / kKChunk;
 
-  floatx16 acc[2];
+  floatx16 acc[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 
-  for (int k0 = 0; k0 < g.hidden; k0 += kKChunk) {
+  ScreenRegs<RB, kLo> regs;
+  screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg);
+  screen_store<RB, kLo>(regs, ws[0], hs[0], ls[0]);
+  if (n_chunks > 1) screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg + kKChunk);
+  int cur = 0;
+  for (int ci = 0; ci < n_chunks; ++ci, cur ^= 1) {
     __syncthreads();
-    for (int c = threadIdx.x; c < kVocabTile * kKChunk / 8; c += blockDim.x) {
-      const int vr = c / (kKChunk / 8), kc = c % (kKChunk / 8);
-      const int v = min(v0 + vr, g.V - 1);
-      *reinterpret_cast<u16x8*>(ws + vr * WPAD + kc * 8) =
-          *reinterpret_cast<const u16x8*>(w + (int64_t)v * g.hidden + k0 + kc * 8);
-    }
-    for (int c = threadIdx.x; c < kRowTile * kKChunk / 8; c += blockDim.x) {
-      const int r = c / (kKChunk / 8), kc = c % (kKChunk / 8);
-      const int64_t off = (int64_t)(m0 + r) * g.hidden + k0 + kc * 8;
-      *reinterpret_cast<u16x8*>(hs + r * WPAD + kc * 8) = *reinterpret_cast<const u16x8*>(a.hhi + off);
-      if (kLo) *reinterpret_cast<u16x8*>(ls + r * WPAD + kc * 8) = *reinterpret_cast<const u16x8*>(a.hlo + off);
-    }
-    __syncthreads();
+    const uint16_t* wb = ws[cur];
+    const uint16_t* hb = hs[cur];
+    const uint16_t* lb = ls[kLo ? cur : 0];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(ws + (32 * wave + l32) * WPAD + 16 * t + 8 * half);
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wb + (32 * wave + l32) * WPAD + 16 * t + 8 * half);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(hs + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(hb + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
         if (kLo) {
-          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(ls + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(lb + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
           acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lf, acc[rb], 0, 0, 0);
+        }
+      }
+    }
+    if (ci + 1 < n_chunks) {
+      screen_store<RB, kLo>(regs, ws[cur ^ 1], hs[cur ^ 1], ls[kLo ? cur ^ 1 : 0]);
+      if (ci + 2 < n_chunks)
+        screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg + (ci + 2) * kKChunk);
+    }
+  }
+
+  // lane holds z for row m0 + 32rb + l32 and vocab v0 + 32w + 8jj + 4half + ii
+  if (n_split > 1) {
+    float* zp = a.zpart;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = m0 + 32 * rb + l32;
+      if (r < M) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int v = v0 + 32 * wave + 8 * jj + 4 * half;
+          floatx4 q = {acc[rb][4 * jj], acc[rb][4 * jj + 1], acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]};
+          *reinterpret_cast<floatx4*>(zp + ((int64_t)split * M + r) * a.v_pad + v) = q;
+        }
+      }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* ticket = a.tickets + mt * gridDim.x + vt;
+      const int prev = atomicAdd(ticket, 1);
+      last_flag = (prev == n_split - 1);
+      if (last_flag) *ticket = 0;             // self-cleaning for the next launch
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = m0 + 32 * rb + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+      if (r < M) {
+        for (int sp = 0; sp < n_split; ++sp) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int v = v0 + 32 * wave + 8 * jj + 4 * half;
+            const floatx4 q = *reinterpret_cast<const floatx4*>(zp + ((int64_t)sp * M + r) * a.v_pad + v);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[rb][4 * jj + ii] += q[ii];
+          }
         }
       }
     }
   }
 
-  // epilogue: lane holds z for row 32rb + l32 and vocab v0 + 32w + 8jj + 4half + ii
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     float vals[16];
     int idx[16];
     const int r = m0 + 32 * rb + l32;
@@ -184,13 +284,13 @@ __global__ __launch_bounds__(256) void k_screen_bf16(Geometry g, VocabArgs a, in
     if (half == 0) red[wave][32 * rb + l32] = t;
   }
   __syncthreads();
-  if (threadIdx.x < kRowTile) {
+  if (threadIdx.x < MT) {
     const int r = threadIdx.x;
     Top2 t = red[0][r];
 #pragma unroll
     for (int wv = 1; wv < 4; ++wv) t = top2_merge(t, red[wv][r]);
     const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
-    store_partial(a.partials + ((int64_t)(m0 + r) * n_vt + vt) * 8, t);
+    if (m0 + r < a.m_pad) store_partial(a.partials + ((int64_t)(m0 + r) * n_vt + vt) * 8, t);
   }
 }
 
@@ -263,26 +363,42 @@ __global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int
 }
 
 // ----------------------------------------------------- merge and re-score --
+// One wavefront per row, 4 rows per block.
 struct Cand {
   float v;
   int i;
 };
 
 template <typename WT>
-__device__ inline float w_elem(const WT* w, int64_t i);
+struct W8;
 template <>
-__device__ inline float w_elem<uint16_t>(const uint16_t* w, int64_t i) { return bf16_to_f32(w[i]); }
+struct W8<uint16_t> {
+  static __device__ inline void load(const uint16_t* p, float* out) {
+    const u16x8 r = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = bf16_to_f32(r[e]);
+  }
+};
 template <>
-__device__ inline float w_elem<float>(const float* w, int64_t i) { return w[i]; }
+struct W8<float> {
+  static __device__ inline void load(const float* p, float* out) {
+    const floatx4 a = reinterpret_cast<const floatx4*>(p)[0];
+    const floatx4 b = reinterpret_cast<const floatx4*>(p)[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
+  }
+};
 
 template <typename WT>
-__global__ __launch_bounds__(64) void k_merge(Geometry g, VocabArgs a, int M) {
-  const int m = blockIdx.x;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
+  const int wave = threadIdx.x / kWave;
+  const int m = blockIdx.x * 4 + wave;
+  if (m >= M) return;
+  const int lane = threadIdx.x % kWave;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
   const float* part = a.partials + (int64_t)m * n_vt * 8;
 
-  // per-lane running (max, sumexp) in double and top-K candidates
+  // per-lane running (max, sum of exp) in double and top-K candidates
   double lm = -1e300, lse = 0.0;
   Cand c[kTopK];
 #pragma unroll
@@ -308,7 +424,6 @@ __global__ __launch_bounds__(64) void k_merge(Geometry g, VocabArgs a, int M) {
       }
     }
   }
-  // wave reduce (max, sumexp)
 #pragma unroll
   for (int mask = 32; mask >= 1; mask >>= 1) {
     const double om = __shfl_xor(lm, mask), ose = __shfl_xor(lse, mask);
@@ -318,14 +433,10 @@ __global__ __launch_bounds__(64) void k_merge(Geometry g, VocabArgs a, int M) {
   }
   // wave top-K: K rounds of a (value desc, index asc) argmax; the winner pops.
   Cand best[kTopK];
-  int head = 0;
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) {
-    float v = head < kTopK ? c[0].v : kNegInf;
-    int i = head < kTopK ? c[0].i : 0x7fffffff;
-    // c[0] is always this lane's current best (popped entries shift down)
-    float bv = v;
-    int bi = i;
+    float bv = c[0].v;
+    int bi = c[0].i;
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) {
       const float ov = __shfl_xor(bv, mask);
@@ -334,30 +445,50 @@ __global__ __launch_bounds__(64) void k_merge(Geometry g, VocabArgs a, int M) {
     }
     best[k].v = bv;
     best[k].i = bi;
-    if (bi == i && bv == v && i != 0x7fffffff) {   // this lane held the winner: pop it
+    if (bi == c[0].i && bi != 0x7fffffff) {          // this lane held the winner: pop it
 #pragma unroll
       for (int q = 0; q < kTopK - 1; ++q) c[q] = c[q + 1];
       c[kTopK - 1].v = kNegInf;
       c[kTopK - 1].i = 0x7fffffff;
-      ++head;
     }
   }
-  // exact fp32 re-score of the candidates from the fp32 h
+  // exact fp32 re-score of the candidates from the fp32 h: lane covers 8
+  // consecutive elements per 512-wide stride; all candidates' rows in flight.
   const int b = m / a.n_c, cc = m % a.n_c;
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
   const WT* w = static_cast<const WT*>(a.w);
+  const WT* wr[kTopK];
+  bool okc[kTopK];
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    okc[k] = best[k].i >= 0 && best[k].i < g.V;
+    wr[k] = w + (int64_t)(okc[k] ? best[k].i : 0) * g.hidden;
+  }
+  float sacc[kTopK];
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) sacc[k] = 0.f;
+#pragma unroll 2
+  for (int e0 = 8 * lane; e0 < g.hidden; e0 += 8 * kWave) {
+    const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
+    const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
+    float wv[kTopK][8];
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) W8<WT>::load(wr[k] + e0, wv[k]);
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[k] = fmaf(h0[e], wv[k][e], sacc[k]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[k] = fmaf(h1[e], wv[k][4 + e], sacc[k]);
+    }
+  }
   float ze[kTopK];
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) {
-    const int v = best[k].i;
-    float s = 0.f;
-    if (v >= 0 && v < g.V) {
-      const WT* wr = w + (int64_t)v * g.hidden;
-      for (int e = lane; e < g.hidden; e += kWave) s = fmaf(hrow[e], w_elem<WT>(wr, e), s);
-    }
+    float s = sacc[k];
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
-    ze[k] = (v >= 0 && v < g.V) ? s : kNegInf;
+    ze[k] = okc[k] ? s : kNegInf;
   }
   if (lane == 0) {
     int tb = 0;
@@ -386,27 +517,41 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   const int M = g.B * a.n_c;
   if (M <= 0) return hipSuccess;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+  const dim3 merge_grid((M + 3) / 4);
   if (g.fp32) {
     dim3 grid(n_vt, (M + 31) / 32);
     hipLaunchKernelGGL(k_screen_f32, grid, dim3(256), 0, s, g, a, M);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_merge<float>), dim3(M), dim3(kWave), 0, s, g, a, M);
+    hipLaunchKernelGGL((k_merge<float>), merge_grid, dim3(256), 0, s, g, a, M);
     return hipGetLastError();
   }
-  const int m_tiles = (M + kRowTile - 1) / kRowTile;
+  const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  const int mt_rows = 32 * rb;
+  const int m_tiles = (M + mt_rows - 1) / mt_rows;
   VocabArgs pa = a;
-  pa.m_pad = m_tiles * kRowTile;
+  pa.m_pad = ((M + 63) / 64) * 64;
+  if (m_tiles * mt_rows > pa.m_pad) pa.m_pad = m_tiles * mt_rows;
+  int n_split = 1;
+  const int chunks = g.hidden / kKChunk;
+  while (n_split < 8 && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks && chunks % (n_split * 2) == 0 &&
+         (int64_t)n_split * 2 * M * pa.v_pad * 4 <= a.zpart_bytes)
+    n_split *= 2;
   const int64_t n8 = (int64_t)pa.m_pad * g.hidden / 8;
   hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, g, pa, M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid(n_vt, m_tiles);
-  if (a.hlo) hipLaunchKernelGGL((k_screen_bf16<true>), grid, dim3(256), 0, s, g, pa, M);
-  else hipLaunchKernelGGL((k_screen_bf16<false>), grid, dim3(256), 0, s, g, pa, M);
+  dim3 grid(n_vt, m_tiles, n_split);
+#define MDM_SCREEN(RB)                                                                              \
+  if (a.hlo) hipLaunchKernelGGL((k_screen_bf16<RB, true>), grid, dim3(kScreenThreads), 0, s, g, pa, M, n_split); \
+  else hipLaunchKernelGGL((k_screen_bf16<RB, false>), grid, dim3(kScreenThreads), 0, s, g, pa, M, n_split)
+  if (rb == 1) { MDM_SCREEN(1); }
+  else if (rb == 2) { MDM_SCREEN(2); }
+  else { MDM_SCREEN(4); }
+#undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_merge<uint16_t>), dim3(M), dim3(kWave), 0, s, g, pa, M);
+  hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_sizes():
     c = _cfg()
-    assert L.mdm_cache_slots(c) == 128                       # 100 + 8 rounded up to 64
+    assert L.mdm_cache_slots(c) == 128                       # 100 rounded up to 64
     assert L.mdm_element_bytes(c) == 2
     assert L.mdm_element_bytes(_cfg(precision=L.MDM_FP32)) == 4
     ws = L.mdm_workspace_bytes(c)

@@ -136,11 +136,11 @@ def test_forbidden_keys_nan_poison():
     forbidden = [cfg.vocab] + list(range(cfg.vocab + 1, cfg.vocab + 1 + cfg.n_registers))
     run.tk.view(cfg.table_rows, -1)[forbidden] = nan
     run.tv.view(cfg.table_rows, -1)[forbidden] = nan
-    s_tot = L.mdm_cache_len(run.ctx) + st.n_c + cfg.n_registers
+    s_len = L.mdm_cache_len(run.ctx)                 # slots past the committed rows
     kc = run.k_cache.view(cfg.batch, cfg.n_kv_heads, run.slots, cfg.head_dim)
     vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, cfg.head_dim, run.slots)
-    kc[:, :, s_tot:] = nan
-    vc[:, :, :, s_tot:] = nan
+    kc[:, :, s_len:] = nan
+    vc[:, :, :, s_len:] = nan
     got = attend()
     n_d = st.n_d
     assert torch.isfinite(got[:, :n_d]).all()
