@@ -143,15 +143,13 @@ __device__ inline void tile_dma(const uint16_t* kc, const uint16_t* vc, int slot
       const int u = blk * kWave + lane;
       const int r = u / T::KU, c = u % T::KU;
       const uint16_t* gk = kc + (int64_t)(kt + r) * D + (c < T::KC ? c : 0) * 8;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gk,
-                                       (void __attribute__((address_space(3)))*)(ks + blk * kWave * 8), 16, 0, 0);
+      dma16(gk, ks + blk * kWave * 8);
     } else if (blk < T::BLOCKS) {
       const int vb = blk - T::K_BLOCKS;
       const int u = vb * kWave + lane;
       const int d = u / T::VU, c = u % T::VU;
       const uint16_t* gv = vc + (int64_t)d * slots + kt + (c < T::VC ? c : 0) * 8;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gv,
-                                       (void __attribute__((address_space(3)))*)(vs + vb * kWave * 8), 16, 0, 0);
+      dma16(gv, vs + vb * kWave * 8);
     }
   }
 }
@@ -204,38 +202,6 @@ __device__ inline void tile_fill(const Geometry& g, const AttnArgs& a, int b, in
   else tile_edge<D>(g, a, b, kvh, kc, vc, kt, ks, vs);
 }
 
-// s_waitcnt vmcnt(n) (and lgkmcnt(0)) for a run-time n: the immediate must be a
-// constant, so dispatch over the counts a ring can ask for; anything else
-// waits for everything, which is always correct.
-__device__ inline void wait_vmcnt(int n) {
-  switch (n) {
-    case 1: asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
-    case 11: asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory"); break;
-    case 13: asm volatile("s_waitcnt vmcnt(13) lgkmcnt(0)" ::: "memory"); break;
-    case 14: asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)" ::: "memory"); break;
-    case 15: asm volatile("s_waitcnt vmcnt(15) lgkmcnt(0)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-  }
-}
-
-// Barrier without the release fence of __syncthreads (which would wait for
-// every in-flight LDS-DMA load); the waits are explicit around it.
-__device__ inline void tile_barrier() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Split p into bf16 hi + lo for a pair of values, packed two per word.
 struct HiLo {
   uint32_t hi, lo;
@@ -255,54 +221,32 @@ __device__ inline HiLo split_pair(float p0, float p1) {
 // divides by the same l, so the result is the same softmax.
 constexpr float kRescaleLog2 = 8.f;
 
-// One 64-key tile for one wavefront (32 query rows): S^T = K Q^T, online
-// softmax, O^T += V^T (P_hi + P_lo)^T.  All K fragments of the tile are read
-// before the two independent 32-key MFMA chains run interleaved; the first
-// half's V fragments are read before the softmax so their LDS latency hides
-// behind it.  kEdge: keys at or past wlen are removed by select.
-template <int D, bool kEdge>
-__device__ inline void attn_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf, floatx16* acc,
-                                 float& m_ref, float& l_run, int kt, int wlen, int krow, int half, int l32,
-                                 float sc) {
-  using T = AttnTile<D>;
-  constexpr int NKS = D / 16;
-  constexpr int NDB = D / 32;
-  bf16x8 kf[2][NKS];
-  const uint16_t* kbase = kb + (krow * T::KU + half) * 8;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int t = 0; t < NKS; ++t)
-      kf[sub][t] = *reinterpret_cast<const bf16x8*>(kbase + (sub * 32 * T::KU + 2 * t) * 8);
-  floatx16 s0, s1;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-#pragma unroll
-  for (int t = 0; t < NKS; ++t) {
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][t], qf[t], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][t], qf[t], s1, 0, 0, 0);
-  }
-  const uint16_t* vbase = vb + (l32 * T::VU + half) * 8;
-  u16x8 vf[2][NDB];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 2 * u) * 8);
+// max of three floats.  IEEE maximum (NaN-propagating) needs no canonicalising
+// moves in front of MFMA results and becomes one v_maximum3_f32; the compiler
+// inserts the MFMA-to-VALU wait states itself.  Scores are finite or -1e30
+// (masked) unless the inputs hold NaN, which then propagates.
+__device__ inline float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Softmax of one 32-key half for this lane's row: lazily raise the reference
+// (rescaling O and l when a row maximum passes it by more than kRescaleLog2),
+// then p = exp2(s * sc - m_ref) in place and their sum added to l.
+template <int NDB, bool kEdge>
+__device__ inline void half_softmax(floatx16& sv, floatx16* acc, float& m_ref, float& l_run, int key_base,
+                                    int wlen, int half, float sc) {
   if (kEdge) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int jj = e / 4, ii = e % 4;
-      const int key = kt + 16 * (jj / 2) + 8 * half + 4 * (jj % 2) + ii;
-      s0[e] = key < wlen ? s0[e] : kMaskedScore;
-      s1[e] = key + 32 < wlen ? s1[e] : kMaskedScore;
+      const int key = key_base + 16 * (jj / 2) + 8 * half + 4 * (jj % 2) + ii;
+      sv[e] = key < wlen ? sv[e] : kMaskedScore;
     }
   }
-  // tile maximum of the raw scores of this lane's row (partner lane holds the rest)
-  float mt = fmaxf(s0[0], s1[0]);
+  float mt = max3(sv[0], sv[1], sv[2]);
 #pragma unroll
-  for (int e = 1; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
+  for (int e = 3; e < 15; e += 2) mt = max3(mt, sv[e], sv[e + 1]);
+  mt = max3(mt, sv[15], __shfl_xor(max3(mt, sv[15], sv[15]), 32)) * sc;
   if (__any(mt > m_ref + kRescaleLog2)) {
     const float m_new = fmaxf(m_ref, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -316,50 +260,85 @@ __device__ inline void attn_tile(const uint16_t* kb, const uint16_t* vb, const b
   float lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], sc, -m_ref));
-    s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], sc, -m_ref));
-    lsum += s0[e] + s1[e];
+    sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], sc, -m_ref));
+    lsum += sv[e];
   }
   l_run += lsum;
+}
 
+// O^T += V^T (P_hi + P_lo)^T for one 32-key half (two 16-key k-steps).
+template <int NDB, bool kEdge>
+__device__ inline void half_pv(const floatx16& p, const u16x8 (*vf)[NDB], floatx16* acc, int key_base, int wlen,
+                               int half) {
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    if (sub == 1) {
+  for (int u = 0; u < 2; ++u) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 hi, lo;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 4 + 2 * u) * 8);
+    for (int q = 0; q < 4; ++q) {
+      const HiLo w = split_pair(p[8 * u + 2 * q], p[8 * u + 2 * q + 1]);
+      hi[q] = w.hi;
+      lo[q] = w.lo;
     }
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, hi);
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, lo);
+    bf16x8 v[NDB];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      u32x4 hi, lo;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float p0 = sub == 0 ? s0[8 * u + 2 * q] : s1[8 * u + 2 * q];
-        const float p1 = sub == 0 ? s0[8 * u + 2 * q + 1] : s1[8 * u + 2 * q + 1];
-        const HiLo w = split_pair(p0, p1);
-        hi[q] = w.hi;
-        lo[q] = w.lo;
-      }
-      const bf16x8 phi = __builtin_bit_cast(bf16x8, hi);
-      const bf16x8 plo = __builtin_bit_cast(bf16x8, lo);
+    for (int db = 0; db < NDB; ++db) {
+      u16x8 raw = vf[u][db];
       if (kEdge) {
-        const int key0 = kt + 8 * (4 * sub + 2 * u + half);
+        const int key0 = key_base + 16 * u + 8 * half;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[u][db][e] = (key0 + e < wlen) ? vf[u][db][e] : (uint16_t)0;
+        for (int e = 0; e < 8; ++e) raw[e] = (key0 + e < wlen) ? raw[e] : (uint16_t)0;
       }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[u][db]), phi, acc[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[u][db]), plo, acc[db], 0, 0, 0);
+      v[db] = __builtin_bit_cast(bf16x8, raw);
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], phi, acc[db], 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db], plo, acc[db], 0, 0, 0);
   }
+}
+
+// One 64-key tile for one wavefront (32 query rows), as two 32-key halves
+// pipelined so that each half's softmax (VALU) can run while the other half's
+// MFMAs execute: S0, S1 issued; softmax(S0) overlaps S1; PV(0) issued;
+// softmax(S1) overlaps PV(0); PV(1).  kEdge: keys at or past wlen are
+// removed by select.
+template <int D, bool kEdge>
+__device__ inline void attn_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf, floatx16* acc,
+                                 float& m_ref, float& l_run, int kt, int wlen, int krow, int half, int l32,
+                                 float sc) {
+  using T = AttnTile<D>;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  const uint16_t* kbase = kb + (krow * T::KU + half) * 8;
+  const uint16_t* vbase = vb + (l32 * T::VU + half) * 8;
+  floatx16 s0, s1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) {
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
+    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kbase + (32 * T::KU + 2 * t) * 8);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[t], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[t], s1, 0, 0, 0);
+  }
+  u16x8 vf[2][NDB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 2 * u) * 8);
+  half_softmax<NDB, kEdge>(s0, acc, m_ref, l_run, kt, wlen, half, sc);
+  half_pv<NDB, kEdge>(s0, vf, acc, kt, wlen, half);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 4 + 2 * u) * 8);
+  half_softmax<NDB, kEdge>(s1, acc, m_ref, l_run, kt + 32, wlen, half, sc);
+  half_pv<NDB, kEdge>(s1, vf, acc, kt + 32, wlen, half);
 }
 
 // Block: kAttnWaves wavefronts, each owning one 32-row chunk of one query head;
@@ -452,8 +431,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
 
   for (int t = 0; t < n_tiles; ++t) {
     const int younger = min(kStages - 2, n_tiles - 1 - t);
-    wait_vmcnt(younger * my_loads);
-    tile_barrier();
+    ring_wait(younger * my_loads);
+    ring_barrier();
     const int nxt = t + kStages - 1;
     if (nxt < n_tiles) tile_fill<D>(g, a, b, kvh, kc, vc, nxt * KT, ks[nxt % kStages], vs[nxt % kStages]);
     const int kt = t * KT;

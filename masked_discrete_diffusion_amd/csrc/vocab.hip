@@ -363,7 +363,9 @@ __global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int
 }
 
 // ----------------------------------------------------- merge and re-score --
-// One wavefront per row, 4 rows per block.
+// One block (4 wavefronts) per row: the threads fold the tiles' (max, sum of
+// exp, top-2) partials, the block keeps the kTopK best candidates, and wave k
+// re-scores candidate k exactly in fp32 from the fp32 h.
 struct Cand {
   float v;
   int i;
@@ -389,50 +391,50 @@ struct W8<float> {
   }
 };
 
+__device__ inline void cand_insert(Cand* c, float v, int i) {
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    if (ranks_before(v, i, c[k].v, c[k].i)) {
+      const Cand t = c[k];
+      c[k].v = v; c[k].i = i;
+      v = t.v; i = t.i;
+    }
+  }
+}
+
+// (max, sum of exp) of two partial sums
+__device__ inline void lse_merge(float& m, float& se, float om, float ose) {
+  const float nm = fmaxf(m, om);
+  se = (m == kNegInf ? 0.f : se * expf(m - nm)) + (om == kNegInf ? 0.f : ose * expf(om - nm));
+  m = nm;
+}
+
 template <typename WT>
 __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
-  const int wave = threadIdx.x / kWave;
-  const int m = blockIdx.x * 4 + wave;
-  if (m >= M) return;
-  const int lane = threadIdx.x % kWave;
+  __shared__ float s_m[4], s_se[4];
+  __shared__ Cand s_c[4][kTopK];
+  __shared__ Cand s_best[kTopK];
+  __shared__ float s_ze[kTopK];
+  const int m = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
   const float* part = a.partials + (int64_t)m * n_vt * 8;
 
-  // per-lane running (max, sum of exp) in double and top-K candidates
-  double lm = -1e300, lse = 0.0;
+  float lm = kNegInf, lse = 0.f;
   Cand c[kTopK];
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
-  for (int tile = lane; tile < n_vt; tile += kWave) {
+  for (int tile = threadIdx.x; tile < n_vt; tile += blockDim.x) {
     const floatx4 p0 = reinterpret_cast<const floatx4*>(part + tile * 8)[0];
     const floatx4 p1 = reinterpret_cast<const floatx4*>(part + tile * 8)[1];
-    const double tm = p0[0], tse = p0[1];
-    if (tm > lm) { lse = lse * exp(lm - tm) + tse; lm = tm; }
-    else lse += tse * exp(tm - lm);
-    const float cv[2] = {p0[2], p1[0]};
-    const int ci[2] = {__float_as_int(p0[3]), __float_as_int(p1[1])};
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float v = cv[q];
-      int i = ci[q];
-#pragma unroll
-      for (int k = 0; k < kTopK; ++k) {
-        if (ranks_before(v, i, c[k].v, c[k].i)) {
-          const float tv = c[k].v; const int ti = c[k].i;
-          c[k].v = v; c[k].i = i; v = tv; i = ti;
-        }
-      }
-    }
+    lse_merge(lm, lse, p0[0], p0[1]);
+    cand_insert(c, p0[2], __float_as_int(p0[3]));
+    cand_insert(c, p1[0], __float_as_int(p1[1]));
   }
 #pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) {
-    const double om = __shfl_xor(lm, mask), ose = __shfl_xor(lse, mask);
-    const double nm = fmax(lm, om);
-    lse = lse * exp(lm - nm) + ose * exp(om - nm);
-    lm = nm;
-  }
-  // wave top-K: K rounds of a (value desc, index asc) argmax; the winner pops.
-  Cand best[kTopK];
+  for (int mask = 32; mask >= 1; mask >>= 1) lse_merge(lm, lse, __shfl_xor(lm, mask), __shfl_xor(lse, mask));
+  // wave top-K: K rounds of a (value desc, index asc) argmax; the owner pops
+  Cand wb[kTopK];
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) {
     float bv = c[0].v;
@@ -443,71 +445,77 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
       const int oi = __shfl_xor(bi, mask);
       if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
-    best[k].v = bv;
-    best[k].i = bi;
-    if (bi == c[0].i && bi != 0x7fffffff) {          // this lane held the winner: pop it
+    wb[k].v = bv;
+    wb[k].i = bi;
+    if (bi == c[0].i && bi != 0x7fffffff) {
 #pragma unroll
       for (int q = 0; q < kTopK - 1; ++q) c[q] = c[q + 1];
       c[kTopK - 1].v = kNegInf;
       c[kTopK - 1].i = 0x7fffffff;
     }
   }
-  // exact fp32 re-score of the candidates from the fp32 h: lane covers 8
-  // consecutive elements per 512-wide stride; all candidates' rows in flight.
+  if (lane == 0) {
+    s_m[wave] = lm;
+    s_se[wave] = lse;
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) s_c[wave][k] = wb[k];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Cand best[kTopK];
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) { best[k].v = kNegInf; best[k].i = 0x7fffffff; }
+    for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+      for (int k = 0; k < kTopK; ++k) cand_insert(best, s_c[wv][k].v, s_c[wv][k].i);
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) s_best[k] = best[k];
+  }
+  __syncthreads();
+  // wave k re-scores candidate k
   const int b = m / a.n_c, cc = m % a.n_c;
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
   const WT* w = static_cast<const WT*>(a.w);
-  const WT* wr[kTopK];
-  bool okc[kTopK];
+  for (int k = wave; k < kTopK; k += 4) {
+    const int v = s_best[k].i;
+    const bool ok = v >= 0 && v < g.V;
+    const WT* wr = w + (int64_t)(ok ? v : 0) * g.hidden;
+    float sacc = 0.f;
+#pragma unroll 4
+    for (int e0 = 8 * lane; e0 < g.hidden; e0 += 8 * kWave) {
+      const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
+      const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
+      float wv[8];
+      W8<WT>::load(wr + e0, wv);
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    okc[k] = best[k].i >= 0 && best[k].i < g.V;
-    wr[k] = w + (int64_t)(okc[k] ? best[k].i : 0) * g.hidden;
-  }
-  float sacc[kTopK];
+      for (int e = 0; e < 4; ++e) sacc = fmaf(h0[e], wv[e], sacc);
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) sacc[k] = 0.f;
-#pragma unroll 2
-  for (int e0 = 8 * lane; e0 < g.hidden; e0 += 8 * kWave) {
-    const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
-    const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
-    float wv[kTopK][8];
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) W8<WT>::load(wr[k] + e0, wv[k]);
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[k] = fmaf(h0[e], wv[k][e], sacc[k]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[k] = fmaf(h1[e], wv[k][4 + e], sacc[k]);
+      for (int e = 0; e < 4; ++e) sacc = fmaf(h1[e], wv[4 + e], sacc);
     }
-  }
-  float ze[kTopK];
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    float s = sacc[k];
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
-    ze[k] = okc[k] ? s : kNegInf;
+    for (int mask = 32; mask >= 1; mask >>= 1) sacc += __shfl_xor(sacc, mask);
+    if (lane == 0) s_ze[k] = ok ? sacc : kNegInf;
   }
-  if (lane == 0) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bm = s_m[0], bse = s_se[0];
+    for (int wv = 1; wv < 4; ++wv) lse_merge(bm, bse, s_m[wv], s_se[wv]);
     int tb = 0;
 #pragma unroll
     for (int k = 1; k < kTopK; ++k)
-      if (ranks_before(ze[k], best[k].i, ze[tb], best[tb].i)) tb = k;
-    double mx = lm;
+      if (ranks_before(s_ze[k], s_best[k].i, s_ze[tb], s_best[tb].i)) tb = k;
+    double mx = bm;
 #pragma unroll
     for (int k = 0; k < kTopK; ++k)
-      if (ze[k] != kNegInf) mx = fmax(mx, (double)ze[k]);
-    double tot = lse * exp(lm - mx);
+      if (s_ze[k] != kNegInf) mx = fmax(mx, (double)s_ze[k]);
+    double tot = (double)bse * exp((double)bm - mx);
 #pragma unroll
     for (int k = 0; k < kTopK; ++k) {
-      if (ze[k] == kNegInf) continue;
-      tot += exp((double)ze[k] - mx) - exp((double)best[k].v - mx);
+      if (s_ze[k] == kNegInf) continue;
+      tot += exp((double)s_ze[k] - mx) - exp((double)s_best[k].v - mx);
     }
-    const double conf = exp((double)ze[tb] - mx) / tot;
-    a.conf[m] = (float)conf;
-    a.token[m] = best[tb].i;
+    a.conf[m] = (float)(exp((double)s_ze[tb] - mx) / tot);
+    a.token[m] = s_best[tb].i;
   }
 }
 
@@ -517,7 +525,7 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   const int M = g.B * a.n_c;
   if (M <= 0) return hipSuccess;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
-  const dim3 merge_grid((M + 3) / 4);
+  const dim3 merge_grid(M);
   if (g.fp32) {
     dim3 grid(n_vt, (M + 31) / 32);
     hipLaunchKernelGGL(k_screen_f32, grid, dim3(256), 0, s, g, a, M);
