@@ -28,8 +28,9 @@ thread_local std::string g_last_error;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-  size_t err, rope_cos, rope_sin, ktab, hhi, hlo, partials, zpart, tickets, total;
-  int ktab_rows;
+  size_t err, rope_cos, rope_sin, ktab, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart, tickets,
+      total;
+  int ktab_rows, r_pad;
   size_t zpart_bytes;
   int m_pad, n_vt, v_pad;
 };
@@ -42,6 +43,7 @@ bool config_ok(const mdm_config* c, std::string* why) {
   if (c->vocab <= 0 || c->seq_len <= 0) return fail("vocab and seq_len must be positive");
   if (c->n_registers < 0 || c->n_registers > kMaxRegisters) return fail("n_registers out of range");
   if (c->max_decode <= 0 || c->max_decode > c->seq_len) return fail("max_decode out of range");
+  if (c->precision == MDM_BF16 && c->max_decode > kAttnMaxDecode) return fail("max_decode above 2048 (bf16)");
   if (c->precision != MDM_BF16 && c->precision != MDM_FP32) return fail("unknown precision");
   if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta)) return fail("rope_theta must be finite and > 1");
   return true;
@@ -70,9 +72,18 @@ Layout layout_of(const mdm_config* c) {
   L.rope_sin = off; off = align_up(off + max_pos * (c->head_dim / 2) * sizeof(float), kAlign);
   const bool bf16 = c->precision == MDM_BF16;
   const size_t esz = bf16 ? 2 : 4;
-  // keys of the mask token at every position, then of the registers, per kv head
-  L.ktab_rows = (int)align_up((size_t)c->seq_len + c->n_registers, kKeyTile);
+  // keys of the mask token at every position, then of the registers, per kv
+  // head; rows up to seq_len + r_pad so whole register tiles stay in bounds
+  L.r_pad = (int)align_up((size_t)std::max(c->n_registers, 1), kKeyTile);
+  L.ktab_rows = c->seq_len + L.r_pad;
   L.ktab = off; off = align_up(off + (size_t)c->n_kv_heads * L.ktab_rows * c->head_dim * esz, kAlign);
+  // bf16 attention: value tables of the transient keys, key-split partials
+  const size_t kvd = (size_t)c->n_kv_heads * c->head_dim;
+  L.mvt = off; off = align_up(off + (bf16 ? kvd * 8 * sizeof(uint16_t) : 0), kAlign);
+  L.rvt = off; off = align_up(off + (bf16 ? kvd * L.r_pad * sizeof(uint16_t) : 0), kAlign);
+  const size_t slots_rows = (size_t)kAttnSplitBlocks * 8 * 32;
+  L.apart_o = off; off = align_up(off + (bf16 ? slots_rows * c->head_dim * sizeof(float) : 0), kAlign);
+  L.apart_ml = off; off = align_up(off + (bf16 ? slots_rows * 2 * sizeof(float) : 0), kAlign);
   const size_t hbytes = bf16 ? (size_t)L.m_pad * hidden * sizeof(uint16_t) : 0;
   L.hhi = off; off = align_up(off + hbytes, kAlign);
   L.hlo = off; off = align_up(off + ((bf16 && c->accurate_conf) ? hbytes : 0), kAlign);
@@ -205,9 +216,13 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
     ka.slot0 = 0; ka.err = err_word(ctx);
     st = hip_check(ctx, launch_append(gt, ka, ctx->stream), "key table");
   }
+  if (st == MDM_OK && !g.fp32)
+    st = hip_check(ctx, launch_value_tables(g, buf->tv, ctx->ws() + L.mvt, ctx->ws() + L.rvt, L.r_pad, ctx->stream),
+                   "value tables");
   if (st == MDM_OK)
     st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.tickets), 0,
                                         L.n_vt * (L.m_pad / 32), ctx->stream), "clear tickets");
+
   if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "init synchronize");
   if (st != MDM_OK) {
     delete ctx;
@@ -266,6 +281,11 @@ mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t*
   AttnArgs a{};
   a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
   a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
+  if (!ctx->g.fp32) {
+    a.mvt = ctx->ws() + ctx->L.mvt; a.rvt = ctx->ws() + ctx->L.rvt; a.r_pad = ctx->L.r_pad;
+    a.part_o = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_o);
+    a.part_ml = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_ml);
+  }
   a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
   a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
   a.d_tok = d_tok; a.d_pos = d_pos; a.d_stride = d_stride; a.c_pos = c_pos; a.c_stride = c_stride;

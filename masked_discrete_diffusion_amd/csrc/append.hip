@@ -92,6 +92,20 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   }
 }
 
+// One thread per (kv head, dim, j): j < 8 fills the mask token's value unit,
+// every j < r_pad fills one register column (zero past R).
+__global__ __launch_bounds__(256) void k_value_tables(Geometry g, const uint16_t* tv, uint16_t* mvt, uint16_t* rvt,
+                                                      int r_pad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)g.Hkv * g.D * r_pad;
+  if (i >= n) return;
+  const int j = (int)(i % r_pad);
+  const int col = (int)(i / r_pad);              // kvh * D + d
+  const int64_t kvd = (int64_t)g.Hkv * g.D;
+  if (j < 8) mvt[(int64_t)col * 8 + j] = tv[(int64_t)g.V * kvd + col];
+  rvt[i] = j < g.R ? tv[(int64_t)(g.V + 1 + j) * kvd + col] : (uint16_t)0;
+}
+
 __global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -110,6 +124,14 @@ hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s) 
     if (g.D == 128) hipLaunchKernelGGL((k_append<uint16_t, 128>), grid, dim3(256), 0, s, g, a);
     else hipLaunchKernelGGL((k_append<uint16_t, 64>), grid, dim3(256), 0, s, g, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_value_tables(const Geometry& g, const void* tv, void* mvt, void* rvt, int r_pad, hipStream_t s) {
+  const int64_t n = (int64_t)g.Hkv * g.D * r_pad;
+  hipLaunchKernelGGL(k_value_tables, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
+                     static_cast<const uint16_t*>(tv), static_cast<uint16_t*>(mvt), static_cast<uint16_t*>(rvt),
+                     r_pad);
   return hipGetLastError();
 }
 

@@ -2,34 +2,46 @@
 //
 // The query set of a step is [D | C | R]: rows entering the cache, the masked
 // rows decoded now, the registers (page 1, worked example = the paper's
-// Figure 3).  With keys in append order [cache (incl. D) | C | R], D rows see
-// the first S keys and C/R rows see all S + n_C + R keys, so the mask is a
-// visible prefix whose length depends only on the row kind.  Rows are cut into
-// 32-row chunks of a single kind, so every wavefront has one prefix length and
-// the mask is a wave-uniform key bound.  Keys past the bound are removed by
-// select (scores to -inf, values to 0), never multiplied by zero, so
-// invisible slots cannot leak even when they hold NaN.
+// Figure 3).  D rows see the cache (which already holds D); C and R rows see
+// the cache, every C key and every R key.  The keys a block streams are laid
+// out in three segments of 64-key tiles: the cache slots [0, S), the C keys,
+// the R keys (softmax does not depend on key order).  A D row's visible set is
+// the first segment, a C/R row's all three, so the mask is a per-wavefront
+// tile bound plus the valid count of a segment's last tile.  Rows are cut into
+// 32-row chunks of a single kind.  Keys past a tile's valid count are removed
+// by select (scores to -1e30, values to 0), never multiplied by zero, so stale
+// slots cannot leak even when they hold NaN.
 //
-// Keys in slots [0, S) come from the KV cache.  The C and R keys/values are
-// never stored in the cache: a C row is the mask token, so its key depends on
-// its position only, and a register's key is fixed; both are read from a key
-// table built once at init, and their values are rows of the value table.
+// C and R keys/values are never stored in the cache: a C row is the mask
+// token, so its key depends on its position only and its value is the same
+// for every C key; a register's key and value are fixed.  Tables built once at
+// init hold them in the layouts the tiles need: the keys of the mask token at
+// every position and of the registers (key table), the mask token's value
+// repeated as 8-key V^T units, and the registers' values transposed.
 //
 // bf16 path (block = 8 wavefronts = 8 chunks of 32 rows of the query heads of
-// one key/value head):
-//   K / V^T tiles of 64 keys go from HBM straight into LDS with
-//   global_load_lds_dwordx4 (no register staging) through a 4-deep ring, one
-//   barrier per tile; LDS rows are padded by 16 bytes so the MFMA operand
-//   reads are bank-conflict free with compile-time offsets.
+// one key/value head, over one contiguous range of the tiles):
+//   Every tile goes from HBM straight into LDS with global_load_lds_dwordx4
+//   (no register staging; per-lane source addresses gather the C keys' rows)
+//   through a 4-deep ring, one barrier per tile; LDS rows are padded by 16
+//   bytes so the MFMA operand reads are bank-conflict free with compile-time
+//   offsets.
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q^T in registers, RoPE'd in the
 //   prologue), fp32 online softmax with a lazily raised reference maximum
-//   (one partner exchange per tile for the row max), P split into bf16 hi +
-//   lo, O^T += V^T P_hi^T + V^T P_lo^T, fp32 out.
+//   (one partner exchange per half-tile for the row max), P split into bf16
+//   hi + lo, O^T += V^T P_hi^T + V^T P_lo^T, fp32 out.
 //   The key rows of the K operand are permuted so each lane's eight P values
 //   of a k-step are eight consecutive keys: the V^T operand is one 16-byte read.
-//   Block ids are remapped so that blocks sharing a head's keys/values sit on
-//   the same XCD (and L2).
+//   When there are fewer (sequence, kv head, chunk group) blocks than compute
+//   units, the tiles are split over several blocks; each writes its unscaled
+//   partial (O, row reference, row sum) and a second small kernel merges the
+//   partials in split order.  (A last-arriving-block merge inside the kernel
+//   needs device-scope fences, which write back and invalidate the whole L2
+//   of an XCD and cost more than the launch.)  Block ids are remapped so that
+//   the blocks of a group sit on one XCD (and L2).
 // fp32 path: the same mask with fp32 VALU arithmetic (validation mode).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,6 +57,7 @@ constexpr float kMaskedScore = -1e30f;
 constexpr int kAttnWaves = 8;                  // wavefronts per bf16 attention block
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kStages = 4;                     // LDS ring depth (tiles) of the bf16 kernel
+constexpr int kAhead = 2;                      // tiles loaded ahead of the one being computed
 
 struct RowInfo {
   int id, pos;
@@ -88,21 +101,24 @@ struct ChunkPlan {
   int chunks_d;     // chunks of D rows
   int n_chunks;     // D chunks then C|R chunks
   int per_block;    // chunks (wavefronts) per block
-  int blocks;       // blocks per (sequence, head)
-  int real_blocks;  // B * H * blocks (the grid may be padded to a multiple of 8)
+  int blocks;       // chunk groups per (sequence, kv head)
+  int ksplit;       // blocks sharing one chunk group's key tiles (bf16 path)
+  int real_blocks;  // B * Hkv * blocks * ksplit (the grid may be padded to a multiple of 8)
 };
 
+// Rows [base, end) of chunk ch; is_cr: a chunk of C|R rows (sees every key)
+// rather than D rows (see the cache only).
 __host__ __device__ inline void chunk_rows(const AttnArgs& a, const ChunkPlan& cp, int rows_per_chunk,
-                                           int ch, int& base, int& end, int& len) {
+                                           int ch, int& base, int& end, bool& is_cr) {
   if (ch < cp.chunks_d) {
     base = ch * rows_per_chunk;
     end = min(base + rows_per_chunk, a.n_d);
-    len = a.S;
+    is_cr = false;
   } else {
     const int cc = ch - cp.chunks_d;
     base = a.n_d + cc * rows_per_chunk;
     end = min(base + rows_per_chunk, a.n_d + a.n_c + a.n_r);
-    len = a.S + a.n_c + a.n_r;
+    is_cr = true;
   }
 }
 
@@ -127,79 +143,113 @@ struct AttnTile {
   static constexpr int BLOCKS = K_BLOCKS + V_BLOCKS;
   static constexpr int K_ELEMS = KT * KU * 8;        // bf16 elements per K tile
   static constexpr int V_ELEMS = D * VU * 8;
-  // DMA loads a wavefront issues per tile
-  __host__ __device__ static constexpr int loads_of(int wave) { return (BLOCKS - wave + kAttnWaves - 1) / kAttnWaves; }
+  // DMA loads per loading wavefront per tile: wavefront w issues blocks
+  // [w*LPW, w*LPW + LPW); the remaining wavefronts issue none, so every
+  // loading wavefront has the same count and the ring waits are constants.
+  static constexpr int LPW = (BLOCKS + kAttnWaves - 1) / kAttnWaves;
+  static_assert(BLOCKS % LPW == 0, "DMA blocks must split evenly over the loading wavefronts");
+  static constexpr int LOADERS = BLOCKS / LPW;
 };
 
+// Tile t of a block's key range: segment (0 cache, 1 C keys, 2 registers),
+// first key within the segment, number of valid keys (1..64).
+struct TileRef {
+  int seg, base, valid;
+};
+__device__ inline TileRef tile_ref(const AttnArgs& a, int T0, int T1, int t) {
+  if (t < T0) return TileRef{0, t * kKeyTile, min(kKeyTile, a.S - t * kKeyTile)};
+  t -= T0;
+  if (t < T1) return TileRef{1, t * kKeyTile, min(kKeyTile, a.n_c - t * kKeyTile)};
+  t -= T1;
+  return TileRef{2, t * kKeyTile, min(kKeyTile, a.n_r - t * kKeyTile)};
+}
+
+// Per-(sequence, kv head) sources of the three segments.
+struct KvSrc {
+  const uint16_t* kc;     // cache keys [slots][D]
+  const uint16_t* vc;     // cache values [D][slots]
+  const uint16_t* ktab;   // key table [ktab_rows][D]
+  const uint16_t* mvt;    // mask-token value units [D][8]
+  const uint16_t* rvt;    // register values [D][r_pad]
+  const int* kidx;        // LDS: key-table row of each C key
+};
+
+// Byte offsets, per lane, of this wavefront's DMA units for a cache tile,
+// relative to the tile's first key (K) or first slot (V^T): K unit (row r,
+// chunk c) -> r*D + c, V^T unit (dim d, chunk c) -> d*slots + c (elements,
+// times 2).  A pad unit (c = last) loads chunk 0 of its row, never read.
 template <int D>
-__device__ inline void tile_dma(const uint16_t* kc, const uint16_t* vc, int slots, int kt, uint16_t* ks,
-                                uint16_t* vs) {
+__device__ inline void dma_offsets(int wave, int lane, int slots, uint32_t (&off)[AttnTile<D>::LPW]) {
   using T = AttnTile<D>;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int i = 0; i < (T::BLOCKS + kAttnWaves - 1) / kAttnWaves; ++i) {
-    const int blk = wave + kAttnWaves * i;
+  for (int i = 0; i < T::LPW; ++i) {
+    const int blk = min(wave * T::LPW + i, T::BLOCKS - 1);
     if (blk < T::K_BLOCKS) {
       const int u = blk * kWave + lane;
       const int r = u / T::KU, c = u % T::KU;
-      const uint16_t* gk = kc + (int64_t)(kt + r) * D + (c < T::KC ? c : 0) * 8;
-      dma16(gk, ks + blk * kWave * 8);
-    } else if (blk < T::BLOCKS) {
-      const int vb = blk - T::K_BLOCKS;
-      const int u = vb * kWave + lane;
+      off[i] = 2u * (uint32_t)(r * D + (c < T::KC ? c : 0) * 8);
+    } else {
+      const int u = (blk - T::K_BLOCKS) * kWave + lane;
       const int d = u / T::VU, c = u % T::VU;
-      const uint16_t* gv = vc + (int64_t)d * slots + kt + (c < T::VC ? c : 0) * 8;
-      dma16(gv, vs + vb * kWave * 8);
+      off[i] = 2u * (uint32_t)(d * slots + (c < T::VC ? c : 0) * 8);
     }
   }
 }
 
-// A tile reaching past S: cached slots from the cache, transient slots from the
-// key table and the value table, slots past S + n_C + R zero.  Same layout.
-// Synchronous: its loads complete (and with them every older load) before return.
+// Issue this wavefront's LDS-DMA loads of one tile (segment, first key base).
+// Rows past the valid count load in-bounds rows (spare cache slots, clamped
+// C index, key-table padding, zero register columns); select removes them.
 template <int D>
-__device__ inline void tile_edge(const Geometry& g, const AttnArgs& a, int b, int kvh, const uint16_t* kc,
-                                 const uint16_t* vc, int kt, uint16_t* ks, uint16_t* vs) {
+__device__ inline void tile_dma(const AttnArgs& a, const Geometry& g, const KvSrc& src, const TileRef& tr,
+                                int wave, int lane, const uint32_t (&off)[AttnTile<D>::LPW], uint16_t* ks,
+                                uint16_t* vs) {
   using T = AttnTile<D>;
-  const uint16_t* ktab = static_cast<const uint16_t*>(a.ktab) + (int64_t)kvh * a.ktab_rows * D;
-  const uint16_t* tv = static_cast<const uint16_t*>(a.tv);
-  const int kvd = g.Hkv * D;
-  const int s_tot = a.S + a.n_c + a.n_r;
-  for (int u = threadIdx.x; u < T::K_BLOCKS * kWave; u += kAttnThreads) {
-    const int r = u / T::KU, c = u % T::KU;
-    const int slot = kt + r;
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < T::KC) {
-      if (slot < a.S) {
-        v = *reinterpret_cast<const u16x8*>(kc + (int64_t)slot * D + c * 8);
-      } else if (slot < s_tot) {
-        const int krow = transient_krow(g, a, b, slot - a.S);
-        v = *reinterpret_cast<const u16x8*>(ktab + (int64_t)krow * D + c * 8);
-      }
-    }
-    *reinterpret_cast<u16x8*>(ks + u * 8) = v;
-  }
-  for (int u = threadIdx.x; u < T::V_BLOCKS * kWave; u += kAttnThreads) {
-    const int d = u / T::VU, c = u % T::VU;
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < T::VC) {
-      const int slot0 = kt + c * 8;
+  if (wave >= T::LOADERS) return;
+  // C-key and register tiles (at most one or two per block) compute their
+  // per-lane offsets here; the opaque copy of the lane id keeps the compiler
+  // from hoisting them out of the tile loop, where they would need VGPRs.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const uint16_t* kbase = tr.seg == 0 ? src.kc + (int64_t)tr.base * D
+                                      : src.ktab + (int64_t)(g.seq_len + tr.base) * D;   // seg 2 (seg 1 below)
+  const uint16_t* vbase = src.vc + tr.base;                                            // seg 0
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sl = slot0 + e;
-        if (sl < a.S) v[e] = vc[(int64_t)d * g.slots + sl];
-        else if (sl < s_tot) v[e] = tv[(int64_t)transient_id(g, a, sl - a.S) * kvd + kvh * D + d];
+  for (int i = 0; i < T::LPW; ++i) {
+    const int blk = wave * T::LPW + i;
+    if (blk < T::K_BLOCKS) {
+      uint16_t* dst = ks + blk * kWave * 8;
+      if (tr.seg != 1) {
+        dma16(kbase, off[i], dst);
+      } else {
+        const int u = blk * kWave + ln;
+        const int r = u / T::KU, c = u % T::KU;
+        const int row = src.kidx[min(tr.base + r, a.n_c - 1)];
+        dma16(src.ktab, 2u * (uint32_t)(row * D + (c < T::KC ? c : 0) * 8), dst);
+      }
+    } else {
+      const int vb = blk - T::K_BLOCKS;
+      uint16_t* dst = vs + vb * kWave * 8;
+      if (tr.seg == 0) {
+        dma16(vbase, off[i], dst);
+      } else {
+        const int u = vb * kWave + ln;
+        const int d = u / T::VU, c = u % T::VU;
+        if (tr.seg == 1) dma16(src.mvt, 16u * (uint32_t)d, dst);
+        else dma16(src.rvt + tr.base, 2u * (uint32_t)(d * a.r_pad + (c < T::VC ? c : 0) * 8), dst);
       }
     }
-    *reinterpret_cast<u16x8*>(vs + u * 8) = v;
   }
 }
 
-template <int D>
-__device__ inline void tile_fill(const Geometry& g, const AttnArgs& a, int b, int kvh, const uint16_t* kc,
-                                 const uint16_t* vc, int kt, uint16_t* ks, uint16_t* vs) {
-  if (kt + kKeyTile <= a.S) tile_dma<D>(kc, vc, g.slots, kt, ks, vs);
-  else tile_edge<D>(g, a, b, kvh, kc, vc, kt, ks, vs);
+// Wait for tile i of the ring when `younger` later tiles may stay in flight.
+// (kAhead tiles are loaded ahead; the lagging wavefronts still read the
+// previous tile's buffer, so a 4-deep ring leaves kAhead = 2.)
+template <int LPW>
+__device__ inline void ring_wait_tiles(int younger) {
+  static_assert(kAhead == 2 && kStages >= kAhead + 2, "waits are spelled out for two tiles ahead");
+  if (younger >= 2) ring_wait<LPW>();
+  else if (younger == 1) ring_wait<LPW>();
+  else ring_wait<0>();
 }
 
 // Split p into bf16 hi + lo for a pair of values, packed two per word.
@@ -229,6 +279,19 @@ __device__ inline float max3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// Combine a value of lane l with lane l ^ 32 (the other half of the row's
+// lanes) through v_permlane32_swap: the swap leaves (own, partner) in lanes
+// 0-31 and (partner, own) in lanes 32-63, so max/sum of the pair is the same
+// commutative operation on every lane.
+__device__ inline float halves_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Softmax of one 32-key half for this lane's row: lazily raise the reference
 // (rescaling O and l when a row maximum passes it by more than kRescaleLog2),
 // then p = exp2(s * sc - m_ref) in place and their sum added to l.
@@ -246,7 +309,7 @@ __device__ inline void half_softmax(floatx16& sv, floatx16* acc, float& m_ref, f
   float mt = max3(sv[0], sv[1], sv[2]);
 #pragma unroll
   for (int e = 3; e < 15; e += 2) mt = max3(mt, sv[e], sv[e + 1]);
-  mt = max3(mt, sv[15], __shfl_xor(max3(mt, sv[15], sv[15]), 32)) * sc;
+  mt = halves_max(max3(mt, sv[15], sv[15])) * sc;
   if (__any(mt > m_ref + kRescaleLog2)) {
     const float m_new = fmaxf(m_ref, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -266,12 +329,17 @@ __device__ inline void half_softmax(floatx16& sv, floatx16* acc, float& m_ref, f
   l_run += lsum;
 }
 
-// O^T += V^T (P_hi + P_lo)^T for one 32-key half (two 16-key k-steps).
-template <int NDB, bool kEdge>
-__device__ inline void half_pv(const floatx16& p, const u16x8 (*vf)[NDB], floatx16* acc, int key_base, int wlen,
+// O^T += V^T (P_hi + P_lo)^T for one 32-key half (two 16-key k-steps).  The
+// V^T operands are read from LDS per k-step (vhalf: first unit of this half in
+// this lane's V^T rows); the scheduler hoists the reads as far as registers allow.
+template <int D, bool kEdge>
+__device__ inline void half_pv(const floatx16& p, const uint16_t* vhalf, floatx16* acc, int key_base, int wlen,
                                int half) {
+  using T = AttnTile<D>;
+  constexpr int NDB = D / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
+    if (u > 0) __builtin_amdgcn_sched_barrier(0);   // one k-step's V operands in flight
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 hi, lo;
 #pragma unroll
@@ -285,7 +353,7 @@ __device__ inline void half_pv(const floatx16& p, const u16x8 (*vf)[NDB], floatx
     bf16x8 v[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      u16x8 raw = vf[u][db];
+      u16x8 raw = *reinterpret_cast<const u16x8*>(vhalf + (32 * db * T::VU + 2 * u) * 8);
       if (kEdge) {
         const int key0 = key_base + 16 * u + 8 * half;
 #pragma unroll
@@ -300,45 +368,89 @@ __device__ inline void half_pv(const floatx16& p, const u16x8 (*vf)[NDB], floatx
   }
 }
 
-// One 64-key tile for one wavefront (32 query rows), as two 32-key halves
-// pipelined so that each half's softmax (VALU) can run while the other half's
-// MFMAs execute: S0, S1 issued; softmax(S0) overlaps S1; PV(0) issued;
-// softmax(S1) overlaps PV(0); PV(1).  kEdge: keys at or past wlen are
-// removed by select.
-template <int D, bool kEdge>
-__device__ inline void attn_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf, floatx16* acc,
-                                 float& m_ref, float& l_run, int kt, int wlen, int krow, int half, int l32,
-                                 float sc) {
+// S^T for one 32-key half hk of a tile: lane holds keys 16(jj/2) + 8*half +
+// 4(jj%2) + ii of the half for row l32 (K rows permuted, see krow).
+template <int D>
+__device__ inline floatx16 s_half(const uint16_t* kb, const bf16x8* qf, int hk, int krow, int half) {
   using T = AttnTile<D>;
   constexpr int NKS = D / 16;
-  constexpr int NDB = D / 32;
-  const uint16_t* kbase = kb + (krow * T::KU + half) * 8;
-  const uint16_t* vbase = vb + (l32 * T::VU + half) * 8;
-  floatx16 s0, s1;
+  const uint16_t* kbase = kb + ((32 * hk + krow) * T::KU + half) * 8;
+  floatx16 sv;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+  for (int e = 0; e < 16; ++e) sv[e] = 0.f;
 #pragma unroll
   for (int t = 0; t < NKS; ++t) {
-    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
-    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kbase + (32 * T::KU + 2 * t) * 8);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[t], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[t], s1, 0, 0, 0);
+    // at most four K operands in flight: the scheduler would otherwise hoist
+    // all eight LDS reads (32 VGPRs) above the MFMA chain
+    if (t % 4 == 0 && t > 0) __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
+    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv, 0, 0, 0);
   }
-  u16x8 vf[2][NDB];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 2 * u) * 8);
-  half_softmax<NDB, kEdge>(s0, acc, m_ref, l_run, kt, wlen, half, sc);
-  half_pv<NDB, kEdge>(s0, vf, acc, kt, wlen, half);
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      vf[u][db] = *reinterpret_cast<const u16x8*>(vbase + (32 * db * T::VU + 4 + 2 * u) * 8);
-  half_softmax<NDB, kEdge>(s1, acc, m_ref, l_run, kt + 32, wlen, half, sc);
-  half_pv<NDB, kEdge>(s1, vf, acc, kt + 32, wlen, half);
+  return sv;
+}
+
+// Softmax and O += V P for half hk of a tile whose first `valid` keys count
+// (valid < 64: the rest are removed by select).
+template <int D>
+__device__ inline void finish_half(floatx16& sv, const uint16_t* vb, int hk, int valid, floatx16* acc,
+                                   float& m_ref, float& l_run, int half, int l32, float sc) {
+  using T = AttnTile<D>;
+  constexpr int NDB = D / 32;
+  const uint16_t* vhalf = vb + (l32 * T::VU + half + 4 * hk) * 8;
+  if (valid < kKeyTile) {
+    half_softmax<NDB, true>(sv, acc, m_ref, l_run, 32 * hk, valid, half, sc);
+    half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
+  } else {
+    half_softmax<NDB, false>(sv, acc, m_ref, l_run, 32 * hk, valid, half, sc);
+    half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
+  }
+}
+
+// The tile loop of one wavefront.  LAG = false: both halves of tile i in
+// iteration i.  LAG = true (the second wavefront of each SIMD): iteration i
+// first finishes the second half of tile i-1 (scores carried in registers,
+// V still in its ring slot), then the first half of tile i, and leaves the
+// second half's scores for the next iteration.  The two wavefronts of a SIMD
+// are then in different phases (one in MFMA, the other in softmax VALU work)
+// instead of in lockstep after every barrier.
+template <int D, bool LAG>
+__device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvSrc& src,
+                                 const uint32_t (&off)[AttnTile<D>::LPW], uint16_t (*ks)[AttnTile<D>::K_ELEMS],
+                                 uint16_t (*vs)[AttnTile<D>::V_ELEMS], const bf16x8* qf, floatx16* acc, float& m_ref,
+                                 float& l_run, int T0, int T1, int t_lo, int n_my, int w_end, bool active, int wave,
+                                 int lane, int krow, int half, int l32, float sc) {
+  using T = AttnTile<D>;
+  floatx16 sv_carry;
+  int carry_valid = 0, carry_buf = 0;      // carry_valid > 0: a second half is pending
+  for (int i = 0; i < n_my; ++i) {
+    ring_wait_tiles<T::LPW>(n_my - 1 - i);
+    ring_barrier();
+    const int nxt = i + kAhead;
+    if (nxt < n_my)
+      tile_dma<D>(a, g, src, tile_ref(a, T0, T1, t_lo + nxt), wave, lane, off, ks[nxt % kStages],
+                  vs[nxt % kStages]);
+    if (!active) continue;
+    if (LAG && carry_valid > 0) {
+      finish_half<D>(sv_carry, vs[carry_buf], 1, carry_valid, acc, m_ref, l_run, half, l32, sc);
+      carry_valid = 0;
+    }
+    const int t = t_lo + i;
+    if (t >= w_end) continue;
+    const TileRef tr = tile_ref(a, T0, T1, t);
+    const int cur = i % kStages;
+    floatx16 sv = s_half<D>(ks[cur], qf, 0, krow, half);
+    finish_half<D>(sv, vs[cur], 0, tr.valid, acc, m_ref, l_run, half, l32, sc);
+    if (LAG) {
+      sv_carry = s_half<D>(ks[cur], qf, 1, krow, half);
+      carry_valid = tr.valid;
+      carry_buf = cur;
+    } else {
+      sv = s_half<D>(ks[cur], qf, 1, krow, half);
+      finish_half<D>(sv, vs[cur], 1, tr.valid, acc, m_ref, l_run, half, l32, sc);
+    }
+  }
+  if (LAG && carry_valid > 0)
+    finish_half<D>(sv_carry, vs[carry_buf], 1, carry_valid, acc, m_ref, l_run, half, l32, sc);
 }
 
 // Block: kAttnWaves wavefronts, each owning one 32-row chunk of one query head;
@@ -351,21 +463,23 @@ __device__ inline void attn_tile(const uint16_t* kb, const uint16_t* vb, const b
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnArgs a, ChunkPlan cp) {
   using T = AttnTile<D>;
-  constexpr int KT = kKeyTile;
   constexpr int NKS = D / 16;           // k-steps of the QK^T product
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
   __shared__ __align__(1024) uint16_t ks[kStages][T::K_ELEMS];
   __shared__ __align__(1024) uint16_t vs[kStages][T::V_ELEMS];
+  __shared__ int kidx[kAttnMaxDecode];
 
   const int n_grid = gridDim.x;
   const int logical = (blockIdx.x % 8) * (n_grid / 8) + blockIdx.x / 8;
   if (logical >= cp.real_blocks) return;
   const int G = g.H / g.Hkv;
-  const int j = logical % cp.blocks;
-  const int bk = logical / cp.blocks;
+  const int split = logical % cp.ksplit;
+  const int group = logical / cp.ksplit;
+  const int j = group % cp.blocks;
+  const int bk = group / cp.blocks;
   const int kvh = bk % g.Hkv;
   const int b = bk / g.Hkv;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
   const int l32 = lane % 32;
@@ -374,21 +488,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   // of the group, local chunk c % n_chunks
   const int c0 = j * cp.per_block;
   const int c1 = min(G * cp.n_chunks, c0 + cp.per_block);
-  int kend = 0;
-  for (int c = c0; c < c1; ++c) kend = max(kend, (c % cp.n_chunks) >= cp.chunks_d ? a.S + a.n_c + a.n_r : a.S);
+  bool any_cr = false;
+  for (int c = c0; c < c1; ++c) any_cr |= (c % cp.n_chunks) >= cp.chunks_d;
   const int ch = c0 + wave;
   const bool active = ch < c1;
   const int h = kvh * G + (active ? ch / cp.n_chunks : 0);
-  int row_base = 0, row_end = 0, wlen = 0;
-  if (active) chunk_rows(a, cp, 32, ch % cp.n_chunks, row_base, row_end, wlen);
+  int row_base = 0, row_end = 0;
+  bool is_cr = false;
+  if (active) chunk_rows(a, cp, 32, ch % cp.n_chunks, row_base, row_end, is_cr);
   const int row = row_base + l32;
   const bool rvalid = active && row < row_end;
 
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + ((int64_t)b * g.Hkv + kvh) * g.slots * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + ((int64_t)b * g.Hkv + kvh) * D * g.slots;
+  // this block's tiles [t_lo, t_hi) of the segmented key range
+  const int T0 = (a.S + kKeyTile - 1) / kKeyTile;
+  const int T1 = (a.n_c + kKeyTile - 1) / kKeyTile;
+  const int T2 = (a.n_r + kKeyTile - 1) / kKeyTile;
+  const int kend = any_cr ? T0 + T1 + T2 : T0;
+  const int tps = (kend + cp.ksplit - 1) / cp.ksplit;
+  const int t_lo = min(kend, split * tps);
+  const int n_my = min(kend, t_lo + tps) - t_lo;
+  const int w_end = is_cr ? T0 + T1 + T2 : T0;       // tiles this wavefront's rows see
 
-  const int n_tiles = (kend + KT - 1) / KT;
-  for (int t = 0; t < kStages - 1 && t < n_tiles; ++t) tile_fill<D>(g, a, b, kvh, kc, vc, t * KT, ks[t], vs[t]);
+  // key-table rows of the C keys, if this block streams any C tile
+  if (T1 > 0 && t_lo < T0 + T1 && t_lo + n_my > T0) {
+    for (int jj = threadIdx.x; jj < a.n_c; jj += kAttnThreads) {
+      int pos = a.c_pos[(int64_t)b * a.c_stride + jj];
+      if (pos < 0 || pos >= g.seq_len) { flag_error(a.err, kErrPos); pos = 0; }
+      kidx[jj] = pos;
+    }
+  }
+  __syncthreads();
+
+  KvSrc src;
+  src.kc = static_cast<const uint16_t*>(a.kc) + ((int64_t)b * g.Hkv + kvh) * g.slots * D;
+  src.vc = static_cast<const uint16_t*>(a.vc) + ((int64_t)b * g.Hkv + kvh) * D * g.slots;
+  src.ktab = static_cast<const uint16_t*>(a.ktab) + (int64_t)kvh * a.ktab_rows * D;
+  src.mvt = static_cast<const uint16_t*>(a.mvt) + (int64_t)kvh * D * 8;
+  src.rvt = static_cast<const uint16_t*>(a.rvt) + (int64_t)kvh * D * a.r_pad;
+  src.kidx = kidx;
+
+  uint32_t off[T::LPW];
+  dma_offsets<D>(wave, lane, g.slots, off);
+  for (int i = 0; i < kAhead && i < n_my; ++i)
+    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, t_lo + i), wave, lane, off, ks[i], vs[i]);
 
   // Q^T fragment (B operand): lane holds row l32, dims 16t + 8*half + 0..7, RoPE'd.
   bf16x8 qf[NKS];
@@ -427,35 +569,108 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
     for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
   float m_ref = -1e30f, l_run = 0.f;     // softmax reference (log2 units) and row sum
   const float sc = kLog2e / sqrtf((float)D);
-  const int my_loads = T::loads_of(wave);
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int younger = min(kStages - 2, n_tiles - 1 - t);
-    ring_wait(younger * my_loads);
-    ring_barrier();
-    const int nxt = t + kStages - 1;
-    if (nxt < n_tiles) tile_fill<D>(g, a, b, kvh, kc, vc, nxt * KT, ks[nxt % kStages], vs[nxt % kStages]);
-    const int kt = t * KT;
-    if (!active || kt >= wlen) continue;
-    const int cur = t % kStages;
-    if (kt + KT > wlen) attn_tile<D, true>(ks[cur], vs[cur], qf, acc, m_ref, l_run, kt, wlen, krow, half, l32, sc);
-    else attn_tile<D, false>(ks[cur], vs[cur], qf, acc, m_ref, l_run, kt, wlen, krow, half, l32, sc);
+  // Wavefronts 0-3 take a tile's halves in order within the iteration;
+  // wavefronts 4-7 (the second wavefront of each SIMD) run half a tile
+  // behind (see tile_loop).
+  if (wave >= kAttnWaves / 2)
+    tile_loop<D, true>(a, g, src, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, t_lo, n_my, w_end, active, wave, lane,
+                       krow, half, l32, sc);
+  else
+    tile_loop<D, false>(a, g, src, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, t_lo, n_my, w_end, active, wave, lane,
+                        krow, half, l32, sc);
+
+  const float l_tot = halves_sum(l_run);
+  const int n_q = a.n_d + a.n_c + a.n_r;
+  float* o = a.out + ((int64_t)b * n_q + row) * g.hidden + h * D;
+  if (cp.ksplit == 1) {
+    if (rvalid) {
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          floatx4 v;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii] * inv;
+          *reinterpret_cast<floatx4*>(o + 32 * db + 8 * jj + 4 * half) = v;
+        }
+    }
+    return;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (rvalid) {
-    const float inv = 1.f / l_tot;
-    const int n_q = a.n_d + a.n_c + a.n_r;
-    float* o = a.out + ((int64_t)b * n_q + row) * g.hidden + h * D;
+  // Split: publish this block's unscaled partial; k_attn_combine merges them.
+  if (!active) return;
+  float* po = a.part_o + ((int64_t)logical * kAttnWaves + wave) * 32 * D + l32 * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        floatx4 v;
+    for (int jj = 0; jj < 4; ++jj) {
+      floatx4 v;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii] * inv;
-        *reinterpret_cast<floatx4*>(o + 32 * db + 8 * jj + 4 * half) = v;
-      }
+      for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii];
+      *reinterpret_cast<floatx4*>(po + 32 * db + 8 * jj + 4 * half) = v;
+    }
+  if (half == 0) {
+    float* pml = a.part_ml + ((int64_t)logical * kAttnWaves + wave) * 64;
+    pml[2 * l32] = m_ref;
+    pml[2 * l32 + 1] = l_tot;
+  }
+}
+
+// Merge of the key-split partials: block = one chunk group, wavefront w = its
+// chunk w; lane: row lane/2, dims [D/2 * (lane%2), +D/2).  Splits are folded
+// in split order (fixed arithmetic, independent of which block ran first):
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(Geometry g, AttnArgs a, ChunkPlan cp) {
+  constexpr int HD = D / 2;
+  const int group = blockIdx.x;
+  const int G = g.H / g.Hkv;
+  const int j = group % cp.blocks;
+  const int bk = group / cp.blocks;
+  const int kvh = bk % g.Hkv;
+  const int b = bk / g.Hkv;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c0 = j * cp.per_block;
+  const int c1 = min(G * cp.n_chunks, c0 + cp.per_block);
+  const int ch = c0 + wave;
+  if (ch >= c1) return;
+  const int h = kvh * G + ch / cp.n_chunks;
+  int row_base, row_end;
+  bool is_cr;
+  chunk_rows(a, cp, 32, ch % cp.n_chunks, row_base, row_end, is_cr);
+  const int r = lane / 2, part = lane % 2;
+  const int row = row_base + r;
+  if (row >= row_end) return;
+  const int64_t slot0 = (int64_t)group * cp.ksplit;
+  float mx = -1e30f;
+  for (int s = 0; s < cp.ksplit; ++s) mx = fmaxf(mx, a.part_ml[((slot0 + s) * kAttnWaves + wave) * 64 + 2 * r]);
+  floatx4 sum[HD / 4];
+#pragma unroll
+  for (int q = 0; q < HD / 4; ++q) sum[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  for (int s = 0; s < cp.ksplit; ++s) {
+    const int64_t slot = (slot0 + s) * kAttnWaves + wave;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[slot * 64 + 2 * r] - mx);
+    lsum = fmaf(w, a.part_ml[slot * 64 + 2 * r + 1], lsum);
+    const floatx4* ps = reinterpret_cast<const floatx4*>(a.part_o + slot * 32 * D + r * D + part * HD);
+#pragma unroll
+    for (int q = 0; q < HD / 4; ++q) {
+      const floatx4 v = ps[q];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sum[q][ii] = fmaf(w, v[ii], sum[q][ii]);
+    }
+  }
+  const float inv = 1.f / lsum;
+  const int n_q = a.n_d + a.n_c + a.n_r;
+  floatx4* o = reinterpret_cast<floatx4*>(a.out + ((int64_t)b * n_q + row) * g.hidden + h * D + part * HD);
+#pragma unroll
+  for (int q = 0; q < HD / 4; ++q) {
+    floatx4 v;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) v[ii] = sum[q][ii] * inv;
+    o[q] = v;
   }
 }
 
@@ -474,8 +689,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(Geometry g, AttnArgs a, ChunkP
   const int h = bh % g.H;
   const int b = bh / g.H;
   const int kvh = h / (g.H / g.Hkv);
-  int row_base, row_end, wlen;
-  chunk_rows(a, cp, 64, ch, row_base, row_end, wlen);
+  int row_base, row_end;
+  bool is_cr;
+  chunk_rows(a, cp, 64, ch, row_base, row_end, is_cr);
+  const int wlen = is_cr ? a.S + a.n_c + a.n_r : a.S;
   const int t = threadIdx.x;
   const int qpart = t % 4;
   const int row = row_base + t / 4;
@@ -578,20 +795,35 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
   if (g.fp32) {
     cp.per_block = 1;
     cp.blocks = cp.n_chunks;
+    cp.ksplit = 1;
     cp.real_blocks = g.B * g.H * cp.n_chunks;
     dim3 grid(cp.real_blocks);
     if (g.D == 128) hipLaunchKernelGGL((k_attn_f32<128>), grid, dim3(256), 0, s, g, a, cp);
     else hipLaunchKernelGGL((k_attn_f32<64>), grid, dim3(256), 0, s, g, a, cp);
   } else {
+    if (a.n_c > kAttnMaxDecode) return hipErrorInvalidValue;
     const int G = g.H / g.Hkv;
     const int space = G * cp.n_chunks;                 // chunks per (sequence, kv head)
     const int nb = (space + kAttnWaves - 1) / kAttnWaves;
     cp.blocks = nb;
     cp.per_block = (space + nb - 1) / nb;
-    cp.real_blocks = g.B * g.Hkv * nb;
+    const int groups = g.B * g.Hkv * nb;
+    // split the key tiles while the groups leave compute units idle, keeping
+    // at least kAttnMinSplitTiles tiles per block
+    const int tiles = (a.S + kKeyTile - 1) / kKeyTile + (a.n_c + kKeyTile - 1) / kKeyTile +
+                      (a.n_r + kKeyTile - 1) / kKeyTile;
+    int ks = 1;
+    if (groups < kAttnSplitBlocks && a.part_o)
+      ks = std::max(1, std::min(std::min(kAttnSplitBlocks / groups, kAttnMaxSplit), tiles / kAttnMinSplitTiles));
+    cp.ksplit = ks;
+    cp.real_blocks = groups * ks;
     dim3 grid((cp.real_blocks + 7) / 8 * 8);
     if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     else hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+    if (ks > 1) {
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(groups), dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_combine<64>), dim3(groups), dim3(kAttnThreads), 0, s, g, a, cp);
+    }
   }
   return hipGetLastError();
 }

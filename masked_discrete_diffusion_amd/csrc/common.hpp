@@ -73,8 +73,9 @@ __device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
 
 // ---- LDS-DMA rings -----------------------------------------------------------
 // A wave-wide global_load_lds_dwordx4 writes 64 consecutive 16-byte units of
-// LDS starting at `lds_block` (uniform); lane l's 16 bytes come from its own
-// global address `src` and land in unit l.
+// LDS starting at `lds_block` (uniform); lane l's 16 bytes come from
+// base + off_l (base uniform, in SGPRs; off_l a per-lane byte offset) and
+// land in unit l.
 //
 // Issued from inline asm on purpose: the compiler treats an LDS-DMA load it
 // can see as a pending write to any LDS it cannot prove disjoint, and then
@@ -84,62 +85,20 @@ __device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
 // own vmcnt waits for its loads only become stricter (the counter retires in
 // issue order).  M0 holds the LDS base; nothing else in these kernels uses M0,
 // and one wait state separates its write from the load.
-__device__ inline void dma16(const void* src, void* lds_block) {
+__device__ inline void dma16(const void* base, uint32_t off, void* lds_block) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(void __attribute__((address_space(3)))*)lds_block);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory");
 }
 
-// Wait until at most n of this wavefront's vector-memory operations are in
+// Wait until at most N of this wavefront's vector-memory operations are in
 // flight, and its LDS operations are done.  vmcnt retires in issue order, so
-// with n = (loads this wave issued after tile i) it waits exactly for tile i.
-// The immediate must be a constant: dispatch over the counts a ring asks for;
-// anything larger waits for everything, which is always correct.
-__device__ inline void ring_wait(int n) {
-  switch (n) {
-    case 1: asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
-    case 11: asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory"); break;
-    case 13: asm volatile("s_waitcnt vmcnt(13) lgkmcnt(0)" ::: "memory"); break;
-    case 14: asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)" ::: "memory"); break;
-    case 15: asm volatile("s_waitcnt vmcnt(15) lgkmcnt(0)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory"); break;
-    case 17: asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)" ::: "memory"); break;
-    case 18: asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)" ::: "memory"); break;
-    case 19: asm volatile("s_waitcnt vmcnt(19) lgkmcnt(0)" ::: "memory"); break;
-    case 20: asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory"); break;
-    case 21: asm volatile("s_waitcnt vmcnt(21) lgkmcnt(0)" ::: "memory"); break;
-    case 22: asm volatile("s_waitcnt vmcnt(22) lgkmcnt(0)" ::: "memory"); break;
-    case 23: asm volatile("s_waitcnt vmcnt(23) lgkmcnt(0)" ::: "memory"); break;
-    case 24: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory"); break;
-    case 25: asm volatile("s_waitcnt vmcnt(25) lgkmcnt(0)" ::: "memory"); break;
-    case 26: asm volatile("s_waitcnt vmcnt(26) lgkmcnt(0)" ::: "memory"); break;
-    case 27: asm volatile("s_waitcnt vmcnt(27) lgkmcnt(0)" ::: "memory"); break;
-    case 28: asm volatile("s_waitcnt vmcnt(28) lgkmcnt(0)" ::: "memory"); break;
-    case 29: asm volatile("s_waitcnt vmcnt(29) lgkmcnt(0)" ::: "memory"); break;
-    case 30: asm volatile("s_waitcnt vmcnt(30) lgkmcnt(0)" ::: "memory"); break;
-    case 31: asm volatile("s_waitcnt vmcnt(31) lgkmcnt(0)" ::: "memory"); break;
-    case 32: asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory"); break;
-    case 33: asm volatile("s_waitcnt vmcnt(33) lgkmcnt(0)" ::: "memory"); break;
-    case 34: asm volatile("s_waitcnt vmcnt(34) lgkmcnt(0)" ::: "memory"); break;
-    case 35: asm volatile("s_waitcnt vmcnt(35) lgkmcnt(0)" ::: "memory"); break;
-    case 36: asm volatile("s_waitcnt vmcnt(36) lgkmcnt(0)" ::: "memory"); break;
-    case 37: asm volatile("s_waitcnt vmcnt(37) lgkmcnt(0)" ::: "memory"); break;
-    case 38: asm volatile("s_waitcnt vmcnt(38) lgkmcnt(0)" ::: "memory"); break;
-    case 39: asm volatile("s_waitcnt vmcnt(39) lgkmcnt(0)" ::: "memory"); break;
-    case 40: asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-  }
+// with N = (loads this wave issued after tile i) it waits exactly for tile i.
+template <int N>
+__device__ inline void ring_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate out of range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier without the release fence of __syncthreads (that fence

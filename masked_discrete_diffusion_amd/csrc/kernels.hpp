@@ -37,12 +37,28 @@ struct AppendArgs {
 };
 hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s);
 
+// Value tables of the transient keys (bf16): mvt[kvh][d][0..7] = value of the
+// mask token, rvt[kvh][d][j] = value of register j (0 for j >= R).
+hipError_t launch_value_tables(const Geometry& g, const void* tv, void* mvt, void* rvt, int r_pad, hipStream_t s);
+
+// bf16 attention: C keys staged in LDS per block (bounds max_decode), and the
+// key-split partial-result slots (one per block of a split launch).
+constexpr int kAttnMaxDecode = 2048;
+constexpr int kAttnSplitBlocks = 256;   // split only while fewer blocks than this
+constexpr int kAttnMaxSplit = 8;
+constexpr int kAttnMinSplitTiles = 2;   // key tiles per block at least
+
 struct AttnArgs {
   const void* tq;
-  const void* tv;           // value table (transient C and R values)
+  const void* tv;           // value table (fp32 path: transient C and R values)
   const void* ktab;         // [H_kv][ktab_rows][d] keys of the mask token at every
                             // position, then of the registers (built at init)
   int ktab_rows;
+  const void* mvt;          // bf16 [H_kv][d][8]: the mask token's value, 8 copies
+  const void* rvt;          // bf16 [H_kv][d][r_pad]: register values, zero past R
+  int r_pad;                // R rounded up to the key tile
+  float* part_o;            // [kAttnSplitBlocks][8 waves][32 rows][d] split partial O
+  float* part_ml;           // [kAttnSplitBlocks][8 waves][32 rows][2] (reference, row sum)
   const void* kc;
   const void* vc;
   const float* rope_cos;

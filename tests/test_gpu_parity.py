@@ -111,7 +111,10 @@ def test_generation_matches_oracle(cfgfn):
 def test_forbidden_keys_nan_poison():
     """Invariant (c) on the GPU: NaN in every key/value a new row may not see
     (this step's masked and register rows, and every slot past the visible
-    prefix) leaves the new rows' outputs finite and bit-identical."""
+    prefix) leaves the new rows' outputs finite and bit-identical.  The C and R
+    keys/values come from tables built at init, so the poisoned tables are
+    loaded by a second context on the same buffers, whose cache is rebuilt
+    from the recorded sparse representation (token id and position per slot)."""
     import torch
     from masked_discrete_diffusion_amd import _lib as L
     cfg = gpu_small_d128()
@@ -125,23 +128,36 @@ def test_forbidden_keys_nan_poison():
     c_ptr, c_stride = run._c_src(st)
     n_q = st.n_d + st.n_c + cfg.n_registers
 
-    def attend():
-        L.mdm_step_attention(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d,
+    def attend(ctx):
+        L.mdm_step_attention(ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d,
                              c_ptr, c_stride, st.n_c, run.out)
         torch.cuda.synchronize()
         return run.out[:cfg.batch * n_q * cfg.hidden].view(cfg.batch, n_q, cfg.hidden).clone()
 
-    ref = attend()
+    ref = attend(run.ctx)
+    s_len = L.mdm_cache_len(run.ctx)                 # slots past the committed rows
+    k_before = run.k_cache.clone()
+    v_before = run.v_cache.clone()
     nan = torch.tensor(0x7FC0, dtype=torch.int32).to(torch.int16).item()
     forbidden = [cfg.vocab] + list(range(cfg.vocab + 1, cfg.vocab + 1 + cfg.n_registers))
     run.tk.view(cfg.table_rows, -1)[forbidden] = nan
     run.tv.view(cfg.table_rows, -1)[forbidden] = nan
-    s_len = L.mdm_cache_len(run.ctx)                 # slots past the committed rows
-    kc = run.k_cache.view(cfg.batch, cfg.n_kv_heads, run.slots, cfg.head_dim)
-    vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, cfg.head_dim, run.slots)
-    kc[:, :, s_len:] = nan
-    vc[:, :, :, s_len:] = nan
-    got = attend()
+    ctx2 = L.mdm_sparse_step_init(run.mc, run.bufs, run.stream.cuda_stream)
+    try:
+        tok = run.cache_tok.clone()
+        pos = run.cache_pos.clone()
+        L.mdm_kv_append(ctx2, tok, pos, run.slots, s_len)
+        torch.cuda.synchronize()
+        kc = run.k_cache.view(cfg.batch, cfg.n_kv_heads, run.slots, cfg.head_dim)
+        vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, cfg.head_dim, run.slots)
+        kb = k_before.view(kc.shape)
+        vb = v_before.view(vc.shape)
+        assert torch.equal(kc[:, :, :s_len], kb[:, :, :s_len]) and torch.equal(vc[..., :s_len], vb[..., :s_len])
+        kc[:, :, s_len:] = nan
+        vc[:, :, :, s_len:] = nan
+        got = attend(ctx2)
+    finally:
+        L.mdm_sparse_step_destroy(ctx2)
     n_d = st.n_d
     assert torch.isfinite(got[:, :n_d]).all()
     assert torch.equal(got[:, :n_d], ref[:, :n_d])
