@@ -9,16 +9,28 @@ batch.  The generation is captured once as a HIP graph; W replays warm up,
 then K replays are timed between device synchronisations.
 
 value  = tokens unmasked per second = batch * generated length * K / seconds.
-roofline: the dominant kernel is the step attention; its average launch
-          duration comes from HIP events recorded around every attention
-          launch of an eager generation on the stream the kernel runs on, and
-          its achieved TFLOP/s counts only algorithmic work (4*d per visible
-          (query, key) pair per head).  `traffic` is read from the committed
-          hardware-counter summary when it was taken on the current kernel
-          source, else null.
+roofline: the dominant call is the step attention (k_attn_bf16, plus
+          k_attn_combine on steps whose key range is split).  Its average
+          duration comes from HIP events recorded around every call of an
+          eager generation on the stream the kernels run on; `achieved`
+          counts only algorithmic bytes (K and V of the visible cache once per
+          (sequence, kv head), the transient table rows, Q rows, fp32 O) per
+          call, against the 8 TB/s HBM peak (the step's arithmetic intensity
+          is below the MFMA/HBM ridge).  The algorithmic MFMA fraction is
+          reported alongside.  `traffic` is the counter-measured HBM bytes per
+          call from the committed summary when it was taken on the current
+          kernel sources, else null.
 cpu_baseline: the CPU oracle (float64 NumPy) timed on this host on a bounded
           sample: sequence 0 of the same workload, from the prompt through as
           many sampling steps as fit in the time budget.
+
+Profiling helpers (used to produce profiles/):
+    python bench.py --profile-steps N         N eager generations, nothing else
+    python bench.py --copy-calibration        one plain 1 GiB device copy
+    python bench.py --traffic-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+        reads rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output of a
+        --profile-steps 1 run and of a --copy-calibration run and writes the
+        per-call HBM traffic of the step attention to profiles/.
 """
 
 from __future__ import annotations
@@ -39,7 +51,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 METRIC = "tokens unmasked/sec at 4096-tok T2I; step-attn+logits % of MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_c3_t2i_4k_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "masked_discrete_diffusion_amd", "csrc", "attention.hip")
+CSRC = os.path.join(ROOT, "masked_discrete_diffusion_amd", "csrc")
+ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("attention.hip", "common.hpp", "kernels.hpp")]
+COPY_BYTES = 1 << 30
 
 
 def attention_work(cfg, plan):
@@ -69,21 +83,71 @@ def logits_work(cfg, plan):
     return flops, nbytes
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(n_launch_units):
-    """Counter-derived HBM bytes per attention launch, if measured on this source."""
+def load_traffic():
+    """Counter-derived HBM bytes per attention call, if measured on these sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("attention_source_sha") != source_sha(ATTN_SRC):
+    if t.get("attention_source_sha") != source_sha(ATTN_SOURCES):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_call")
+
+
+def _pmc_dispatches(d, counter):
+    """{kernel name: {dispatch id: value}} for one counter of a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    tab = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            per = tab.setdefault(r["Kernel_Name"], {})
+            disp = int(r["Dispatch_Id"])
+            per[disp] = per.get(disp, 0.0) + float(r["Counter_Value"])
+    return tab
+
+
+def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Per-call HBM traffic of the step attention from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what its counter reads for a plain copy
+    of COPY_BYTES (which reads and writes COPY_BYTES)."""
+    def largest(d, counter):
+        vals = [v for per in _pmc_dispatches(d, counter).values() for v in per.values()]
+        return max(vals) if vals else float("nan")
+
+    def attention_kib(d, counter):
+        tot, calls = 0.0, 0
+        for name, per in _pmc_dispatches(d, counter).items():
+            if "k_attn_bf16" in name or "k_attn_combine" in name:
+                tot += sum(per.values())
+                if "k_attn_bf16" in name:
+                    calls += len(per)
+        return tot, calls
+
+    f_scale = COPY_BYTES / 1024.0 / largest(copy_fetch_dir, "FETCH_SIZE")
+    w_scale = COPY_BYTES / 1024.0 / largest(copy_write_dir, "WRITE_SIZE")
+    fk, calls = attention_kib(fetch_dir, "FETCH_SIZE")
+    wk, _ = attention_kib(write_dir, "WRITE_SIZE")
+    calls = max(calls, 1)
+    t = {"attention_source_sha": source_sha(ATTN_SOURCES), "calls": calls,
+         "fetch_kib_per_call": fk / calls, "write_kib_per_call": wk / calls,
+         "copy_scale_fetch": f_scale, "copy_scale_write": w_scale,
+         "hbm_bytes_per_call": (fk * f_scale + wk * w_scale) * 1024.0 / calls}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t))
 
 
 def cpu_baseline(cfg, budget_s):
@@ -127,14 +191,29 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many eager generations (for profilers) and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain device copy of 1 GiB (counter calibration) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR: write the attention traffic summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              f"(sequences shard across GPUs with no communication; see the design notes).",
+              f"(sequences are independent and would shard across GPUs with no communication).",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+        return
     from masked_discrete_diffusion_amd import _lib as L
     from masked_discrete_diffusion_amd.sampler import SparseStepRunner
     from mdm_inputs import get_config, make_workload
@@ -203,15 +282,17 @@ def main():
     a_flops, a_bytes = attention_work(cfg, run.plan)
     l_flops, l_bytes = logits_work(cfg, run.plan)
     att_s = att_ms.sum() / 1e3
-    achieved = a_flops.sum() / att_s / 1e12               # = mean flops per launch / mean launch time
-    traffic = load_traffic(n)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic,
-                "kernel": "k_attn_bf16<128>", "launches": n,
-                "avg_launch_us": round(att_ms.mean() * 1e3, 2),
-                "algorithmic_gflop_per_launch": round(a_flops.mean() / 1e9, 3),
-                "hbm_gbs_algorithmic": round(a_bytes.sum() / att_s / 1e9, 1)}
+    achieved = a_bytes.sum() / att_s / 1e9               # = mean algorithmic bytes per call / mean call time
+    mfma_tflops = a_flops.sum() / att_s / 1e12
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(),
+                "kernel": "mdm_step_attention: k_attn_bf16<128> (+ k_attn_combine<128> on split steps)",
+                "calls": n,
+                "avg_call_us": round(att_ms.mean() * 1e3, 2),
+                "algorithmic_bytes_per_call": round(float(a_bytes.mean()), 0),
+                "algorithmic_tflops": round(mfma_tflops, 2),
+                "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     both_s = att_s + log_ms.sum() / 1e3
     step_frac = (a_flops.sum() + l_flops.sum()) / both_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
 
