@@ -85,7 +85,9 @@ typedef struct {
   const void* tv;         /* elem [V+1+R][H_kv*d] folded value table                  */
   const void* w_vocab;    /* elem [V][H*d]        vocabulary head                     */
   void* k_cache;          /* elem [B][H_kv][slots][d]   RoPE'd keys, append order     */
-  void* v_cache;          /* elem [B][H_kv][d][slots]   values, transposed            */
+  void* v_cache;          /* elem [B][H_kv][slots/64][d][64]  values, transposed in
+                             64-slot tiles: slot s of dim d sits at
+                             ((s/64)*d_head + d)*64 + s%64 within its (b, kv head) */
   int32_t* cache_pos;     /* [B][slots] position id of each cached slot               */
   int32_t* cache_tok;     /* [B][slots] token id of each cached slot                  */
   void* workspace;        /* scratch, at least mdm_workspace_bytes() bytes, 256-aligned */

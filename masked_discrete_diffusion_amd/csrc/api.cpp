@@ -28,8 +28,8 @@ thread_local std::string g_last_error;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-  size_t err, rope_cos, rope_sin, ktab, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart, tickets,
-      total;
+  size_t err, rope_cos, rope_sin, ktab, qtab, qbuf, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart,
+      tickets, total;
   int ktab_rows, r_pad;
   size_t zpart_bytes;
   int m_pad, n_vt, v_pad;
@@ -77,6 +77,12 @@ Layout layout_of(const mdm_config* c) {
   L.r_pad = (int)align_up((size_t)std::max(c->n_registers, 1), kKeyTile);
   L.ktab_rows = c->seq_len + L.r_pad;
   L.ktab = off; off = align_up(off + (size_t)c->n_kv_heads * L.ktab_rows * c->head_dim * esz, kAlign);
+  // bf16 attention: RoPE'd queries of the mask token at every position and of
+  // the registers (same rows as the key table, all H heads), and of the rows
+  // of the latest append (D rows of the next step)
+  L.qtab = off; off = align_up(off + (bf16 ? (size_t)c->n_heads * L.ktab_rows * c->head_dim * esz : 0), kAlign);
+  L.qbuf = off;
+  off = align_up(off + (bf16 ? (size_t)c->batch * c->n_heads * c->max_decode * c->head_dim * esz : 0), kAlign);
   // bf16 attention: value tables of the transient keys, key-split partials
   const size_t kvd = (size_t)c->n_kv_heads * c->head_dim;
   L.mvt = off; off = align_up(off + (bf16 ? kvd * 8 * sizeof(uint16_t) : 0), kAlign);
@@ -107,6 +113,7 @@ struct mdm_ctx {
   Geometry g;
   Layout L;
   int len;
+  int q_rows;     // rows of the latest append whose queries are in the workspace, or -1
   std::string err;
   char* ws() const { return static_cast<char*>(buf.workspace); }
 };
@@ -179,6 +186,7 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
   ctx->stream = static_cast<hipStream_t>(stream);
   ctx->L = L;
   ctx->len = 0;
+  ctx->q_rows = -1;
   Geometry& g = ctx->g;
   g.B = cfg->batch; g.H = cfg->n_heads; g.Hkv = cfg->n_kv_heads; g.D = cfg->head_dim; g.V = cfg->vocab;
   g.seq_len = cfg->seq_len; g.R = cfg->n_registers; g.slots = (int)slots_of(cfg);
@@ -219,6 +227,20 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
   if (st == MDM_OK && !g.fp32)
     st = hip_check(ctx, launch_value_tables(g, buf->tv, ctx->ws() + L.mvt, ctx->ws() + L.rvt, L.r_pad, ctx->stream),
                    "value tables");
+  if (st == MDM_OK && !g.fp32) {
+    // Query table: the key-table recipe applied to the query table over all H heads.
+    Geometry gq = g;
+    gq.B = 1;
+    gq.Hkv = g.H;
+    gq.slots = L.ktab_rows;
+    AppendArgs qa{};
+    qa.tk = buf->tq; qa.tv = buf->tv; qa.kc = ctx->ws() + L.qtab; qa.vc = nullptr;
+    qa.cache_pos = nullptr; qa.cache_tok = nullptr;
+    qa.rope_cos = rope_cos(ctx); qa.rope_sin = rope_sin(ctx);
+    qa.tok = nullptr; qa.pos = nullptr; qa.stride = 0; qa.n_a = cfg->seq_len; qa.n_reg = cfg->n_registers;
+    qa.slot0 = 0; qa.err = err_word(ctx);
+    st = hip_check(ctx, launch_append(gq, qa, ctx->stream), "query table");
+  }
   if (st == MDM_OK)
     st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.tickets), 0,
                                         L.n_vt * (L.m_pad / 32), ctx->stream), "clear tickets");
@@ -253,8 +275,18 @@ mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, i
   a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
   a.tok = tok; a.pos = pos; a.stride = stride; a.n_a = n; a.n_reg = 0; a.slot0 = ctx->len;
   a.err = err_word(ctx);
+  // Rows that can be the D rows of the next step also get their queries.
+  const bool with_q = !ctx->g.fp32 && n <= ctx->cfg.max_decode;
+  if (with_q) {
+    a.tq = ctx->buf.tq;
+    a.qout = ctx->ws() + ctx->L.qbuf;
+    a.q_rows = ctx->cfg.max_decode;
+  }
   mdm_status st = hip_check(ctx, launch_append(ctx->g, a, ctx->stream), "kv_append launch");
-  if (st == MDM_OK) ctx->len += n;
+  if (st == MDM_OK) {
+    ctx->len += n;
+    ctx->q_rows = with_q ? n : -1;
+  }
   return st;
 }
 
@@ -282,6 +314,11 @@ mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t*
   a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
   a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
   if (!ctx->g.fp32) {
+    a.qtab = ctx->ws() + ctx->L.qtab; a.qtab_rows = ctx->L.ktab_rows;
+    if (n_new_cached > 0 && ctx->q_rows == n_new_cached) {
+      a.qbuf = ctx->ws() + ctx->L.qbuf;
+      a.qbuf_rows = ctx->cfg.max_decode;
+    }
     a.mvt = ctx->ws() + ctx->L.mvt; a.rvt = ctx->ws() + ctx->L.rvt; a.r_pad = ctx->L.r_pad;
     a.part_o = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_o);
     a.part_ml = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_ml);
@@ -343,6 +380,7 @@ mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand
 mdm_status mdm_sparse_step_reset(mdm_ctx* ctx) {
   if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
   ctx->len = 0;
+  ctx->q_rows = -1;
   return MDM_OK;
 }
 

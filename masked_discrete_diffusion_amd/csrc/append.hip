@@ -31,7 +31,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   constexpr int kEpt = D / 8;                 // elements per thread (8 threads per row)
   __shared__ T vs[kRowsPerBlock][D + 2];
-  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const bool q_block = blockIdx.y >= g.Hkv;   // blocks past the kv heads write queries
+  const int kvh = q_block ? blockIdx.y - g.Hkv : blockIdx.y;
   const int r0 = blockIdx.x * kRowsPerBlock;
   const int n_rows = a.n_a + a.n_reg;
   const int t = threadIdx.x;
@@ -51,6 +53,22 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
     }
     if (id < 0 || id >= g.table_rows) { flag_error(a.err, kErrTok); id = 0; }
     if (pos < 0 || pos >= g.max_pos) { flag_error(a.err, kErrPos); pos = 0; }
+  }
+
+  if (q_block) {
+    if (!valid) return;
+    const T* qsrc = static_cast<const T*>(a.tq) + (int64_t)id * g.H * D + kvh * D + part * kEpt;
+    T* qdst = static_cast<T*>(a.qout) + (((int64_t)b * g.H + kvh) * a.q_rows + r) * D + part * kEpt;
+    const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+    const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+#pragma unroll
+    for (int p = 0; p < kEpt / 2; ++p) {
+      double r0d, r1d;
+      rope_pair(Elem<T>::load(qsrc, 2 * p), Elem<T>::load(qsrc, 2 * p + 1), cs[p], sn[p], r0d, r1d);
+      qdst[2 * p] = Elem<T>::from_f64(r0d);
+      qdst[2 * p + 1] = Elem<T>::from_f64(r1d);
+    }
+    return;
   }
 
   const T* tk = static_cast<const T*>(a.tk);
@@ -84,11 +102,14 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   }
   if (!vc) return;
   __syncthreads();
-  // transposed value store: for each d, the block's rows are consecutive slots
+  // transposed value store in 64-slot tiles ([slot tile][d][64]): for each d,
+  // the block's rows are consecutive slots of one or two tiles
   const int rows_here = min(kRowsPerBlock, n_rows - r0);
+  T* vhead = vc + ((int64_t)b * g.Hkv + kvh) * D * g.slots;
   for (int e = t; e < D * kRowsPerBlock; e += blockDim.x) {
     const int dd = e / kRowsPerBlock, rr = e % kRowsPerBlock;
-    if (rr < rows_here) vc[((int64_t)b * g.Hkv + kvh) * D * g.slots + (int64_t)dd * g.slots + a.slot0 + r0 + rr] = vs[rr][dd];
+    const int sl = a.slot0 + r0 + rr;
+    if (rr < rows_here) vhead[((int64_t)(sl / kKeyTile) * D + dd) * kKeyTile + sl % kKeyTile] = vs[rr][dd];
   }
 }
 
@@ -116,7 +137,7 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
 hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s) {
   const int n_rows = a.n_a + a.n_reg;
   if (n_rows <= 0) return hipSuccess;
-  dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, g.Hkv, g.B);
+  dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, g.Hkv + (a.qout ? g.H : 0), g.B);
   if (g.fp32) {
     if (g.D == 128) hipLaunchKernelGGL((k_append<float, 128>), grid, dim3(256), 0, s, g, a);
     else hipLaunchKernelGGL((k_append<float, 64>), grid, dim3(256), 0, s, g, a);

@@ -167,7 +167,7 @@ __device__ inline TileRef tile_ref(const AttnArgs& a, int T0, int T1, int t) {
 // Per-(sequence, kv head) sources of the three segments.
 struct KvSrc {
   const uint16_t* kc;     // cache keys [slots][D]
-  const uint16_t* vc;     // cache values [D][slots]
+  const uint16_t* vc;     // cache values [slots/64][D][64] (V^T in 64-slot tiles)
   const uint16_t* ktab;   // key table [ktab_rows][D]
   const uint16_t* mvt;    // mask-token value units [D][8]
   const uint16_t* rvt;    // register values [D][r_pad]
@@ -175,11 +175,12 @@ struct KvSrc {
 };
 
 // Byte offsets, per lane, of this wavefront's DMA units for a cache tile,
-// relative to the tile's first key (K) or first slot (V^T): K unit (row r,
-// chunk c) -> r*D + c, V^T unit (dim d, chunk c) -> d*slots + c (elements,
-// times 2).  A pad unit (c = last) loads chunk 0 of its row, never read.
+// relative to the tile's first key (K) or its V^T tile (each 64-slot V^T
+// tile is one contiguous [D][64] block): K unit (row r, chunk c) -> r*D + 8c,
+// V^T unit (dim d, chunk c) -> 64d + 8c (elements, times 2).  A pad unit
+// (c = last) loads chunk 0 of its row, never read.
 template <int D>
-__device__ inline void dma_offsets(int wave, int lane, int slots, uint32_t (&off)[AttnTile<D>::LPW]) {
+__device__ inline void dma_offsets(int wave, int lane, uint32_t (&off)[AttnTile<D>::LPW]) {
   using T = AttnTile<D>;
 #pragma unroll
   for (int i = 0; i < T::LPW; ++i) {
@@ -191,7 +192,7 @@ __device__ inline void dma_offsets(int wave, int lane, int slots, uint32_t (&off
     } else {
       const int u = (blk - T::K_BLOCKS) * kWave + lane;
       const int d = u / T::VU, c = u % T::VU;
-      off[i] = 2u * (uint32_t)(d * slots + (c < T::VC ? c : 0) * 8);
+      off[i] = 2u * (uint32_t)(d * kKeyTile + (c < T::VC ? c : 0) * 8);
     }
   }
 }
@@ -212,7 +213,7 @@ __device__ inline void tile_dma(const AttnArgs& a, const Geometry& g, const KvSr
   asm volatile("" : "+v"(ln));
   const uint16_t* kbase = tr.seg == 0 ? src.kc + (int64_t)tr.base * D
                                       : src.ktab + (int64_t)(g.seq_len + tr.base) * D;   // seg 2 (seg 1 below)
-  const uint16_t* vbase = src.vc + tr.base;                                            // seg 0
+  const uint16_t* vbase = src.vc + (int64_t)tr.base * D;                               // seg 0: V^T tile
 #pragma unroll
   for (int i = 0; i < T::LPW; ++i) {
     const int blk = wave * T::LPW + i;
@@ -528,32 +529,61 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   src.kidx = kidx;
 
   uint32_t off[T::LPW];
-  dma_offsets<D>(wave, lane, g.slots, off);
+  dma_offsets<D>(wave, lane, off);
   for (int i = 0; i < kAhead && i < n_my; ++i)
     tile_dma<D>(a, g, src, tile_ref(a, T0, T1, t_lo + i), wave, lane, off, ks[i], vs[i]);
 
   // Q^T fragment (B operand): lane holds row l32, dims 16t + 8*half + 0..7, RoPE'd.
+  // C and R rows read the query table (the mask token at the row's position,
+  // the registers); D rows read the queries their append wrote, or, if the
+  // append did not write them, rotate their table row here.
   bf16x8 qf[NKS];
   {
+    const uint16_t* qrow = nullptr;
+    bool rotate = false;
     RowInfo ri = {0, 0};
-    if (rvalid) ri = query_row(g, a, b, row);
-    const uint16_t* tq = static_cast<const uint16_t*>(a.tq) + (int64_t)ri.id * g.hidden + h * D;
-    const float* cs = a.rope_cos + (int64_t)ri.pos * (D / 2);
-    const float* sn = a.rope_sin + (int64_t)ri.pos * (D / 2);
-#pragma unroll
-    for (int t = 0; t < NKS; ++t) {
-      u16x8 raw = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (rvalid) raw = *reinterpret_cast<const u16x8*>(tq + 16 * t + 8 * half);
-      u16x8 rot;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int pi = 8 * t + 4 * half + p;
-        double r0, r1;
-        rope_pair(bf16_to_f32(raw[2 * p]), bf16_to_f32(raw[2 * p + 1]), cs[pi], sn[pi], r0, r1);
-        rot[2 * p] = f64_to_bf16(r0);
-        rot[2 * p + 1] = f64_to_bf16(r1);
+    if (rvalid) {
+      if (row < a.n_d && !a.qbuf) {
+        rotate = true;
+        ri = query_row(g, a, b, row);
+      } else if (row < a.n_d) {
+        qrow = static_cast<const uint16_t*>(a.qbuf) + (((int64_t)b * g.H + h) * a.qbuf_rows + row) * D;
+      } else {
+        int pos;
+        if (row < a.n_d + a.n_c) {
+          pos = a.c_pos[(int64_t)b * a.c_stride + (row - a.n_d)];
+          if (pos < 0 || pos >= g.seq_len) { flag_error(a.err, kErrPos); pos = 0; }
+        } else {
+          pos = g.seq_len + (row - a.n_d - a.n_c);
+        }
+        qrow = static_cast<const uint16_t*>(a.qtab) + ((int64_t)h * a.qtab_rows + pos) * D;
       }
-      qf[t] = __builtin_bit_cast(bf16x8, rot);
+    }
+    if (rotate) {
+      const uint16_t* tq = static_cast<const uint16_t*>(a.tq) + (int64_t)ri.id * g.hidden + h * D;
+      const float* cs = a.rope_cos + (int64_t)ri.pos * (D / 2);
+      const float* sn = a.rope_sin + (int64_t)ri.pos * (D / 2);
+#pragma unroll
+      for (int t = 0; t < NKS; ++t) {
+        const u16x8 raw = *reinterpret_cast<const u16x8*>(tq + 16 * t + 8 * half);
+        u16x8 rot;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int pi = 8 * t + 4 * half + p;
+          double r0, r1;
+          rope_pair(bf16_to_f32(raw[2 * p]), bf16_to_f32(raw[2 * p + 1]), cs[pi], sn[pi], r0, r1);
+          rot[2 * p] = f64_to_bf16(r0);
+          rot[2 * p + 1] = f64_to_bf16(r1);
+        }
+        qf[t] = __builtin_bit_cast(bf16x8, rot);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NKS; ++t) {
+        u16x8 raw = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (qrow) raw = *reinterpret_cast<const u16x8*>(qrow + 16 * t + 8 * half);
+        qf[t] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
   }
 
@@ -618,20 +648,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   }
 }
 
-// Merge of the key-split partials: block = one chunk group, wavefront w = its
-// chunk w; lane: row lane/2, dims [D/2 * (lane%2), +D/2).  Splits are folded
-// in split order (fixed arithmetic, independent of which block ran first):
-// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// Merge of the key-split partials: one 128-thread block per chunk (blockIdx =
+// chunk group * 8 + chunk slot); thread: row tid/4, dims [D/4 * (tid%4), +D/4).
+// Splits are folded in split order (fixed arithmetic, independent of which
+// block ran first): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// M = max_s m_s.
+constexpr int kCombineThreads = 128;
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(Geometry g, AttnArgs a, ChunkPlan cp) {
-  constexpr int HD = D / 2;
-  const int group = blockIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(Geometry g, AttnArgs a, ChunkPlan cp) {
+  constexpr int QD = D / 4;
+  const int group = blockIdx.x / kAttnWaves;
+  const int wave = blockIdx.x % kAttnWaves;       // chunk slot of the group (the wavefront that wrote it)
   const int G = g.H / g.Hkv;
   const int j = group % cp.blocks;
   const int bk = group / cp.blocks;
   const int kvh = bk % g.Hkv;
   const int b = bk / g.Hkv;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int c0 = j * cp.per_block;
   const int c1 = min(G * cp.n_chunks, c0 + cp.per_block);
   const int ch = c0 + wave;
@@ -640,23 +673,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(Geometry g, AttnA
   int row_base, row_end;
   bool is_cr;
   chunk_rows(a, cp, 32, ch % cp.n_chunks, row_base, row_end, is_cr);
-  const int r = lane / 2, part = lane % 2;
+  const int r = threadIdx.x / 4, part = threadIdx.x % 4;
   const int row = row_base + r;
   if (row >= row_end) return;
   const int64_t slot0 = (int64_t)group * cp.ksplit;
   float mx = -1e30f;
   for (int s = 0; s < cp.ksplit; ++s) mx = fmaxf(mx, a.part_ml[((slot0 + s) * kAttnWaves + wave) * 64 + 2 * r]);
-  floatx4 sum[HD / 4];
+  floatx4 sum[QD / 4];
 #pragma unroll
-  for (int q = 0; q < HD / 4; ++q) sum[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < QD / 4; ++q) sum[q] = floatx4{0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   for (int s = 0; s < cp.ksplit; ++s) {
     const int64_t slot = (slot0 + s) * kAttnWaves + wave;
     const float w = __builtin_amdgcn_exp2f(a.part_ml[slot * 64 + 2 * r] - mx);
     lsum = fmaf(w, a.part_ml[slot * 64 + 2 * r + 1], lsum);
-    const floatx4* ps = reinterpret_cast<const floatx4*>(a.part_o + slot * 32 * D + r * D + part * HD);
+    const floatx4* ps = reinterpret_cast<const floatx4*>(a.part_o + slot * 32 * D + r * D + part * QD);
 #pragma unroll
-    for (int q = 0; q < HD / 4; ++q) {
+    for (int q = 0; q < QD / 4; ++q) {
       const floatx4 v = ps[q];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) sum[q][ii] = fmaf(w, v[ii], sum[q][ii]);
@@ -664,9 +697,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(Geometry g, AttnA
   }
   const float inv = 1.f / lsum;
   const int n_q = a.n_d + a.n_c + a.n_r;
-  floatx4* o = reinterpret_cast<floatx4*>(a.out + ((int64_t)b * n_q + row) * g.hidden + h * D + part * HD);
+  floatx4* o = reinterpret_cast<floatx4*>(a.out + ((int64_t)b * n_q + row) * g.hidden + h * D + part * QD);
 #pragma unroll
-  for (int q = 0; q < HD / 4; ++q) {
+  for (int q = 0; q < QD / 4; ++q) {
     floatx4 v;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) v[ii] = sum[q][ii] * inv;
@@ -739,7 +772,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(Geometry g, AttnArgs a, ChunkP
       const int dd = c / KT, kr = c % KT;
       const int slot = kt + kr;
       float v = 0.f;
-      if (slot < a.S) v = vc[(int64_t)dd * g.slots + slot];
+      if (slot < a.S) v = vc[((int64_t)(slot / kKeyTile) * D + dd) * kKeyTile + slot % kKeyTile];
       else if (slot < min(s_tot, wlen)) v = tv[(int64_t)transient_id(g, a, slot - a.S) * kvd + kvh * D + dd];
       vs[dd][kr] = v;
     }
@@ -821,8 +854,9 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     else hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     if (ks > 1) {
-      if (g.D == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(groups), dim3(kAttnThreads), 0, s, g, a, cp);
-      else hipLaunchKernelGGL((k_attn_combine<64>), dim3(groups), dim3(kAttnThreads), 0, s, g, a, cp);
+      const dim3 cgrid(groups * kAttnWaves);
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_combine<128>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_combine<64>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp);
     }
   }
   return hipGetLastError();

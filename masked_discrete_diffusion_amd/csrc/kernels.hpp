@@ -19,7 +19,8 @@ struct Geometry {
 // position pos[b*stride + r] (or r when pos == NULL).  Rows [n_a, n_a + n_reg):
 // register r - n_a (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) and,
 // when vc != NULL, transposed values to slots slot0 + r; records (pos, id) when
-// cache_pos != NULL.
+// cache_pos != NULL.  When qout != NULL the same launch also writes the rows'
+// RoPE'd queries for all H heads: qout[b][h][q_rows][d], row r at index r.
 struct AppendArgs {
   const void* tk;
   const void* tv;
@@ -34,6 +35,9 @@ struct AppendArgs {
   int64_t stride;
   int n_a, n_reg, slot0;
   int* err;
+  const void* tq;           // query table (with qout)
+  void* qout;               // bf16 [B][H][q_rows][d] or NULL
+  int q_rows;
 };
 hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s);
 
@@ -57,6 +61,12 @@ struct AttnArgs {
   const void* mvt;          // bf16 [H_kv][d][8]: the mask token's value, 8 copies
   const void* rvt;          // bf16 [H_kv][d][r_pad]: register values, zero past R
   int r_pad;                // R rounded up to the key tile
+  const void* qtab;         // bf16 [H][qtab_rows][d]: RoPE'd queries of the mask token at
+                            // every position, then of the registers (built at init)
+  int qtab_rows;
+  const void* qbuf;         // bf16 [B][H][qbuf_rows][d]: RoPE'd queries of the D rows written
+                            // by the preceding append, or NULL (then RoPE in the kernel)
+  int qbuf_rows;
   float* part_o;            // [kAttnSplitBlocks][8 waves][32 rows][d] split partial O
   float* part_ml;           // [kAttnSplitBlocks][8 waves][32 rows][2] (reference, row sum)
   const void* kc;

@@ -113,63 +113,89 @@ __global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
 // ------------------------------------------------------- screen, bf16 MFMA --
 // Block: 4 wavefronts; wave w owns vocab columns [32w, 32w+32) of a 128-column
 // tile and all 32*RB rows of the row tile.  Hidden is consumed in 64-wide
-// chunks, double-buffered in LDS with the next chunk's global loads in flight
-// while the current one is multiplied.  With n_split > 1 the hidden dimension
-// is split over blockIdx.z: every split writes its partial tile, and the last
-// split to arrive (ticket per tile) sums the partials in split order and runs
-// the epilogue, so the result does not depend on arrival order.
+// chunks ("stages") that flow from HBM straight into LDS (LDS-DMA, issued
+// from asm with explicit waits, see common.hpp) through an NST-deep ring:
+// NST-1 stages are in flight while one is multiplied, one barrier per stage.
+// LDS rows are 8 data units (16 B) plus one pad unit, which keeps the MFMA
+// operand reads of 16 consecutive rows on distinct banks with compile-time
+// offsets.  A stage's DMA blocks (1 KiB each) are padded to a multiple of the
+// wavefront count so every wavefront issues the same number of loads and the
+// ring waits are constants; pad blocks reload W row v0 into spare LDS.
+// With n_split > 1 the hidden dimension is split over blockIdx.z: every split
+// writes its partial tile, and the last split to arrive (ticket per tile)
+// sums the partials in split order and runs the epilogue, so the result does
+// not depend on arrival order.
 constexpr int kScreenThreads = 256;
+constexpr int kScreenWaves = kScreenThreads / kWave;
 
 template <int RB, bool kLo>
-struct ScreenRegs {
-  u16x8 w[4];
-  u16x8 h[RB];
-  u16x8 l[kLo ? RB : 1];
+struct ScreenStage {
+  static constexpr int U = kKChunk / 8 + 1;                        // units per padded row
+  static constexpr int W_BLOCKS = kVocabTile * U / kWave;          // 18
+  static constexpr int H_BLOCKS = (32 * RB * U + kWave - 1) / kWave;
+  static constexpr int REAL = W_BLOCKS + H_BLOCKS * (kLo ? 2 : 1);
+  static constexpr int LPW = (REAL + kScreenWaves - 1) / kScreenWaves;   // loads per wavefront per stage
+  static constexpr int BLOCKS = LPW * kScreenWaves;                // incl. pad blocks
+  static constexpr int ELEMS = BLOCKS * kWave * 8;                 // bf16 elements per stage
+  static constexpr int H_OFF = W_BLOCKS * kWave * 8;               // element offsets in a stage
+  static constexpr int L_OFF = H_OFF + H_BLOCKS * kWave * 8;
+  static constexpr int FIT = 140 * 1024 / (ELEMS * 2);             // stages that fit beside the epilogue
+  static constexpr int NST = FIT >= 4 ? 4 : (FIT < 2 ? 2 : FIT);    // ring depth
 };
 
+// Per-lane byte offsets of this wavefront's DMA units, relative to the
+// stage's W base (W row v0) or h base (row m0), and the kind of each slot
+// (0 W, 1 h hi, 2 h lo, 3 pad).
 template <int RB, bool kLo>
-__device__ inline void screen_load(ScreenRegs<RB, kLo>& r, const uint16_t* w, const uint16_t* hhi,
-                                   const uint16_t* hlo, int hidden, int V, int v0, int m0, int k0) {
-  constexpr int CPR = kKChunk / 8;   // 16-byte chunks per row of a chunk
+__device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int v0, uint32_t* off, int* kind) {
+  using S = ScreenStage<RB, kLo>;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * kScreenThreads;
-    const int v = min(v0 + c / CPR, V - 1);
-    r.w[i] = *reinterpret_cast<const u16x8*>(w + (int64_t)v * hidden + k0 + (c % CPR) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < RB; ++i) {
-    const int c = threadIdx.x + i * kScreenThreads;
-    const int64_t off = (int64_t)(m0 + c / CPR) * hidden + k0 + (c % CPR) * 8;
-    r.h[i] = *reinterpret_cast<const u16x8*>(hhi + off);
-    if (kLo) r.l[i] = *reinterpret_cast<const u16x8*>(hlo + off);
+  for (int i = 0; i < S::LPW; ++i) {
+    const int blk = wave * S::LPW + i;
+    if (blk < S::W_BLOCKS) {
+      const int u = blk * kWave + lane;
+      const int r = u / S::U, c = u % S::U;
+      off[i] = (uint32_t)((min(v0 + r, V - 1) - v0) * hidden + (c < S::U - 1 ? c : 0) * 8) * 2u;
+      kind[i] = 0;
+    } else if (blk < S::REAL) {
+      const int hb = (blk - S::W_BLOCKS) % S::H_BLOCKS;
+      const int u = hb * kWave + lane;
+      const int r = min(u / S::U, 32 * RB - 1), c = u % S::U;
+      off[i] = (uint32_t)(r * hidden + (c < S::U - 1 ? c : 0) * 8) * 2u;
+      kind[i] = blk - S::W_BLOCKS >= S::H_BLOCKS ? 2 : 1;
+    } else {
+      off[i] = (uint32_t)(lane % (S::U - 1)) * 16u;
+      kind[i] = 3;
+    }
   }
 }
 
 template <int RB, bool kLo>
-__device__ inline void screen_store(const ScreenRegs<RB, kLo>& r, uint16_t* ws, uint16_t* hs, uint16_t* ls) {
-  constexpr int WPAD = kKChunk + 8;
-  constexpr int CPR = kKChunk / 8;
+__device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const uint16_t* lb, int wave,
+                                  const uint32_t* off, const int* kind, uint16_t* stage) {
+  using S = ScreenStage<RB, kLo>;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * kScreenThreads;
-    *reinterpret_cast<u16x8*>(ws + (c / CPR) * WPAD + (c % CPR) * 8) = r.w[i];
+  for (int i = 0; i < S::LPW; ++i) {
+    const int blk = wave * S::LPW + i;
+    const uint16_t* base = kind[i] == 1 ? hb : (kind[i] == 2 ? lb : wb);
+    dma16(base, off[i], stage + blk * kWave * 8);
   }
-#pragma unroll
-  for (int i = 0; i < RB; ++i) {
-    const int c = threadIdx.x + i * kScreenThreads;
-    *reinterpret_cast<u16x8*>(hs + (c / CPR) * WPAD + (c % CPR) * 8) = r.h[i];
-    if (kLo) *reinterpret_cast<u16x8*>(ls + (c / CPR) * WPAD + (c % CPR) * 8) = r.l[i];
-  }
+}
+
+template <int LPW, int AHEAD>
+__device__ inline void screen_wait(int younger) {
+  static_assert(AHEAD <= 3, "waits are spelled out for up to three stages ahead");
+  if (younger >= 2 && AHEAD >= 3) ring_wait<2 * LPW>();
+  else if (younger >= 1 && AHEAD >= 2) ring_wait<LPW>();
+  else ring_wait<0>();
 }
 
 template <int RB, bool kLo>
 __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, VocabArgs a, int M, int n_split) {
-  constexpr int WPAD = kKChunk + 8;
+  using S = ScreenStage<RB, kLo>;
   constexpr int MT = 32 * RB;
-  __shared__ __align__(16) uint16_t ws[2][kVocabTile * WPAD];
-  __shared__ __align__(16) uint16_t hs[2][MT * WPAD];
-  __shared__ __align__(16) uint16_t ls[kLo ? 2 : 1][kLo ? MT * WPAD : 8];
+  constexpr int AHEAD = S::NST - 1;
+  __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
   __shared__ Top2 red[4][MT];
   __shared__ int last_flag;
 
@@ -178,12 +204,15 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, Voca
   const int split = blockIdx.z;
   const int v0 = vt * kVocabTile;
   const int m0 = mt * MT;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int half = lane / 32, l32 = lane % 32;
-  const uint16_t* w = static_cast<const uint16_t*>(a.w);
   const int k_len = g.hidden / n_split;
   const int k_beg = split * k_len;
   const int n_chunks = k_len / kKChunk;
+  const uint16_t* wrow = static_cast<const uint16_t*>(a.w) + (int64_t)v0 * g.hidden + k_beg;
+  const uint16_t* hrow = a.hhi + (int64_t)m0 * g.hidden + k_beg;
+  const uint16_t* lrow = kLo ? a.hlo + (int64_t)m0 * g.hidden + k_beg : hrow;
 
   floatx16 acc[RB];
 #pragma unroll
@@ -191,33 +220,33 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, Voca
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 
-  ScreenRegs<RB, kLo> regs;
-  screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg);
-  screen_store<RB, kLo>(regs, ws[0], hs[0], ls[0]);
-  if (n_chunks > 1) screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg + kKChunk);
-  int cur = 0;
-  for (int ci = 0; ci < n_chunks; ++ci, cur ^= 1) {
-    __syncthreads();
-    const uint16_t* wb = ws[cur];
-    const uint16_t* hb = hs[cur];
-    const uint16_t* lb = ls[kLo ? cur : 0];
+  uint32_t off[S::LPW];
+  int kind[S::LPW];
+  screen_offsets<RB, kLo>(wave, lane, g.hidden, g.V, v0, off, kind);
+  for (int c = 0; c < AHEAD && c < n_chunks; ++c)
+    screen_dma<RB, kLo>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind, ring[c]);
+  const int woff = ((32 * wave + l32) * S::U + half) * 8;
+  const int hoff = (l32 * S::U + half) * 8;
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    screen_wait<S::LPW, AHEAD>(n_chunks - 1 - ci);
+    ring_barrier();
+    const int nxt = ci + AHEAD;
+    if (nxt < n_chunks)
+      screen_dma<RB, kLo>(wrow + nxt * kKChunk, hrow + nxt * kKChunk, lrow + nxt * kKChunk, wave, off, kind,
+                          ring[nxt % S::NST]);
+    const uint16_t* st = ring[ci % S::NST];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wb + (32 * wave + l32) * WPAD + 16 * t + 8 * half);
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + woff + 16 * t);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(hb + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff + rb * 32 * S::U * 8 + 16 * t);
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
         if (kLo) {
-          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(lb + (32 * rb + l32) * WPAD + 16 * t + 8 * half);
+          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff + rb * 32 * S::U * 8 + 16 * t);
           acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lf, acc[rb], 0, 0, 0);
         }
       }
-    }
-    if (ci + 1 < n_chunks) {
-      screen_store<RB, kLo>(regs, ws[cur ^ 1], hs[cur ^ 1], ls[kLo ? cur ^ 1 : 0]);
-      if (ci + 2 < n_chunks)
-        screen_load<RB, kLo>(regs, w, a.hhi, a.hlo, g.hidden, g.V, v0, m0, k_beg + (ci + 2) * kKChunk);
     }
   }
 

@@ -61,7 +61,9 @@ def test_append_keys_bit_exact(cfgfn):
     torch.cuda.synchronize()
     P, d, S = cfg.prompt_len, cfg.head_dim, run.slots
     kc = run.k_cache.cpu().numpy().reshape(cfg.batch, cfg.n_kv_heads, S, d)
-    vc = run.v_cache.cpu().numpy().reshape(cfg.batch, cfg.n_kv_heads, d, S)
+    # V^T in 64-slot tiles: [B][Hkv][S/64][d][64] -> [B][Hkv][d][S]
+    vc = run.v_cache.cpu().numpy().reshape(cfg.batch, cfg.n_kv_heads, S // 64, d, 64)
+    vc = vc.transpose(0, 1, 3, 2, 4).reshape(cfg.batch, cfg.n_kv_heads, d, S)
     model = Model.from_workload(wl)
     for b in range(cfg.batch):
         seq = SequenceOracle(model, wl.prompt_ids[b])
@@ -149,12 +151,15 @@ def test_forbidden_keys_nan_poison():
         L.mdm_kv_append(ctx2, tok, pos, run.slots, s_len)
         torch.cuda.synchronize()
         kc = run.k_cache.view(cfg.batch, cfg.n_kv_heads, run.slots, cfg.head_dim)
-        vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, cfg.head_dim, run.slots)
+        # V^T in 64-slot tiles: view as [B][Hkv][S/64][d][64]; slot s = 64*tile + w
+        vc = run.v_cache.view(cfg.batch, cfg.n_kv_heads, run.slots // 64, cfg.head_dim, 64)
         kb = k_before.view(kc.shape)
         vb = v_before.view(vc.shape)
-        assert torch.equal(kc[:, :, :s_len], kb[:, :, :s_len]) and torch.equal(vc[..., :s_len], vb[..., :s_len])
+        vis = torch.arange(run.slots, device=vc.device).view(run.slots // 64, 1, 64) < s_len
+        assert torch.equal(kc[:, :, :s_len], kb[:, :, :s_len]) and torch.equal(vc[..., vis.expand_as(vc[0, 0])],
+                                                                                 vb[..., vis.expand_as(vb[0, 0])])
         kc[:, :, s_len:] = nan
-        vc[:, :, :, s_len:] = nan
+        vc.masked_fill_(~vis, nan)
         got = attend(ctx2)
     finally:
         L.mdm_sparse_step_destroy(ctx2)
