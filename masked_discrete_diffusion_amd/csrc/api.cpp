@@ -29,7 +29,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
   size_t err, rope_cos, rope_sin, ktab, qtab, qbuf, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart,
-      tickets, total;
+      total;
   int ktab_rows, r_pad;
   size_t zpart_bytes;
   int m_pad, n_vt, v_pad;
@@ -99,7 +99,6 @@ Layout layout_of(const mdm_config* c) {
   const size_t zfull = 8 * (size_t)c->batch * c->max_decode * L.v_pad * sizeof(float);
   L.zpart_bytes = bf16 ? std::min(zfull, (size_t)32 << 20) : 0;
   L.zpart = off; off = align_up(off + L.zpart_bytes, kAlign);
-  L.tickets = off; off = align_up(off + (size_t)L.n_vt * (L.m_pad / 32) * sizeof(int), kAlign);
   L.total = off;
   return L;
 }
@@ -241,9 +240,6 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
     qa.slot0 = 0; qa.err = err_word(ctx);
     st = hip_check(ctx, launch_append(gq, qa, ctx->stream), "query table");
   }
-  if (st == MDM_OK)
-    st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.tickets), 0,
-                                        L.n_vt * (L.m_pad / 32), ctx->stream), "clear tickets");
 
   if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "init synchronize");
   if (st != MDM_OK) {
@@ -351,7 +347,7 @@ mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_
   a.partials = reinterpret_cast<float*>(ctx->ws() + ctx->L.partials);
   a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
   a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
-  a.tickets = reinterpret_cast<int*>(ctx->ws() + ctx->L.tickets); a.v_pad = ctx->L.v_pad;
+  a.v_pad = ctx->L.v_pad;
   return hip_check(ctx, launch_vocab(ctx->g, a, ctx->stream), "vocab launch");
 }
 

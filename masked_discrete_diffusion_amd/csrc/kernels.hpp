@@ -95,7 +95,6 @@ struct VocabArgs {
   float* partials;          // [m_pad][n_vt][8]
   float* zpart;             // split partial logits [n_split][M][v_pad] (bf16 path)
   int64_t zpart_bytes;
-  int* tickets;             // [m_tiles][n_vt] arrival counters, zero between launches
   int v_pad;                // V rounded up to the vocab tile
   float* logits;            // optional [M][V]
   float* conf;              // [M]

@@ -111,31 +111,34 @@ __global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
 }
 
 // ------------------------------------------------------- screen, bf16 MFMA --
-// Block: 4 wavefronts; wave w owns vocab columns [32w, 32w+32) of a 128-column
-// tile and all 32*RB rows of the row tile.  Hidden is consumed in 64-wide
-// chunks ("stages") that flow from HBM straight into LDS (LDS-DMA, issued
-// from asm with explicit waits, see common.hpp) through an NST-deep ring:
-// NST-1 stages are in flight while one is multiplied, one barrier per stage.
-// LDS rows are 8 data units (16 B) plus one pad unit, which keeps the MFMA
-// operand reads of 16 consecutive rows on distinct banks with compile-time
-// offsets.  A stage's DMA blocks (1 KiB each) are padded to a multiple of the
-// wavefront count so every wavefront issues the same number of loads and the
-// ring waits are constants; pad blocks reload W row v0 into spare LDS.
+// Block: 4 * NG wavefronts; wave w owns vocab columns [32(w%4), +32) of a
+// 128-column tile and row blocks (w/4)*RB/NG .. +RB/NG of the 32*RB-row tile
+// (NG = 2 gives each SIMD two wavefronts to overlap LDS latency and barriers).
+// Hidden is consumed in 64-wide chunks ("stages") that flow from HBM straight
+// into LDS (LDS-DMA, issued from asm with explicit waits, see common.hpp)
+// through an NST-deep ring: NST-1 stages are in flight while one is
+// multiplied, one barrier per stage.  LDS rows are 8 data units (16 B) plus
+// one pad unit, which keeps the MFMA operand reads of 16 consecutive rows on
+// distinct banks with compile-time offsets.  A stage's DMA blocks (1 KiB each)
+// are padded to a multiple of the wavefront count so every wavefront issues
+// the same number of loads and the ring waits are constants; pad blocks
+// reload W row v0 into spare LDS.
 // With n_split > 1 the hidden dimension is split over blockIdx.z: every split
-// writes its partial tile, and the last split to arrive (ticket per tile)
-// sums the partials in split order and runs the epilogue, so the result does
-// not depend on arrival order.
-constexpr int kScreenThreads = 256;
-constexpr int kScreenWaves = kScreenThreads / kWave;
-
-template <int RB, bool kLo>
+// writes its partial logits and k_screen_reduce sums them in split order and
+// runs the epilogue (a separate launch: an in-kernel last-block reduction
+// needs device-scope fences, which write back and invalidate a whole L2).
+template <int RB, int NG, bool kLo>
 struct ScreenStage {
+  static constexpr int NW = 4 * NG;                                // wavefronts per block
+  static constexpr int THREADS = NW * kWave;
+  static constexpr int RBW = RB / NG;                              // row blocks per wavefront
+  static_assert(RB % NG == 0, "row blocks must split evenly over the row groups");
   static constexpr int U = kKChunk / 8 + 1;                        // units per padded row
   static constexpr int W_BLOCKS = kVocabTile * U / kWave;          // 18
   static constexpr int H_BLOCKS = (32 * RB * U + kWave - 1) / kWave;
   static constexpr int REAL = W_BLOCKS + H_BLOCKS * (kLo ? 2 : 1);
-  static constexpr int LPW = (REAL + kScreenWaves - 1) / kScreenWaves;   // loads per wavefront per stage
-  static constexpr int BLOCKS = LPW * kScreenWaves;                // incl. pad blocks
+  static constexpr int LPW = (REAL + NW - 1) / NW;                 // loads per wavefront per stage
+  static constexpr int BLOCKS = LPW * NW;                          // incl. pad blocks
   static constexpr int ELEMS = BLOCKS * kWave * 8;                 // bf16 elements per stage
   static constexpr int H_OFF = W_BLOCKS * kWave * 8;               // element offsets in a stage
   static constexpr int L_OFF = H_OFF + H_BLOCKS * kWave * 8;
@@ -146,9 +149,8 @@ struct ScreenStage {
 // Per-lane byte offsets of this wavefront's DMA units, relative to the
 // stage's W base (W row v0) or h base (row m0), and the kind of each slot
 // (0 W, 1 h hi, 2 h lo, 3 pad).
-template <int RB, bool kLo>
+template <class S>
 __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int v0, uint32_t* off, int* kind) {
-  using S = ScreenStage<RB, kLo>;
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
     const int blk = wave * S::LPW + i;
@@ -160,7 +162,7 @@ __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int
     } else if (blk < S::REAL) {
       const int hb = (blk - S::W_BLOCKS) % S::H_BLOCKS;
       const int u = hb * kWave + lane;
-      const int r = min(u / S::U, 32 * RB - 1), c = u % S::U;
+      const int r = min(u / S::U, 32 * S::RBW * (S::NW / 4) - 1), c = u % S::U;
       off[i] = (uint32_t)(r * hidden + (c < S::U - 1 ? c : 0) * 8) * 2u;
       kind[i] = blk - S::W_BLOCKS >= S::H_BLOCKS ? 2 : 1;
     } else {
@@ -170,10 +172,9 @@ __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int
   }
 }
 
-template <int RB, bool kLo>
+template <class S>
 __device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const uint16_t* lb, int wave,
                                   const uint32_t* off, const int* kind, uint16_t* stage) {
-  using S = ScreenStage<RB, kLo>;
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
     const int blk = wave * S::LPW + i;
@@ -190,14 +191,14 @@ __device__ inline void screen_wait(int younger) {
   else ring_wait<0>();
 }
 
-template <int RB, bool kLo>
-__global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, VocabArgs a, int M, int n_split) {
-  using S = ScreenStage<RB, kLo>;
+template <int RB, int NG, bool kLo>
+__global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, VocabArgs a, int M, int n_split) {
+  using S = ScreenStage<RB, NG, kLo>;
   constexpr int MT = 32 * RB;
+  constexpr int RBW = S::RBW;
   constexpr int AHEAD = S::NST - 1;
   __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
   __shared__ Top2 red[4][MT];
-  __shared__ int last_flag;
 
   const int vt = blockIdx.x;
   const int mt = blockIdx.y;
@@ -205,6 +206,8 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, Voca
   const int v0 = vt * kVocabTile;
   const int m0 = mt * MT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wv = wave % 4;                  // vocab block of the tile
+  const int rb0 = (wave / 4) * RBW;         // first row block of this wavefront
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32, l32 = lane % 32;
   const int k_len = g.hidden / n_split;
@@ -214,32 +217,32 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, Voca
   const uint16_t* hrow = a.hhi + (int64_t)m0 * g.hidden + k_beg;
   const uint16_t* lrow = kLo ? a.hlo + (int64_t)m0 * g.hidden + k_beg : hrow;
 
-  floatx16 acc[RB];
+  floatx16 acc[RBW];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
 
   uint32_t off[S::LPW];
   int kind[S::LPW];
-  screen_offsets<RB, kLo>(wave, lane, g.hidden, g.V, v0, off, kind);
+  screen_offsets<S>(wave, lane, g.hidden, g.V, v0, off, kind);
   for (int c = 0; c < AHEAD && c < n_chunks; ++c)
-    screen_dma<RB, kLo>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind, ring[c]);
-  const int woff = ((32 * wave + l32) * S::U + half) * 8;
-  const int hoff = (l32 * S::U + half) * 8;
+    screen_dma<S>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind, ring[c]);
+  const int woff = ((32 * wv + l32) * S::U + half) * 8;
+  const int hoff = ((32 * rb0 + l32) * S::U + half) * 8;
   for (int ci = 0; ci < n_chunks; ++ci) {
     screen_wait<S::LPW, AHEAD>(n_chunks - 1 - ci);
     ring_barrier();
     const int nxt = ci + AHEAD;
     if (nxt < n_chunks)
-      screen_dma<RB, kLo>(wrow + nxt * kKChunk, hrow + nxt * kKChunk, lrow + nxt * kKChunk, wave, off, kind,
-                          ring[nxt % S::NST]);
+      screen_dma<S>(wrow + nxt * kKChunk, hrow + nxt * kKChunk, lrow + nxt * kKChunk, wave, off, kind,
+                    ring[nxt % S::NST]);
     const uint16_t* st = ring[ci % S::NST];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
       const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + woff + 16 * t);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff + rb * 32 * S::U * 8 + 16 * t);
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
         if (kLo) {
@@ -250,77 +253,85 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_bf16(Geometry g, Voca
     }
   }
 
-  // lane holds z for row m0 + 32rb + l32 and vocab v0 + 32w + 8jj + 4half + ii
+  // lane holds z for row m0 + 32(rb0 + rb) + l32 and vocab v0 + 32wv + 8jj + 4half + ii
   if (n_split > 1) {
     float* zp = a.zpart;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = m0 + 32 * rb + l32;
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int r = m0 + 32 * (rb0 + rb) + l32;
       if (r < M) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int v = v0 + 32 * wave + 8 * jj + 4 * half;
+          const int v = v0 + 32 * wv + 8 * jj + 4 * half;
           floatx4 q = {acc[rb][4 * jj], acc[rb][4 * jj + 1], acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]};
           *reinterpret_cast<floatx4*>(zp + ((int64_t)split * M + r) * a.v_pad + v) = q;
         }
       }
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int* ticket = a.tickets + mt * gridDim.x + vt;
-      const int prev = atomicAdd(ticket, 1);
-      last_flag = (prev == n_split - 1);
-      if (last_flag) *ticket = 0;             // self-cleaning for the next launch
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = m0 + 32 * rb + l32;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
-      if (r < M) {
-        for (int sp = 0; sp < n_split; ++sp) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int v = v0 + 32 * wave + 8 * jj + 4 * half;
-            const floatx4 q = *reinterpret_cast<const floatx4*>(zp + ((int64_t)sp * M + r) * a.v_pad + v);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[rb][4 * jj + ii] += q[ii];
-          }
-        }
-      }
-    }
+    return;                                   // k_screen_reduce folds the splits
   }
 
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     float vals[16];
     int idx[16];
-    const int r = m0 + 32 * rb + l32;
+    const int r = m0 + 32 * (rb0 + rb) + l32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int jj = e / 4, ii = e % 4;
-      const int v = v0 + 32 * wave + 8 * jj + 4 * half + ii;
+      const int v = v0 + 32 * wv + 8 * jj + 4 * half + ii;
       idx[e] = v;
       vals[e] = v < g.V ? acc[rb][e] : kNegInf;
       if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[rb][e];
     }
     Top2 t = summarize<16>(vals, idx);
     t = top2_merge(t, top2_shfl_xor(t, 32));
-    if (half == 0) red[wave][32 * rb + l32] = t;
+    if (half == 0) red[wv][32 * (rb0 + rb) + l32] = t;
   }
   __syncthreads();
   if (threadIdx.x < MT) {
     const int r = threadIdx.x;
     Top2 t = red[0][r];
 #pragma unroll
-    for (int wv = 1; wv < 4; ++wv) t = top2_merge(t, red[wv][r]);
+    for (int w = 1; w < 4; ++w) t = top2_merge(t, red[w][r]);
     const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
     if (m0 + r < a.m_pad) store_partial(a.partials + ((int64_t)(m0 + r) * n_vt + vt) * 8, t);
   }
+}
+
+// Fold the hidden-split partial logits of one 128-vocab tile for 32 rows:
+// thread t: row t/8, vocab columns 16(t%8) .. +16; splits summed in order.
+__global__ __launch_bounds__(256) void k_screen_reduce(Geometry g, VocabArgs a, int M, int n_split) {
+  const int vt = blockIdx.x;
+  const int r = blockIdx.y * 32 + threadIdx.x / 8;
+  const int c0 = vt * kVocabTile + 16 * (threadIdx.x % 8);
+  float vals[16];
+  int idx[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) vals[e] = 0.f;
+  if (r < M) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const floatx4* z = reinterpret_cast<const floatx4*>(a.zpart + ((int64_t)sp * M + r) * a.v_pad + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v = z[q];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) vals[4 * q + ii] += v[ii];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int v = c0 + e;
+    idx[e] = v;
+    if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = vals[e];
+    if (v >= g.V) vals[e] = kNegInf;
+  }
+  Top2 t = summarize<16>(vals, idx);
+#pragma unroll
+  for (int mask = 1; mask < 8; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
+  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+  if (threadIdx.x % 8 == 0 && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, t);
 }
 
 // ------------------------------------------------------------ screen, fp32 --
@@ -579,15 +590,22 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(n_vt, m_tiles, n_split);
-#define MDM_SCREEN(RB)                                                                              \
-  if (a.hlo) hipLaunchKernelGGL((k_screen_bf16<RB, true>), grid, dim3(kScreenThreads), 0, s, g, pa, M, n_split); \
-  else hipLaunchKernelGGL((k_screen_bf16<RB, false>), grid, dim3(kScreenThreads), 0, s, g, pa, M, n_split)
-  if (rb == 1) { MDM_SCREEN(1); }
-  else if (rb == 2) { MDM_SCREEN(2); }
-  else { MDM_SCREEN(4); }
+#define MDM_SCREEN(RB, NG)                                                                              \
+  if (a.hlo) hipLaunchKernelGGL((k_screen_bf16<RB, NG, true>), grid, dim3(ScreenStage<RB, NG, true>::THREADS), 0, s, \
+                                g, pa, M, n_split);                                                      \
+  else hipLaunchKernelGGL((k_screen_bf16<RB, NG, false>), grid, dim3(ScreenStage<RB, NG, false>::THREADS), 0, s,     \
+                          g, pa, M, n_split)
+  if (rb == 1) { MDM_SCREEN(1, 1); }
+  else if (rb == 2) { MDM_SCREEN(2, 2); }
+  else { MDM_SCREEN(4, 2); }
 #undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (n_split > 1) {
+    hipLaunchKernelGGL(k_screen_reduce, dim3(n_vt, (M + 31) / 32), dim3(256), 0, s, g, pa, M, n_split);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
   return hipGetLastError();
 }
