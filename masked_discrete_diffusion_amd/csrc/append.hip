@@ -27,13 +27,77 @@ struct Elem<float> {
   static __device__ float from_f64(double x) { return (float)x; }
 };
 
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {   // 16 bf16 = two 16-byte units
+  static __device__ inline void load(const uint16_t* p, float* out) {
+    const u16x8 x0 = reinterpret_cast<const u16x8*>(p)[0];
+    const u16x8 x1 = reinterpret_cast<const u16x8*>(p)[1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { out[e] = bf16_to_f32(x0[e]); out[8 + e] = bf16_to_f32(x1[e]); }
+  }
+};
+template <>
+struct Vec16<float> {
+  static __device__ inline void load(const float* p, float* out) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4 x = reinterpret_cast<const floatx4*>(p)[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * q + e] = x[e];
+    }
+  }
+};
+
+// RoPE of kEpt consecutive elements (kEpt/2 interleaved pairs) from src to dst.
+template <typename T, int kEpt>
+__device__ inline void rope_store(const T* src, T* dst, const float* cs, const float* sn) {
+  static_assert(kEpt % 16 == 0 || kEpt == 8, "kEpt");
+  float x[kEpt];
+  if constexpr (kEpt >= 16) {
+#pragma unroll
+    for (int q = 0; q < kEpt / 16; ++q) Vec16<T>::load(src + 16 * q, x + 16 * q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) x[e] = Elem<T>::load(src, e);
+  }
+  T y[kEpt];
+#pragma unroll
+  for (int p = 0; p < kEpt / 2; ++p) {
+    double r0d, r1d;
+    rope_pair(x[2 * p], x[2 * p + 1], cs[p], sn[p], r0d, r1d);
+    y[2 * p] = Elem<T>::from_f64(r0d);
+    y[2 * p + 1] = Elem<T>::from_f64(r1d);
+  }
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < kEpt / 8; ++q) {
+      u16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = y[8 * q + e];
+      reinterpret_cast<u16x8*>(dst)[q] = v;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kEpt / 4; ++q) {
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = y[4 * q + e];
+      reinterpret_cast<floatx4*>(dst)[q] = v;
+    }
+  }
+}
+
+// Block: 32 rows of one (sequence, kv head); thread: row t/8, elements
+// [D/8 * (t%8), +D/8).  Writes the keys, the transposed values and, with qout,
+// the queries of the kv head's G query heads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   constexpr int kEpt = D / 8;                 // elements per thread (8 threads per row)
   __shared__ T vs[kRowsPerBlock][D + 2];
   const int b = blockIdx.z;
-  const bool q_block = blockIdx.y >= g.Hkv;   // blocks past the kv heads write queries
-  const int kvh = q_block ? blockIdx.y - g.Hkv : blockIdx.y;
+  const int kvh = blockIdx.y;
   const int r0 = blockIdx.x * kRowsPerBlock;
   const int n_rows = a.n_a + a.n_reg;
   const int t = threadIdx.x;
@@ -55,43 +119,34 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
     if (pos < 0 || pos >= g.max_pos) { flag_error(a.err, kErrPos); pos = 0; }
   }
 
-  if (q_block) {
-    if (!valid) return;
-    const T* qsrc = static_cast<const T*>(a.tq) + (int64_t)id * g.H * D + kvh * D + part * kEpt;
-    T* qdst = static_cast<T*>(a.qout) + (((int64_t)b * g.H + kvh) * a.q_rows + r) * D + part * kEpt;
-    const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + part * (kEpt / 2);
-    const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + part * (kEpt / 2);
-#pragma unroll
-    for (int p = 0; p < kEpt / 2; ++p) {
-      double r0d, r1d;
-      rope_pair(Elem<T>::load(qsrc, 2 * p), Elem<T>::load(qsrc, 2 * p + 1), cs[p], sn[p], r0d, r1d);
-      qdst[2 * p] = Elem<T>::from_f64(r0d);
-      qdst[2 * p + 1] = Elem<T>::from_f64(r1d);
-    }
-    return;
-  }
-
-  const T* tk = static_cast<const T*>(a.tk);
   const T* tv = static_cast<const T*>(a.tv);
-  T* kc = static_cast<T*>(a.kc);
   T* vc = static_cast<T*>(a.vc);
-  const int64_t head_base = ((int64_t)b * g.Hkv + kvh) * g.slots;
   const int slot = a.slot0 + r;
-
   if (valid) {
-    const T* ksrc = tk + (int64_t)id * g.Hkv * D + kvh * D + part * kEpt;
-    const T* vsrc = tv + (int64_t)id * g.Hkv * D + kvh * D + part * kEpt;
-    T* kdst = kc + (head_base + slot) * D + part * kEpt;
-    const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + part * (kEpt / 2);
-    const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+    float cs[kEpt / 2], sn[kEpt / 2];
+    const float* cp = a.rope_cos + (int64_t)pos * (D / 2) + part * (kEpt / 2);
+    const float* sp = a.rope_sin + (int64_t)pos * (D / 2) + part * (kEpt / 2);
 #pragma unroll
-    for (int p = 0; p < kEpt / 2; ++p) {
-      double r0d, r1d;
-      rope_pair(Elem<T>::load(ksrc, 2 * p), Elem<T>::load(ksrc, 2 * p + 1), cs[p], sn[p], r0d, r1d);
-      kdst[2 * p] = Elem<T>::from_f64(r0d);
-      kdst[2 * p + 1] = Elem<T>::from_f64(r1d);
+    for (int q = 0; q < kEpt / 8; ++q) {
+      const floatx4 c4 = reinterpret_cast<const floatx4*>(cp)[q];
+      const floatx4 s4 = reinterpret_cast<const floatx4*>(sp)[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { cs[4 * q + e] = c4[e]; sn[4 * q + e] = s4[e]; }
+    }
+    const int64_t head_base = ((int64_t)b * g.Hkv + kvh) * g.slots;
+    rope_store<T, kEpt>(static_cast<const T*>(a.tk) + ((int64_t)id * g.Hkv + kvh) * D + part * kEpt,
+                        static_cast<T*>(a.kc) + (head_base + slot) * D + part * kEpt, cs, sn);
+    if (a.qout) {
+      const int G = g.H / g.Hkv;
+      for (int gi = 0; gi < G; ++gi) {
+        const int h = kvh * G + gi;
+        rope_store<T, kEpt>(static_cast<const T*>(a.tq) + ((int64_t)id * g.H + h) * D + part * kEpt,
+                            static_cast<T*>(a.qout) + (((int64_t)b * g.H + h) * a.q_rows + r) * D + part * kEpt,
+                            cs, sn);
+      }
     }
     if (vc) {
+      const T* vsrc = tv + ((int64_t)id * g.Hkv + kvh) * D + part * kEpt;
 #pragma unroll
       for (int e = 0; e < kEpt; ++e) vs[lr][part * kEpt + e] = vsrc[e];
     }
@@ -106,7 +161,9 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
   // the block's rows are consecutive slots of one or two tiles
   const int rows_here = min(kRowsPerBlock, n_rows - r0);
   T* vhead = vc + ((int64_t)b * g.Hkv + kvh) * D * g.slots;
-  for (int e = t; e < D * kRowsPerBlock; e += blockDim.x) {
+#pragma unroll
+  for (int e0 = 0; e0 < D * kRowsPerBlock; e0 += 256) {
+    const int e = e0 + t;
     const int dd = e / kRowsPerBlock, rr = e % kRowsPerBlock;
     const int sl = a.slot0 + r0 + rr;
     if (rr < rows_here) vhead[((int64_t)(sl / kKeyTile) * D + dd) * kKeyTile + sl % kKeyTile] = vs[rr][dd];
@@ -137,7 +194,7 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
 hipError_t launch_append(const Geometry& g, const AppendArgs& a, hipStream_t s) {
   const int n_rows = a.n_a + a.n_reg;
   if (n_rows <= 0) return hipSuccess;
-  dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, g.Hkv + (a.qout ? g.H : 0), g.B);
+  dim3 grid((n_rows + kRowsPerBlock - 1) / kRowsPerBlock, g.Hkv, g.B);
   if (g.fp32) {
     if (g.D == 128) hipLaunchKernelGGL((k_append<float, 128>), grid, dim3(256), 0, s, g, a);
     else hipLaunchKernelGGL((k_append<float, 64>), grid, dim3(256), 0, s, g, a);

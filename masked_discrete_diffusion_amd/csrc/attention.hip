@@ -648,16 +648,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   }
 }
 
-// Merge of the key-split partials: one 128-thread block per chunk (blockIdx =
-// chunk group * 8 + chunk slot); thread: row tid/4, dims [D/4 * (tid%4), +D/4).
+// Merge of the key-split partials: one 256-thread block per chunk (blockIdx =
+// chunk group * 8 + chunk slot); thread: row tid/8, dims [D/8 * (tid%8), +D/8).
 // Splits are folded in split order (fixed arithmetic, independent of which
 // block ran first): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// M = max_s m_s.
-constexpr int kCombineThreads = 128;
+// M = max_s m_s.  KS >= ksplit bounds the unrolled split loop, so that every
+// split's loads are in flight together.
+constexpr int kCombineThreads = 256;
 
-template <int D>
+template <int D, int KS>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(Geometry g, AttnArgs a, ChunkPlan cp) {
-  constexpr int QD = D / 4;
+  constexpr int QD = D / 8;
   const int group = blockIdx.x / kAttnWaves;
   const int wave = blockIdx.x % kAttnWaves;       // chunk slot of the group (the wavefront that wrote it)
   const int G = g.H / g.Hkv;
@@ -673,37 +674,47 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(Geometry g, At
   int row_base, row_end;
   bool is_cr;
   chunk_rows(a, cp, 32, ch % cp.n_chunks, row_base, row_end, is_cr);
-  const int r = threadIdx.x / 4, part = threadIdx.x % 4;
+  const int r = threadIdx.x / 8, part = threadIdx.x % 8;
   const int row = row_base + r;
   if (row >= row_end) return;
   const int64_t slot0 = (int64_t)group * cp.ksplit;
+  float2 ml[KS];
+  floatx4 v[KS][QD / 4];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int64_t slot = (slot0 + (s < cp.ksplit ? s : 0)) * kAttnWaves + wave;
+    ml[s] = *reinterpret_cast<const float2*>(a.part_ml + slot * 64 + 2 * r);
+    const floatx4* ps = reinterpret_cast<const floatx4*>(a.part_o + slot * 32 * D + r * D + part * QD);
+#pragma unroll
+    for (int q = 0; q < QD / 4; ++q) v[s][q] = ps[q];
+  }
   float mx = -1e30f;
-  for (int s = 0; s < cp.ksplit; ++s) mx = fmaxf(mx, a.part_ml[((slot0 + s) * kAttnWaves + wave) * 64 + 2 * r]);
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    if (s < cp.ksplit) mx = fmaxf(mx, ml[s].x);
   floatx4 sum[QD / 4];
 #pragma unroll
   for (int q = 0; q < QD / 4; ++q) sum[q] = floatx4{0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int s = 0; s < cp.ksplit; ++s) {
-    const int64_t slot = (slot0 + s) * kAttnWaves + wave;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[slot * 64 + 2 * r] - mx);
-    lsum = fmaf(w, a.part_ml[slot * 64 + 2 * r + 1], lsum);
-    const floatx4* ps = reinterpret_cast<const floatx4*>(a.part_o + slot * 32 * D + r * D + part * QD);
 #pragma unroll
-    for (int q = 0; q < QD / 4; ++q) {
-      const floatx4 v = ps[q];
+  for (int s = 0; s < KS; ++s) {
+    if (s >= cp.ksplit) break;
+    const float w = __builtin_amdgcn_exp2f(ml[s].x - mx);
+    lsum = fmaf(w, ml[s].y, lsum);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sum[q][ii] = fmaf(w, v[ii], sum[q][ii]);
-    }
+    for (int q = 0; q < QD / 4; ++q)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sum[q][ii] = fmaf(w, v[s][q][ii], sum[q][ii]);
   }
   const float inv = 1.f / lsum;
   const int n_q = a.n_d + a.n_c + a.n_r;
   floatx4* o = reinterpret_cast<floatx4*>(a.out + ((int64_t)b * n_q + row) * g.hidden + h * D + part * QD);
 #pragma unroll
   for (int q = 0; q < QD / 4; ++q) {
-    floatx4 v;
+    floatx4 x;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) v[ii] = sum[q][ii] * inv;
-    o[q] = v;
+    for (int ii = 0; ii < 4; ++ii) x[ii] = sum[q][ii] * inv;
+    o[q] = x;
   }
 }
 
@@ -855,8 +866,13 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     else hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     if (ks > 1) {
       const dim3 cgrid(groups * kAttnWaves);
-      if (g.D == 128) hipLaunchKernelGGL((k_attn_combine<128>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp);
-      else hipLaunchKernelGGL((k_attn_combine<64>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp);
+#define MDM_COMBINE(KS)                                                                                 \
+  if (g.D == 128) hipLaunchKernelGGL((k_attn_combine<128, KS>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp); \
+  else hipLaunchKernelGGL((k_attn_combine<64, KS>), cgrid, dim3(kCombineThreads), 0, s, g, a, cp)
+      if (ks <= 2) { MDM_COMBINE(2); }
+      else if (ks <= 4) { MDM_COMBINE(4); }
+      else { MDM_COMBINE(kAttnMaxSplit); }
+#undef MDM_COMBINE
     }
   }
   return hipGetLastError();

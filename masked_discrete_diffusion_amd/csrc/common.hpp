@@ -71,6 +71,60 @@ __device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// ---- wavefront all-reduce without LDS ------------------------------------------
+// wave_pair<S>(x) returns this lane's value and its step-S partner's as {a, b},
+// in an order that may differ between the two partners.  Steps 0..5 pair the
+// lanes 1 apart and 2 apart (DPP quad permutes), across the two halves of each
+// 8 and each 16 lanes (DPP row half-mirror, row mirror), 16 apart
+// (v_permlane16_swap) and 32 apart (v_permlane32_swap).  After steps 0..s
+// every lane holds the result over its aligned group of 2^(s+1) lanes; with a
+// symmetric combining function both partners compute identical bits, so the
+// result is deterministic and uniform over the group.
+struct U2 {
+  uint32_t a, b;
+};
+template <int S>
+__device__ inline U2 wave_pair(uint32_t x) {
+  static_assert(S >= 0 && S <= 5, "step");
+  if constexpr (S == 0) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false)};
+  else if constexpr (S == 1) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false)};
+  else if constexpr (S == 2) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false)};
+  else if constexpr (S == 3) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false)};
+  else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return {(uint32_t)r[0], (uint32_t)r[1]};
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return {(uint32_t)r[0], (uint32_t)r[1]};
+  }
+}
+
+// Sum over aligned groups of 2^N lanes (N <= 6): steps 0..N-1.
+template <int N>
+__device__ inline float group_sum(float x) {
+  if constexpr (N > 0) {
+    x = group_sum<N - 1>(x);
+    const U2 p = wave_pair<N - 1>(__float_as_uint(x));
+    x = __uint_as_float(p.a) + __uint_as_float(p.b);
+  }
+  return x;
+}
+
+// (value desc, index asc) best pair over aligned groups of 2^N lanes.
+template <int N>
+__device__ inline void group_argmax(float& v, int& i) {
+  if constexpr (N > 0) {
+    group_argmax<N - 1>(v, i);
+    const U2 pv = wave_pair<N - 1>(__float_as_uint(v));
+    const U2 pi = wave_pair<N - 1>((uint32_t)i);
+    const float va = __uint_as_float(pv.a), vb = __uint_as_float(pv.b);
+    const int ia = (int)pi.a, ib = (int)pi.b;
+    const bool tb = ranks_before(vb, ib, va, ia);
+    v = tb ? vb : va;
+    i = tb ? ib : ia;
+  }
+}
+
 // ---- LDS-DMA rings -----------------------------------------------------------
 // A wave-wide global_load_lds_dwordx4 writes 64 consecutive 16-byte units of
 // LDS starting at `lds_block` (uniform); lane l's 16 bytes come from

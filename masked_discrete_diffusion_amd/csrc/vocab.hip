@@ -404,8 +404,10 @@ __global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int
 
 // ----------------------------------------------------- merge and re-score --
 // One block (4 wavefronts) per row: the threads fold the tiles' (max, sum of
-// exp, top-2) partials, the block keeps the kTopK best candidates, and wave k
-// re-scores candidate k exactly in fp32 from the fp32 h.
+// exp, top-2) partials, the block keeps the kTopK best candidates, and all
+// threads re-score the candidates together exactly in fp32 from the fp32 h
+// (each thread a slice of hidden for every candidate, then a fixed-order
+// reduction).
 struct Cand {
   float v;
   int i;
@@ -449,17 +451,33 @@ __device__ inline void lse_merge(float& m, float& se, float om, float ose) {
   m = nm;
 }
 
+// (max, sum of exp) over the whole wavefront
+__device__ inline void wave_lse(float& m, float& se) {
+  static_assert(kWave == 64, "wave");
+#define MDM_LSE_STEP(S)                                                   \
+  {                                                                       \
+    const U2 pm = wave_pair<S>(__float_as_uint(m));                       \
+    const U2 ps = wave_pair<S>(__float_as_uint(se));                      \
+    float m0 = __uint_as_float(pm.a), s0 = __uint_as_float(ps.a);          \
+    lse_merge(m0, s0, __uint_as_float(pm.b), __uint_as_float(ps.b));       \
+    m = m0;                                                               \
+    se = s0;                                                              \
+  }
+  MDM_LSE_STEP(0) MDM_LSE_STEP(1) MDM_LSE_STEP(2) MDM_LSE_STEP(3) MDM_LSE_STEP(4) MDM_LSE_STEP(5)
+#undef MDM_LSE_STEP
+}
+
 template <typename WT>
 __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
   __shared__ float s_m[4], s_se[4];
   __shared__ Cand s_c[4][kTopK];
-  __shared__ Cand s_best[kTopK];
-  __shared__ float s_ze[kTopK];
+  __shared__ float s_dot[4][kTopK];
   const int m = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
   const float* part = a.partials + (int64_t)m * n_vt * 8;
 
+  // 1. fold the tiles: (max, sum of exp) and each lane's kTopK best
   float lm = kNegInf, lse = 0.f;
   Cand c[kTopK];
 #pragma unroll
@@ -471,22 +489,14 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
     cand_insert(c, p0[2], __float_as_int(p0[3]));
     cand_insert(c, p1[0], __float_as_int(p1[1]));
   }
-#pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) lse_merge(lm, lse, __shfl_xor(lm, mask), __shfl_xor(lse, mask));
+  wave_lse(lm, lse);
   // wave top-K: K rounds of a (value desc, index asc) argmax; the owner pops
-  Cand wb[kTopK];
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) {
     float bv = c[0].v;
     int bi = c[0].i;
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) {
-      const float ov = __shfl_xor(bv, mask);
-      const int oi = __shfl_xor(bi, mask);
-      if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    wb[k].v = bv;
-    wb[k].i = bi;
+    group_argmax<6>(bv, bi);
+    if (lane == 0) s_c[wave][k] = Cand{bv, bi};
     if (bi == c[0].i && bi != 0x7fffffff) {
 #pragma unroll
       for (int q = 0; q < kTopK - 1; ++q) c[q] = c[q + 1];
@@ -494,68 +504,108 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
       c[kTopK - 1].i = 0x7fffffff;
     }
   }
-  if (lane == 0) {
-    s_m[wave] = lm;
-    s_se[wave] = lse;
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) s_c[wave][k] = wb[k];
-  }
+  if (lane == 0) { s_m[wave] = lm; s_se[wave] = lse; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    Cand best[kTopK];
+
+  // 2. block top-K, taken by every wave from the 4 x kTopK wave candidates in
+  //    lanes 0..15 (indices are distinct: each vocab column lives in one tile)
+  float bestv[kTopK];
+  int besti[kTopK];
+  {
+    float cv = kNegInf;
+    int ci = 0x7fffffff;
+    if (lane < 4 * kTopK) { cv = s_c[lane / kTopK][lane % kTopK].v; ci = s_c[lane / kTopK][lane % kTopK].i; }
 #pragma unroll
-    for (int k = 0; k < kTopK; ++k) { best[k].v = kNegInf; best[k].i = 0x7fffffff; }
-    for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-      for (int k = 0; k < kTopK; ++k) cand_insert(best, s_c[wv][k].v, s_c[wv][k].i);
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) s_best[k] = best[k];
+    for (int k = 0; k < kTopK; ++k) {
+      float bv = cv;
+      int bi = ci;
+      group_argmax<4>(bv, bi);
+      bestv[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
+      besti[k] = __builtin_amdgcn_readfirstlane(bi);
+      if (ci == besti[k] && ci != 0x7fffffff) { cv = kNegInf; ci = 0x7fffffff; }
+    }
   }
-  __syncthreads();
-  // wave k re-scores candidate k
+
+  // 3. exact fp32 logits of the candidates: thread t takes hidden elements
+  //    [8t + 2048j, +8) for all kTopK candidates, so the h row is read once;
+  //    then a fixed-order sum (lanes, then waves)
   const int b = m / a.n_c, cc = m % a.n_c;
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
   const WT* w = static_cast<const WT*>(a.w);
-  for (int k = wave; k < kTopK; k += 4) {
-    const int v = s_best[k].i;
-    const bool ok = v >= 0 && v < g.V;
-    const WT* wr = w + (int64_t)(ok ? v : 0) * g.hidden;
-    float sacc = 0.f;
-#pragma unroll 4
-    for (int e0 = 8 * lane; e0 < g.hidden; e0 += 8 * kWave) {
-      const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
-      const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
-      float wv[8];
-      W8<WT>::load(wr + e0, wv);
+  const WT* wr[kTopK];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sacc = fmaf(h0[e], wv[e], sacc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc = fmaf(h1[e], wv[4 + e], sacc);
-    }
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) sacc += __shfl_xor(sacc, mask);
-    if (lane == 0) s_ze[k] = ok ? sacc : kNegInf;
+  for (int k = 0; k < kTopK; ++k) {
+    const bool ok = besti[k] >= 0 && besti[k] < g.V;
+    wr[k] = w + (int64_t)(ok ? besti[k] : 0) * g.hidden;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float bm = s_m[0], bse = s_se[0];
-    for (int wv = 1; wv < 4; ++wv) lse_merge(bm, bse, s_m[wv], s_se[wv]);
-    int tb = 0;
+  float dot[kTopK];
 #pragma unroll
-    for (int k = 1; k < kTopK; ++k)
-      if (ranks_before(s_ze[k], s_best[k].i, s_ze[tb], s_best[tb].i)) tb = k;
-    double mx = bm;
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k)
-      if (s_ze[k] != kNegInf) mx = fmax(mx, (double)s_ze[k]);
-    double tot = (double)bse * exp((double)bm - mx);
+  for (int k = 0; k < kTopK; ++k) dot[k] = 0.f;
+#pragma unroll 2
+  for (int e0 = 8 * threadIdx.x; e0 < g.hidden; e0 += 8 * 256) {
+    const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
+    const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
 #pragma unroll
     for (int k = 0; k < kTopK; ++k) {
-      if (s_ze[k] == kNegInf) continue;
-      tot += exp((double)s_ze[k] - mx) - exp((double)s_best[k].v - mx);
+      float wv[8];
+      W8<WT>::load(wr[k] + e0, wv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[k] = fmaf(h0[e], wv[e], dot[k]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[k] = fmaf(h1[e], wv[4 + e], dot[k]);
     }
-    a.conf[m] = (float)(exp((double)s_ze[tb] - mx) / tot);
-    a.token[m] = s_best[tb].i;
+  }
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) dot[k] = group_sum<6>(dot[k]);
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) s_dot[wave][k] = dot[k];
+  __syncthreads();
+  if (wave != 0) return;
+
+  // 4. decision and confidence (wave 0).  The exact logit replaces the
+  //    screened term of each candidate in the sum of exp; the double exps are
+  //    taken one per lane and summed by lane 0 in a fixed order.
+  float bm = s_m[0], bse = s_se[0];
+  for (int wv = 1; wv < 4; ++wv) lse_merge(bm, bse, s_m[wv], s_se[wv]);
+  float ze[kTopK];
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    const bool ok = besti[k] >= 0 && besti[k] < g.V;
+    ze[k] = ok ? ((s_dot[0][k] + s_dot[1][k]) + (s_dot[2][k] + s_dot[3][k])) : kNegInf;
+  }
+  int tb = 0;
+#pragma unroll
+  for (int k = 1; k < kTopK; ++k)
+    if (ranks_before(ze[k], besti[k], ze[tb], besti[tb])) tb = k;
+  double mx = bm;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k)
+    if (ze[k] != kNegInf) mx = fmax(mx, (double)ze[k]);
+  // lane 0: the screened sum; lane 1+k: exact term k; lane 1+kTopK+k: screened term k
+  double arg = (double)bm - mx;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) {
+    if (lane == 1 + k) arg = (double)ze[k] - mx;
+    if (lane == 1 + kTopK + k) arg = (double)bestv[k] - mx;
+  }
+  const double ex = exp(arg);
+  double terms[2 * kTopK + 1];
+#pragma unroll
+  for (int q = 0; q <= 2 * kTopK; ++q) terms[q] = __shfl(ex, q);
+  if (lane == 0) {
+    double tot = (double)bse * terms[0];
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+      if (ze[k] == kNegInf) continue;
+      tot += terms[1 + k] - terms[1 + kTopK + k];
+    }
+    double et = terms[1];
+#pragma unroll
+    for (int k = 1; k < kTopK; ++k)
+      if (tb == k) et = terms[1 + k];
+    a.conf[m] = (float)(et / tot);
+    a.token[m] = besti[tb];
   }
 }
 
