@@ -293,12 +293,9 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Softmax of one 32-key half for this lane's row: lazily raise the reference
-// (rescaling O and l when a row maximum passes it by more than kRescaleLog2),
-// then p = exp2(s * sc - m_ref) in place and their sum added to l.
-template <int NDB, bool kEdge>
-__device__ inline void half_softmax(floatx16& sv, floatx16* acc, float& m_ref, float& l_run, int key_base,
-                                    int wlen, int half, float sc) {
+// Masking and row maximum (log2 units) of one 32-key half for this lane's row.
+template <bool kEdge>
+__device__ inline float half_max(floatx16& sv, int key_base, int wlen, int half, float sc) {
   if (kEdge) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -310,17 +307,24 @@ __device__ inline void half_softmax(floatx16& sv, floatx16* acc, float& m_ref, f
   float mt = max3(sv[0], sv[1], sv[2]);
 #pragma unroll
   for (int e = 3; e < 15; e += 2) mt = max3(mt, sv[e], sv[e + 1]);
-  mt = halves_max(max3(mt, sv[15], sv[15])) * sc;
-  if (__any(mt > m_ref + kRescaleLog2)) {
-    const float m_new = fmaxf(m_ref, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-    l_run *= alpha;
+  return halves_max(max3(mt, sv[15], sv[15])) * sc;
+}
+
+// Raise the reference to mt (when above it), rescaling O and l.
+template <int NDB>
+__device__ inline void rescale(floatx16* acc, float& m_ref, float& l_run, float mt) {
+  const float m_new = fmaxf(m_ref, mt);
+  const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+  l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-    m_ref = m_new;
-  }
+    for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+  m_ref = m_new;
+}
+
+// p = exp2(s * sc - m_ref) in place, their sum added to l.
+__device__ inline void half_exp(floatx16& sv, float m_ref, float& l_run, float sc) {
   float lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -398,12 +402,28 @@ __device__ inline void finish_half(floatx16& sv, const uint16_t* vb, int hk, int
   using T = AttnTile<D>;
   constexpr int NDB = D / 32;
   const uint16_t* vhalf = vb + (l32 * T::VU + half + 4 * hk) * 8;
+  // The rare rescale path repeats the exp and PV code, so that no branch
+  // merges two definitions of the accumulators in front of the PV MFMAs.
   if (valid < kKeyTile) {
-    half_softmax<NDB, true>(sv, acc, m_ref, l_run, 32 * hk, valid, half, sc);
-    half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
+    const float mt = half_max<true>(sv, 32 * hk, valid, half, sc);
+    if (__any(mt > m_ref + kRescaleLog2)) {
+      rescale<NDB>(acc, m_ref, l_run, mt);
+      half_exp(sv, m_ref, l_run, sc);
+      half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
+    } else {
+      half_exp(sv, m_ref, l_run, sc);
+      half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
+    }
   } else {
-    half_softmax<NDB, false>(sv, acc, m_ref, l_run, 32 * hk, valid, half, sc);
-    half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
+    const float mt = half_max<false>(sv, 32 * hk, valid, half, sc);
+    if (__any(mt > m_ref + kRescaleLog2)) {
+      rescale<NDB>(acc, m_ref, l_run, mt);
+      half_exp(sv, m_ref, l_run, sc);
+      half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
+    } else {
+      half_exp(sv, m_ref, l_run, sc);
+      half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
+    }
   }
 }
 
