@@ -272,6 +272,14 @@ __device__ inline HiLo split_pair(float p0, float p1) {
 // divides by the same l, so the result is the same softmax.
 constexpr float kRescaleLog2 = 8.f;
 
+// Full tiles take a cheaper path: the reference is the row maximum over the
+// first full tile and is never raised in the loop, so no branch rescales (and
+// redefines) the accumulators there.  A wavefront only checks that no later
+// score passes the reference by more than kOverflowLog2 (p <= 2^16, far from
+// the fp32 range); if one does, the block recomputes everything on the lazy
+// path above.
+constexpr float kOverflowLog2 = 16.f;
+
 // max of three floats.  IEEE maximum (NaN-propagating) needs no canonicalising
 // moves in front of MFMA results and becomes one v_maximum3_f32; the compiler
 // inserts the MFMA-to-VALU wait states itself.  Scores are finite or -1e30
@@ -394,9 +402,9 @@ __device__ inline floatx16 s_half(const uint16_t* kb, const bf16x8* qf, int hk, 
   return sv;
 }
 
-// Softmax and O += V P for half hk of a tile whose first `valid` keys count
-// (valid < 64: the rest are removed by select).
-template <int D>
+// Softmax and O += V P for half hk of a tile.  kEdge: only the first `valid`
+// keys count (valid < 64; the rest are removed by select).
+template <int D, bool kEdge>
 __device__ inline void finish_half(floatx16& sv, const uint16_t* vb, int hk, int valid, floatx16* acc,
                                    float& m_ref, float& l_run, int half, int l32, float sc) {
   using T = AttnTile<D>;
@@ -404,74 +412,154 @@ __device__ inline void finish_half(floatx16& sv, const uint16_t* vb, int hk, int
   const uint16_t* vhalf = vb + (l32 * T::VU + half + 4 * hk) * 8;
   // The rare rescale path repeats the exp and PV code, so that no branch
   // merges two definitions of the accumulators in front of the PV MFMAs.
-  if (valid < kKeyTile) {
-    const float mt = half_max<true>(sv, 32 * hk, valid, half, sc);
-    if (__any(mt > m_ref + kRescaleLog2)) {
-      rescale<NDB>(acc, m_ref, l_run, mt);
-      half_exp(sv, m_ref, l_run, sc);
-      half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
-    } else {
-      half_exp(sv, m_ref, l_run, sc);
-      half_pv<D, true>(sv, vhalf, acc, 32 * hk, valid, half);
-    }
+  const float mt = half_max<kEdge>(sv, 32 * hk, valid, half, sc);
+  if (__builtin_expect(__any(mt > m_ref + kRescaleLog2), 0)) {
+    rescale<NDB>(acc, m_ref, l_run, mt);
+    half_exp(sv, m_ref, l_run, sc);
+    half_pv<D, kEdge>(sv, vhalf, acc, 32 * hk, valid, half);
   } else {
-    const float mt = half_max<false>(sv, 32 * hk, valid, half, sc);
-    if (__any(mt > m_ref + kRescaleLog2)) {
-      rescale<NDB>(acc, m_ref, l_run, mt);
-      half_exp(sv, m_ref, l_run, sc);
-      half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
-    } else {
-      half_exp(sv, m_ref, l_run, sc);
-      half_pv<D, false>(sv, vhalf, acc, 32 * hk, valid, half);
-    }
+    half_exp(sv, m_ref, l_run, sc);
+    half_pv<D, kEdge>(sv, vhalf, acc, 32 * hk, valid, half);
   }
 }
 
-// The tile loop of one wavefront.  LAG = false: both halves of tile i in
-// iteration i.  LAG = true (the second wavefront of each SIMD): iteration i
-// first finishes the second half of tile i-1 (scores carried in registers,
-// V still in its ring slot), then the first half of tile i, and leaves the
-// second half's scores for the next iteration.  The two wavefronts of a SIMD
-// are then in different phases (one in MFMA, the other in softmax VALU work)
-// instead of in lockstep after every barrier.
-template <int D, bool LAG>
-__device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvSrc& src,
+// Softmax and O += V P for half hk of a full tile at a fixed reference;
+// `over` records a score above the reference by more than kOverflowLog2.
+template <int D>
+__device__ inline void finish_half_fixed(floatx16& sv, const uint16_t* vb, int hk, floatx16* acc, float m_ref,
+                                         float& l_run, int half, int l32, float sc, bool& over) {
+  using T = AttnTile<D>;
+  const uint16_t* vhalf = vb + (l32 * T::VU + half + 4 * hk) * 8;
+  const float mt = half_max<false>(sv, 32 * hk, kKeyTile, half, sc);
+  over |= mt > m_ref + kOverflowLog2;
+  half_exp(sv, m_ref, l_run, sc);
+  half_pv<D, false>(sv, vhalf, acc, 32 * hk, kKeyTile, half);
+}
+
+// Order in which a block streams its tiles [t_lo, t_lo + n): the full tiles in
+// key order, then the partial last tiles of the segments (at most three).
+// Softmax does not depend on the order; keeping the partial tiles out of the
+// main loop keeps that loop free of masking code and of branches that would
+// merge accumulator definitions.
+// (Scalar members, read by value: an indexed array, or a select between
+// member addresses, would put the struct in scratch memory.)
+__device__ inline int order_at(int i, int t_lo, int n_full, int e0, int e1, int e2) {
+  if (i >= n_full) {
+    const int k = i - n_full;
+    return k == 0 ? e0 : (k == 1 ? e1 : e2);
+  }
+  int t = t_lo + i;
+  t += t >= e0;
+  t += t >= e1;
+  t += t >= e2;
+  return t;
+}
+struct TileOrder {
+  int t_lo, n, n_full;
+  int e0, e1, e2;          // partial tiles in key order; unused ones are INT_MAX
+  __device__ inline int at(int i) const { return order_at(i, t_lo, n_full, e0, e1, e2); }
+};
+
+// One ring step: wait for tile i (own loads, then the barrier for everyone's)
+// and issue the loads of tile i + kAhead.
+template <int D>
+__device__ inline void ring_step(const AttnArgs& a, const Geometry& g, const KvSrc& src, const TileOrder ord,
+                                 int T0, int T1, const uint32_t (&off)[AttnTile<D>::LPW],
+                                 uint16_t (*ks)[AttnTile<D>::K_ELEMS], uint16_t (*vs)[AttnTile<D>::V_ELEMS], int i,
+                                 int wave, int lane) {
+  using T = AttnTile<D>;
+  ring_wait_tiles<T::LPW>(ord.n - 1 - i);
+  ring_barrier();
+  const int nxt = i + kAhead;
+  if (nxt < ord.n)
+    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(nxt)), wave, lane, off, ks[nxt % kStages],
+                vs[nxt % kStages]);
+}
+
+// The tile loop of one wavefront, in three phases over the block's ring steps:
+//  1. the full tiles this wavefront's rows see (the first n_comp of the order;
+//     for D rows the full cache tiles, which come first), no masking;
+//  2. the remaining full tiles: ring steps only (D rows past the cache);
+//  3. the partial tiles, masked, when this wavefront's rows see them.
+// LAG = false: both halves of tile i in step i.  LAG = true (the second
+// wavefront of each SIMD): step i first finishes the second half of tile i-1
+// (scores carried in registers, V still in its ring slot), then the first
+// half of tile i, and leaves the second half's scores for the next step.  The
+// two wavefronts of a SIMD are then in different phases (one in MFMA, the
+// other in softmax VALU work) instead of in lockstep after every barrier.
+template <int D, bool LAG, bool FAST>
+__device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvSrc& src, const TileOrder ord,
                                  const uint32_t (&off)[AttnTile<D>::LPW], uint16_t (*ks)[AttnTile<D>::K_ELEMS],
                                  uint16_t (*vs)[AttnTile<D>::V_ELEMS], const bf16x8* qf, floatx16* acc, float& m_ref,
-                                 float& l_run, int T0, int T1, int t_lo, int n_my, int w_end, bool active, int wave,
-                                 int lane, int krow, int half, int l32, float sc) {
-  using T = AttnTile<D>;
-  floatx16 sv_carry;
-  int carry_valid = 0, carry_buf = 0;      // carry_valid > 0: a second half is pending
-  for (int i = 0; i < n_my; ++i) {
-    ring_wait_tiles<T::LPW>(n_my - 1 - i);
-    ring_barrier();
-    const int nxt = i + kAhead;
-    if (nxt < n_my)
-      tile_dma<D>(a, g, src, tile_ref(a, T0, T1, t_lo + nxt), wave, lane, off, ks[nxt % kStages],
-                  vs[nxt % kStages]);
-    if (!active) continue;
-    if (LAG && carry_valid > 0) {
-      finish_half<D>(sv_carry, vs[carry_buf], 1, carry_valid, acc, m_ref, l_run, half, l32, sc);
-      carry_valid = 0;
-    }
-    const int t = t_lo + i;
-    if (t >= w_end) continue;
-    const TileRef tr = tile_ref(a, T0, T1, t);
-    const int cur = i % kStages;
-    floatx16 sv = s_half<D>(ks[cur], qf, 0, krow, half);
-    finish_half<D>(sv, vs[cur], 0, tr.valid, acc, m_ref, l_run, half, l32, sc);
+                                 float& l_run, int T0, int T1, int n_comp, int w_end, bool active, int wave,
+                                 int lane, int krow, int half, int l32, float sc, bool& over) {
+  if (FAST && n_comp > 0) {
+    // first full tile: both halves' scores set the reference
+    ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, 0, wave, lane);
+    floatx16 sv = s_half<D>(ks[0], qf, 0, krow, half);
+    floatx16 sv1 = s_half<D>(ks[0], qf, 1, krow, half);
+    m_ref = fmaxf(half_max<false>(sv, 0, kKeyTile, half, sc), half_max<false>(sv1, 32, kKeyTile, half, sc));
+    finish_half_fixed<D>(sv, vs[0], 0, acc, m_ref, l_run, half, l32, sc, over);
     if (LAG) {
-      sv_carry = s_half<D>(ks[cur], qf, 1, krow, half);
-      carry_valid = tr.valid;
-      carry_buf = cur;
+      for (int i = 1; i < n_comp; ++i) {
+        ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+        finish_half_fixed<D>(sv1, vs[(i - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc, over);
+        const int cur = i % kStages;
+        sv = s_half<D>(ks[cur], qf, 0, krow, half);
+        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc, over);
+        sv1 = s_half<D>(ks[cur], qf, 1, krow, half);
+      }
+      finish_half_fixed<D>(sv1, vs[(n_comp - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc, over);
     } else {
-      sv = s_half<D>(ks[cur], qf, 1, krow, half);
-      finish_half<D>(sv, vs[cur], 1, tr.valid, acc, m_ref, l_run, half, l32, sc);
+      finish_half_fixed<D>(sv1, vs[0], 1, acc, m_ref, l_run, half, l32, sc, over);
+      for (int i = 1; i < n_comp; ++i) {
+        ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+        const int cur = i % kStages;
+        sv = s_half<D>(ks[cur], qf, 0, krow, half);
+        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc, over);
+        sv = s_half<D>(ks[cur], qf, 1, krow, half);
+        finish_half_fixed<D>(sv, vs[cur], 1, acc, m_ref, l_run, half, l32, sc, over);
+      }
     }
   }
-  if (LAG && carry_valid > 0)
-    finish_half<D>(sv_carry, vs[carry_buf], 1, carry_valid, acc, m_ref, l_run, half, l32, sc);
+  if (!FAST && n_comp > 0) {
+    if (LAG) {
+      ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, 0, wave, lane);
+      floatx16 sv = s_half<D>(ks[0], qf, 0, krow, half);
+      finish_half<D, false>(sv, vs[0], 0, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+      floatx16 sv_carry = s_half<D>(ks[0], qf, 1, krow, half);
+      for (int i = 1; i < n_comp; ++i) {
+        ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+        finish_half<D, false>(sv_carry, vs[(i - 1) % kStages], 1, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+        const int cur = i % kStages;
+        sv = s_half<D>(ks[cur], qf, 0, krow, half);
+        finish_half<D, false>(sv, vs[cur], 0, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+        sv_carry = s_half<D>(ks[cur], qf, 1, krow, half);
+      }
+      finish_half<D, false>(sv_carry, vs[(n_comp - 1) % kStages], 1, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+    } else {
+      for (int i = 0; i < n_comp; ++i) {
+        ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+        const int cur = i % kStages;
+        floatx16 sv = s_half<D>(ks[cur], qf, 0, krow, half);
+        finish_half<D, false>(sv, vs[cur], 0, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+        sv = s_half<D>(ks[cur], qf, 1, krow, half);
+        finish_half<D, false>(sv, vs[cur], 1, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+      }
+    }
+  }
+  for (int i = max(n_comp, 0); i < ord.n_full; ++i) ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+  for (int i = ord.n_full; i < ord.n; ++i) {
+    ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+    const int t = ord.at(i);
+    if (!active || t >= w_end) continue;
+    const int valid = tile_ref(a, T0, T1, t).valid;
+    const int cur = i % kStages;
+    floatx16 sv = s_half<D>(ks[cur], qf, 0, krow, half);
+    finish_half<D, true>(sv, vs[cur], 0, valid, acc, m_ref, l_run, half, l32, sc);
+    sv = s_half<D>(ks[cur], qf, 1, krow, half);
+    finish_half<D, true>(sv, vs[cur], 1, valid, acc, m_ref, l_run, half, l32, sc);
+  }
 }
 
 // Block: kAttnWaves wavefronts, each owning one 32-row chunk of one query head;
@@ -548,10 +636,43 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   src.rvt = static_cast<const uint16_t*>(a.rvt) + (int64_t)kvh * D * a.r_pad;
   src.kidx = kidx;
 
+  // stream order: full tiles, then the segments' partial last tiles
+  TileOrder ord;
+  ord.t_lo = t_lo;
+  ord.n = n_my;
+  {
+    constexpr int kNone = 0x7fffffff;
+    const int c0e = (a.S % kKeyTile) ? T0 - 1 : -1;
+    const int c1e = (a.n_c % kKeyTile) ? T0 + T1 - 1 : -1;
+    const int c2e = (a.n_r % kKeyTile) ? T0 + T1 + T2 - 1 : -1;
+    const bool in0 = c0e >= t_lo && c0e < t_lo + n_my;
+    const bool in1 = c1e >= t_lo && c1e < t_lo + n_my;
+    const bool in2 = c2e >= t_lo && c2e < t_lo + n_my;
+    // compact the present ones, in key order
+    const int f0 = in0 ? c0e : (in1 ? c1e : (in2 ? c2e : kNone));
+    const int f1 = in0 ? (in1 ? c1e : (in2 ? c2e : kNone)) : (in1 && in2 ? c2e : kNone);
+    const int f2 = in0 && in1 && in2 ? c2e : kNone;
+    ord.e0 = f0;
+    ord.e1 = f1;
+    ord.e2 = f2;
+    ord.n_full = n_my - (int)in0 - (int)in1 - (int)in2;
+  }
+  // full tiles this wavefront computes: all of them for C|R rows, the full
+  // cache tiles (a prefix of the order) for D rows
+  int n_comp = 0;
+  if (active) {
+    if (is_cr) {
+      n_comp = ord.n_full;
+    } else {
+      const bool cache_edge = (a.S % kKeyTile) && T0 - 1 >= t_lo && T0 - 1 < t_lo + n_my;
+      n_comp = max(0, min(t_lo + n_my, T0) - t_lo - (cache_edge ? 1 : 0));
+    }
+  }
+
   uint32_t off[T::LPW];
   dma_offsets<D>(wave, lane, off);
   for (int i = 0; i < kAhead && i < n_my; ++i)
-    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, t_lo + i), wave, lane, off, ks[i], vs[i]);
+    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
 
   // Q^T fragment (B operand): lane holds row l32, dims 16t + 8*half + 0..7, RoPE'd.
   // C and R rows read the query table (the mask token at the row's position,
@@ -623,12 +744,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   // Wavefronts 0-3 take a tile's halves in order within the iteration;
   // wavefronts 4-7 (the second wavefront of each SIMD) run half a tile
   // behind (see tile_loop).
+  bool over = false;
   if (wave >= kAttnWaves / 2)
-    tile_loop<D, true>(a, g, src, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, t_lo, n_my, w_end, active, wave, lane,
-                       krow, half, l32, sc);
+    tile_loop<D, true, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active, wave,
+                             lane, krow, half, l32, sc, over);
   else
-    tile_loop<D, false>(a, g, src, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, t_lo, n_my, w_end, active, wave, lane,
-                        krow, half, l32, sc);
+    tile_loop<D, false, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
+                              wave, lane, krow, half, l32, sc, over);
+  // A score far above its row's first-tile maximum somewhere in the block:
+  // stream the tiles again on the lazily rescaled path.
+  if (__syncthreads_or(over ? 1 : 0)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+    m_ref = -1e30f;
+    l_run = 0.f;
+    for (int i = 0; i < kAhead && i < n_my; ++i)
+      tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
+    bool unused = false;
+    if (wave >= kAttnWaves / 2)
+      tile_loop<D, true, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
+                                wave, lane, krow, half, l32, sc, unused);
+    else
+      tile_loop<D, false, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
+                                 wave, lane, krow, half, l32, sc, unused);
+  }
 
   const float l_tot = halves_sum(l_run);
   const int n_q = a.n_d + a.n_c + a.n_r;

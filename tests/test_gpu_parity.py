@@ -85,6 +85,10 @@ def test_generation_matches_oracle(cfgfn):
     cfg = cfgfn()
     _say(f"generation parity: {cfg.name}")
     wl, run = _runner(cfg)
+    _check_generation(cfg, wl, run)
+
+
+def _check_generation(cfg, wl, run):
     steps = list(range(cfg.n_steps))
     recs, seq = run.generate_recorded(keep_o=steps, keep_logits=steps)
     run.close()
@@ -108,6 +112,44 @@ def test_generation_matches_oracle(cfgfn):
             g["logits"].reshape(-1, cfg.vocab), zref, rtol, atol, f"logits step {k}"))
     assert np.array_equal(seq, res.tokens), "final sequences differ"
     _say(f"  worst abs errors: {worst}")
+
+
+def test_score_jump_falls_back_to_rescaled_path():
+    """Scores that rise far above a row's first-tile maximum.  Full key tiles
+    run at a reference fixed by the first full tile; a later score more than
+    2^16 above it makes the block recompute on the lazily rescaled path.  The
+    key-table row of one token is scaled by 64 (exact in bf16) and the token is
+    placed in the second cache tile only, so that (checked here on the CPU)
+    some register row's score against it passes its first-tile maximum by far
+    more than 16 in log2 units at step 0; the generation must still match the
+    oracle exactly."""
+    from mdm_inputs.generate import bf16_bits_from_f32, bf16_bits_to_f32
+    from oracle import rope
+    cfg = gpu_small_d128(index=114, name="gpu_small_score_jump", prompt_len=150)
+    _say(f"score jump: {cfg.name}")
+    wl = make_workload(cfg)
+    hot = 5
+    wl.tk[hot] = bf16_bits_from_f32(bf16_bits_to_f32(wl.tk[hot]) * np.float32(64.0))
+    p = wl.prompt_ids
+    p[:, :64][p[:, :64] == hot] = hot + 1
+    p[:, 64:128:9] = hot
+    # precondition on the CPU: register rows of step 0 against the prompt keys
+    d, hk = cfg.head_dim, cfg.n_kv_heads
+    cos_t, sin_t = rope.table(cfg.seq_len + cfg.n_registers, d)
+    g = cfg.n_heads // hk
+    jump = 0.0
+    for b in range(cfg.batch):
+        keys = table_values(wl.tk[p[b]]).reshape(cfg.prompt_len, hk, d)
+        keys = rope.rotate(keys, np.arange(cfg.prompt_len), cos_t, sin_t)
+        rid = cfg.vocab + 1 + np.arange(cfg.n_registers)
+        q = table_values(wl.tq[rid]).reshape(cfg.n_registers, cfg.n_heads, d)
+        q = rope.rotate(q, cfg.seq_len + np.arange(cfg.n_registers), cos_t, sin_t)
+        for h in range(cfg.n_heads):
+            s = q[:, h] @ keys[:, h // g].T * (1.4426950408889634 / np.sqrt(d))
+            jump = max(jump, float(np.max(s[:, 64:128].max(axis=1) - s[:, :64].max(axis=1))))
+    assert jump > 32.0, jump
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    _check_generation(cfg, wl, SparseStepRunner(wl, device="cuda"))
 
 
 def test_forbidden_keys_nan_poison():
