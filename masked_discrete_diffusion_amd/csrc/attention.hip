@@ -395,7 +395,6 @@ __device__ inline floatx16 s_half(const uint16_t* kb, const bf16x8* qf, int hk, 
   for (int t = 0; t < NKS; ++t) {
     // at most four K operands in flight: the scheduler would otherwise hoist
     // all eight LDS reads (32 VGPRs) above the MFMA chain
-    if (t % 4 == 0 && t > 0) __builtin_amdgcn_sched_barrier(0);
     const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
     sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv, 0, 0, 0);
   }
@@ -515,10 +514,12 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
       for (int i = 1; i < n_comp; ++i) {
         ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
         const int cur = i % kStages;
+        // both halves' scores first: the second half's MFMAs run under the
+        // first half's softmax
         sv = s_half<D>(ks[cur], qf, 0, krow, half);
+        sv1 = s_half<D>(ks[cur], qf, 1, krow, half);
         finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc, over);
-        sv = s_half<D>(ks[cur], qf, 1, krow, half);
-        finish_half_fixed<D>(sv, vs[cur], 1, acc, m_ref, l_run, half, l32, sc, over);
+        finish_half_fixed<D>(sv1, vs[cur], 1, acc, m_ref, l_run, half, l32, sc, over);
       }
     }
   }
@@ -1009,7 +1010,13 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     if (a.n_c > kAttnMaxDecode) return hipErrorInvalidValue;
     const int G = g.H / g.Hkv;
     const int space = G * cp.n_chunks;                 // chunks per (sequence, kv head)
-    const int nb = (space + kAttnWaves - 1) / kAttnWaves;
+    // One wavefront per SIMD (chunk groups of four) when that still fits one
+    // block per compute unit: a block's tile time is set by its busiest SIMD,
+    // and row groups need no partial results or combine pass.  Otherwise up
+    // to eight chunks (two wavefronts per SIMD) share each streamed tile.
+    int nb = (space + kAttnWaves - 1) / kAttnWaves;
+    const int nb4 = (space + kAttnWaves / 2 - 1) / (kAttnWaves / 2);
+    if (g.B * g.Hkv * nb4 <= kAttnSplitBlocks) nb = nb4;
     cp.blocks = nb;
     cp.per_block = (space + nb - 1) / nb;
     const int groups = g.B * g.Hkv * nb;
