@@ -274,11 +274,12 @@ constexpr float kRescaleLog2 = 8.f;
 
 // Full tiles take a cheaper path: the reference is the row maximum over the
 // first full tile and is never raised in the loop, so no branch rescales (and
-// redefines) the accumulators there.  A wavefront only checks that no later
-// score passes the reference by more than kOverflowLog2 (p <= 2^16, far from
-// the fp32 range); if one does, the block recomputes everything on the lazy
-// path above.
-constexpr float kOverflowLog2 = 16.f;
+// redefines) the accumulators there, and no row maximum is taken.  After the
+// loop a wavefront checks that its row sums stayed below 2^kOverflowLog2
+// (then every p did: p <= 2^50 keeps O = sum p v far inside the fp32 range;
+// an infinite or NaN sum fails the check too); if one did not, the block
+// recomputes everything on the lazy path above.
+constexpr float kOverflowLog2 = 50.f;
 
 // max of three floats.  IEEE maximum (NaN-propagating) needs no canonicalising
 // moves in front of MFMA results and becomes one v_maximum3_f32; the compiler
@@ -422,15 +423,12 @@ __device__ inline void finish_half(floatx16& sv, const uint16_t* vb, int hk, int
   }
 }
 
-// Softmax and O += V P for half hk of a full tile at a fixed reference;
-// `over` records a score above the reference by more than kOverflowLog2.
+// Softmax and O += V P for half hk of a full tile at a fixed reference.
 template <int D>
 __device__ inline void finish_half_fixed(floatx16& sv, const uint16_t* vb, int hk, floatx16* acc, float m_ref,
-                                         float& l_run, int half, int l32, float sc, bool& over) {
+                                         float& l_run, int half, int l32, float sc) {
   using T = AttnTile<D>;
   const uint16_t* vhalf = vb + (l32 * T::VU + half + 4 * hk) * 8;
-  const float mt = half_max<false>(sv, 32 * hk, kKeyTile, half, sc);
-  over |= mt > m_ref + kOverflowLog2;
   half_exp(sv, m_ref, l_run, sc);
   half_pv<D, false>(sv, vhalf, acc, 32 * hk, kKeyTile, half);
 }
@@ -498,19 +496,19 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
     floatx16 sv = s_half<D>(ks[0], qf, 0, krow, half);
     floatx16 sv1 = s_half<D>(ks[0], qf, 1, krow, half);
     m_ref = fmaxf(half_max<false>(sv, 0, kKeyTile, half, sc), half_max<false>(sv1, 32, kKeyTile, half, sc));
-    finish_half_fixed<D>(sv, vs[0], 0, acc, m_ref, l_run, half, l32, sc, over);
+    finish_half_fixed<D>(sv, vs[0], 0, acc, m_ref, l_run, half, l32, sc);
     if (LAG) {
       for (int i = 1; i < n_comp; ++i) {
         ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
-        finish_half_fixed<D>(sv1, vs[(i - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc, over);
+        finish_half_fixed<D>(sv1, vs[(i - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc);
         const int cur = i % kStages;
         sv = s_half<D>(ks[cur], qf, 0, krow, half);
-        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc, over);
+        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc);
         sv1 = s_half<D>(ks[cur], qf, 1, krow, half);
       }
-      finish_half_fixed<D>(sv1, vs[(n_comp - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc, over);
+      finish_half_fixed<D>(sv1, vs[(n_comp - 1) % kStages], 1, acc, m_ref, l_run, half, l32, sc);
     } else {
-      finish_half_fixed<D>(sv1, vs[0], 1, acc, m_ref, l_run, half, l32, sc, over);
+      finish_half_fixed<D>(sv1, vs[0], 1, acc, m_ref, l_run, half, l32, sc);
       for (int i = 1; i < n_comp; ++i) {
         ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
         const int cur = i % kStages;
@@ -518,11 +516,14 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
         // first half's softmax
         sv = s_half<D>(ks[cur], qf, 0, krow, half);
         sv1 = s_half<D>(ks[cur], qf, 1, krow, half);
-        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc, over);
-        finish_half_fixed<D>(sv1, vs[cur], 1, acc, m_ref, l_run, half, l32, sc, over);
+        finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc);
+        finish_half_fixed<D>(sv1, vs[cur], 1, acc, m_ref, l_run, half, l32, sc);
       }
     }
   }
+  // every p of the fast phase is at most this lane's sum (a NaN fails too)
+  if (FAST && n_comp > 0) over = !(l_run < 0x1p50f);
+  static_assert(kOverflowLog2 == 50.f, "the bound above is 2^kOverflowLog2");
   if (!FAST && n_comp > 0) {
     if (LAG) {
       ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, 0, wave, lane);
