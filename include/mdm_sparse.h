@@ -44,7 +44,7 @@ typedef enum {
   MDM_OK = 0,
   MDM_E_ARG = -1,          /* null pointer, bad enum or out-of-range scalar           */
   MDM_E_SHAPE = -2,        /* sizes inconsistent with the config or the buffers      */
-  MDM_E_CAPACITY = -3,     /* the KV cache (or the transient tail) would overflow     */
+  MDM_E_CAPACITY = -3,     /* more rows than the sequence (seq_len) can hold          */
   MDM_E_HIP = -4,          /* a HIP runtime call failed (see mdm_last_error)          */
   MDM_E_UNSUPPORTED = -5,  /* a shape this build does not implement                   */
   MDM_E_DEVICE = -6        /* a kernel met an out-of-range token id or position       */
@@ -98,7 +98,9 @@ typedef struct {
  * to a multiple of 64.  Returns 0 for an invalid config. */
 size_t mdm_cache_slots(const mdm_config* cfg);
 
-/* Bytes of workspace the context needs (RoPE table, partial results).  0 if invalid. */
+/* Bytes of workspace the context needs (RoPE table, the key/query/value tables of
+ * the mask token and the registers, the appended rows' queries, packed h,
+ * partial results).  0 if invalid. */
 size_t mdm_workspace_bytes(const mdm_config* cfg);
 
 /* Bytes per element of tables, caches and the vocab head (2 or 4).  0 if invalid. */
@@ -108,9 +110,14 @@ size_t mdm_element_bytes(const mdm_config* cfg);
  * is prefetched into it by mdm_kv_append).  Validates cfg and the buffers,
  * builds the fp32 RoPE table (cos/sin of pos * base^(-2i/d) evaluated in double,
  * rounded to fp32) on the host and uploads it to the workspace, clears the
- * device error flag, and synchronises the stream once.  `stream` is a
- * hipStream_t (NULL = the default stream).  On success *ctx owns a host
- * allocation released by mdm_sparse_step_destroy. */
+ * device error flag, builds in the workspace the rows every step reuses (bf16:
+ * the RoPE'd keys and queries of the mask token at every position and of the
+ * registers, and their values in the layout the attention tiles read), and
+ * synchronises the stream once.  The tables tq/tk/tv are read here and by later
+ * calls, so they must hold their final contents before init and not change
+ * while the context lives.  `stream` is a hipStream_t (NULL = the default
+ * stream).  On success *ctx owns a host allocation released by
+ * mdm_sparse_step_destroy. */
 mdm_status mdm_sparse_step_init(mdm_ctx** ctx, const mdm_config* cfg, const mdm_buffers* buf,
                                 void* stream);
 
@@ -123,24 +130,30 @@ mdm_status mdm_set_stream(mdm_ctx* ctx, void* stream);
  * its key is Tk[id] rotated by RoPE at pos, its value Tv[id]; both are written
  * to slot len+r, with (pos, id) recorded in cache_pos / cache_tok.  The host
  * cache length becomes len + n.  stride 0 means n.  MDM_E_CAPACITY if
- * len + n > seq_len.  n == 0 is a no-op. */
+ * len + n > seq_len.  n == 0 is a no-op.  bf16 with n <= max_decode: the same
+ * launch also writes the n rows' RoPE'd queries (every query head) into the
+ * workspace, where the next mdm_step_attention takes them for its D rows. */
 mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, int64_t stride,
                          int32_t n);
 
 /* Step attention under the step-causal mask (page 1, worked example = Figure 3;
  * page 1, key design 3).  The query set of every sequence is, in this order:
  *   n_new_cached rows D (token d_tok, position d_pos) - the rows the preceding
- *     mdm_kv_append committed; they see the cache (which includes themselves);
+ *     mdm_kv_append committed, in the same order; they see the cache (which
+ *     includes themselves); when that append wrote their queries (see
+ *     mdm_kv_append) the kernel reads those, else it rotates them itself;
  *   n_decode rows C (the mask token at positions c_pos[b*c_stride + i]);
  *   R register rows (ids V+1.., positions seq_len..);
- * C and R rows see the cache plus all C and R rows.  Keys/values of the C and R
- * rows are gathered from the tables and rotated inside the kernel; they are
- * never written to the cache.  Queries are rotated at their own positions.
- * One kernel launch.  Output
+ * C and R rows see the cache plus all C and R rows.  Keys, values and queries
+ * of the C and R rows come from the rows built at init (the mask token's key
+ * depends only on its position); they are never written to the cache.  One
+ * attention kernel launch, plus a small merge launch when the key range of a
+ * (sequence, head) is split over several blocks.  Output
  * out[b][i][h*d + j] (fp32, [B][n_q][H*d], n_q = n_new_cached + n_decode + R) is
  * the attention output of row i, head h.  Strides of 0 mean compact.
  * MDM_E_CAPACITY if len + n_decode > seq_len; MDM_E_ARG if n_new_cached > len
- * or n_decode > max_decode. */
+ * or n_decode > max_decode (bf16 also requires max_decode <= 2048, checked at
+ * init). */
 mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t* d_pos,
                               int64_t d_stride, int32_t n_new_cached, const int32_t* c_pos,
                               int64_t c_stride, int32_t n_decode, float* out);
