@@ -242,6 +242,27 @@ __device__ inline void tile_dma(const AttnArgs& a, const Geometry& g, const KvSr
   }
 }
 
+// The same for a cache tile (the common case), without the per-load segment
+// branches: each of this wavefront's loads is a K or a V^T unit block,
+// chosen by a select on the block index.
+// (LDS addresses as plain integers: a select between two shared-memory
+// pointers would be redone with null checks for every load.)
+template <int D>
+__device__ inline void tile_dma_cache(const KvSrc& src, int base, int wave, const uint32_t (&off)[AttnTile<D>::LPW],
+                                      uint32_t ks_lds, uint32_t vs_lds) {
+  using T = AttnTile<D>;
+  if (wave >= T::LOADERS) return;
+  const uint16_t* kbase = src.kc + (int64_t)base * D;
+  const uint16_t* vbase = src.vc + (int64_t)base * D;
+#pragma unroll
+  for (int i = 0; i < T::LPW; ++i) {
+    const int blk = wave * T::LPW + i;
+    const bool is_k = blk < T::K_BLOCKS;
+    const uint32_t dst = is_k ? ks_lds + blk * 1024u : vs_lds + (blk - T::K_BLOCKS) * 1024u;
+    dma16_at(is_k ? kbase : vbase, off[i], dst);
+  }
+}
+
 // Wait for tile i of the ring when `younger` later tiles may stay in flight.
 // (kAhead tiles are loaded ahead; the lagging wavefronts still read the
 // previous tile's buffer, so a 4-deep ring leaves kAhead = 2.)
@@ -468,9 +489,13 @@ __device__ inline void ring_step(const AttnArgs& a, const Geometry& g, const KvS
   ring_wait_tiles<T::LPW>(ord.n - 1 - i);
   ring_barrier();
   const int nxt = i + kAhead;
-  if (nxt < ord.n)
-    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(nxt)), wave, lane, off, ks[nxt % kStages],
-                vs[nxt % kStages]);
+  if (nxt < ord.n) {
+    const TileRef tr = tile_ref(a, T0, T1, ord.at(nxt));
+    if (tr.seg == 0)
+      tile_dma_cache<D>(src, tr.base, wave, off, lds_addr(&ks[0][0]) + (nxt % kStages) * (T::K_ELEMS * 2),
+                        lds_addr(&vs[0][0]) + (nxt % kStages) * (T::V_ELEMS * 2));
+    else tile_dma<D>(a, g, src, tr, wave, lane, off, ks[nxt % kStages], vs[nxt % kStages]);
+  }
 }
 
 // The tile loop of one wavefront, in three phases over the block's ring steps:

@@ -139,12 +139,16 @@ __device__ inline void group_argmax(float& v, int& i) {
 // own vmcnt waits for its loads only become stricter (the counter retires in
 // issue order).  M0 holds the LDS base; nothing else in these kernels uses M0,
 // and one wait state separates its write from the load.
-__device__ inline void dma16(const void* base, uint32_t off, void* lds_block) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(void __attribute__((address_space(3)))*)lds_block);
+__device__ inline void dma16_at(const void* base, uint32_t off, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory");
 }
+// LDS byte address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)p;
+}
+__device__ inline void dma16(const void* base, uint32_t off, void* lds_block) { dma16_at(base, off, lds_addr(lds_block)); }
 
 // Wait until at most N of this wavefront's vector-memory operations are in
 // flight, and its LDS operations are done.  vmcnt retires in issue order, so
