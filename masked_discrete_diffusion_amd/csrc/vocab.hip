@@ -174,12 +174,12 @@ __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int
 
 template <class S>
 __device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const uint16_t* lb, int wave,
-                                  const uint32_t* off, const int* kind, uint16_t* stage) {
+                                  const uint32_t* off, const int* kind, uint32_t stage_lds) {
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
     const int blk = wave * S::LPW + i;
     const uint16_t* base = kind[i] == 1 ? hb : (kind[i] == 2 ? lb : wb);
-    dma16(base, off[i], stage + blk * kWave * 8);
+    dma16_at(base, off[i], stage_lds + blk * 1024u);
   }
 }
 
@@ -226,8 +226,10 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   uint32_t off[S::LPW];
   int kind[S::LPW];
   screen_offsets<S>(wave, lane, g.hidden, g.V, v0, off, kind);
+  const uint32_t ring_lds = lds_addr(&ring[0][0]);
   for (int c = 0; c < AHEAD && c < n_chunks; ++c)
-    screen_dma<S>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind, ring[c]);
+    screen_dma<S>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind,
+                  ring_lds + c * (S::ELEMS * 2));
   const int woff = ((32 * wv + l32) * S::U + half) * 8;
   const int hoff = ((32 * rb0 + l32) * S::U + half) * 8;
   for (int ci = 0; ci < n_chunks; ++ci) {
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
     const int nxt = ci + AHEAD;
     if (nxt < n_chunks)
       screen_dma<S>(wrow + nxt * kKChunk, hrow + nxt * kKChunk, lrow + nxt * kKChunk, wave, off, kind,
-                    ring[nxt % S::NST]);
+                    ring_lds + (nxt % S::NST) * (S::ELEMS * 2));
     const uint16_t* st = ring[ci % S::NST];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
