@@ -117,12 +117,13 @@ __global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
 // Hidden is consumed in 64-wide chunks ("stages") that flow from HBM straight
 // into LDS (LDS-DMA, issued from asm with explicit waits, see common.hpp)
 // through an NST-deep ring: NST-1 stages are in flight while one is
-// multiplied, one barrier per stage.  LDS rows are 8 data units (16 B) plus
-// one pad unit, which keeps the MFMA operand reads of 16 consecutive rows on
-// distinct banks with compile-time offsets.  A stage's DMA blocks (1 KiB each)
-// are padded to a multiple of the wavefront count so every wavefront issues
-// the same number of loads and the ring waits are constants; pad blocks
-// reload W row v0 into spare LDS.
+// multiplied, one barrier per stage.  The stream rate is set by the bytes in
+// flight, so the ring is as deep as LDS allows (the epilogue's reduction
+// buffer reuses it) and a stage has no padding: an LDS row is the 8 16-byte
+// units of 64 hidden elements, unit u of row r stored at u ^ ((r >> 1) & 7),
+// which spreads the MFMA operand reads of 16 consecutive rows over distinct
+// banks.  Every wavefront issues the same number of 1 KiB DMA blocks, so the
+// ring waits are constants.
 // With n_split > 1 the hidden dimension is split over blockIdx.z: every split
 // writes its partial logits and k_screen_reduce sums them in split order and
 // runs the epilogue (a separate launch: an in-kernel last-block reduction
@@ -133,41 +134,45 @@ struct ScreenStage {
   static constexpr int THREADS = NW * kWave;
   static constexpr int RBW = RB / NG;                              // row blocks per wavefront
   static_assert(RB % NG == 0, "row blocks must split evenly over the row groups");
-  static constexpr int U = kKChunk / 8 + 1;                        // units per padded row
-  static constexpr int W_BLOCKS = kVocabTile * U / kWave;          // 18
-  static constexpr int H_BLOCKS = (32 * RB * U + kWave - 1) / kWave;
-  static constexpr int REAL = W_BLOCKS + H_BLOCKS * (kLo ? 2 : 1);
-  static constexpr int LPW = (REAL + NW - 1) / NW;                 // loads per wavefront per stage
-  static constexpr int BLOCKS = LPW * NW;                          // incl. pad blocks
+  static constexpr int RU = kKChunk / 8;                           // 16-byte units per LDS row
+  static_assert(RU == 8, "the swizzle assumes 8 units per row");
+  static constexpr int W_BLOCKS = kVocabTile * RU / kWave;         // 16
+  static constexpr int H_BLOCKS = 32 * RB * RU / kWave;
+  static constexpr int BLOCKS = W_BLOCKS + H_BLOCKS * (kLo ? 2 : 1);
+  static constexpr int LPW = BLOCKS / NW;                          // loads per wavefront per stage
+  static_assert(BLOCKS % NW == 0, "DMA blocks must split evenly over the wavefronts");
   static constexpr int ELEMS = BLOCKS * kWave * 8;                 // bf16 elements per stage
   static constexpr int H_OFF = W_BLOCKS * kWave * 8;               // element offsets in a stage
   static constexpr int L_OFF = H_OFF + H_BLOCKS * kWave * 8;
-  static constexpr int FIT = 140 * 1024 / (ELEMS * 2);             // stages that fit beside the epilogue
-  static constexpr int NST = FIT >= 4 ? 4 : (FIT < 2 ? 2 : FIT);    // ring depth
+  static constexpr int FIT = 160 * 1024 / (ELEMS * 2);
+  static constexpr int NST = FIT >= 5 ? 5 : FIT;                   // ring depth
+  static_assert(NST >= 2, "a stage must fit twice");
+  static_assert(NST * ELEMS * 2 >= 4 * 32 * RB * (int)sizeof(float) * 6, "the reduction buffer reuses the ring");
 };
+
+// Physical unit of logical unit u in LDS row r.
+__device__ inline int swz(int r, int u) { return u ^ ((r >> 1) & 7); }
 
 // Per-lane byte offsets of this wavefront's DMA units, relative to the
 // stage's W base (W row v0) or h base (row m0), and the kind of each slot
-// (0 W, 1 h hi, 2 h lo, 3 pad).
+// (0 W, 1 h hi, 2 h lo).  Lane l of block blk fills physical unit q = 64 blk
+// + l (row q / 8, position q % 8) with the logical unit stored there.
 template <class S>
 __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int v0, uint32_t* off, int* kind) {
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
     const int blk = wave * S::LPW + i;
     if (blk < S::W_BLOCKS) {
-      const int u = blk * kWave + lane;
-      const int r = u / S::U, c = u % S::U;
-      off[i] = (uint32_t)((min(v0 + r, V - 1) - v0) * hidden + (c < S::U - 1 ? c : 0) * 8) * 2u;
+      const int q = blk * kWave + lane;
+      const int r = q / S::RU, u = swz(r, q % S::RU);
+      off[i] = (uint32_t)((min(v0 + r, V - 1) - v0) * hidden + u * 8) * 2u;
       kind[i] = 0;
-    } else if (blk < S::REAL) {
-      const int hb = (blk - S::W_BLOCKS) % S::H_BLOCKS;
-      const int u = hb * kWave + lane;
-      const int r = min(u / S::U, 32 * S::RBW * (S::NW / 4) - 1), c = u % S::U;
-      off[i] = (uint32_t)(r * hidden + (c < S::U - 1 ? c : 0) * 8) * 2u;
-      kind[i] = blk - S::W_BLOCKS >= S::H_BLOCKS ? 2 : 1;
     } else {
-      off[i] = (uint32_t)(lane % (S::U - 1)) * 16u;
-      kind[i] = 3;
+      const int hb = (blk - S::W_BLOCKS) % S::H_BLOCKS;
+      const int q = hb * kWave + lane;
+      const int r = q / S::RU, u = swz(r, q % S::RU);
+      off[i] = (uint32_t)(r * hidden + u * 8) * 2u;
+      kind[i] = blk - S::W_BLOCKS >= S::H_BLOCKS ? 2 : 1;
     }
   }
 }
@@ -185,8 +190,9 @@ __device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const 
 
 template <int LPW, int AHEAD>
 __device__ inline void screen_wait(int younger) {
-  static_assert(AHEAD <= 3, "waits are spelled out for up to three stages ahead");
-  if (younger >= 2 && AHEAD >= 3) ring_wait<2 * LPW>();
+  static_assert(AHEAD <= 4, "waits are spelled out for up to four stages ahead");
+  if (younger >= 3 && AHEAD >= 4) ring_wait<3 * LPW>();
+  else if (younger >= 2 && AHEAD >= 3) ring_wait<2 * LPW>();
   else if (younger >= 1 && AHEAD >= 2) ring_wait<LPW>();
   else ring_wait<0>();
 }
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   constexpr int RBW = S::RBW;
   constexpr int AHEAD = S::NST - 1;
   __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
-  __shared__ Top2 red[4][MT];
+  Top2 (*red)[MT] = reinterpret_cast<Top2 (*)[MT]>(&ring[0][0]);   // after the stages are consumed
 
   const int vt = blockIdx.x;
   const int mt = blockIdx.y;
@@ -230,8 +236,14 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   for (int c = 0; c < AHEAD && c < n_chunks; ++c)
     screen_dma<S>(wrow + c * kKChunk, hrow + c * kKChunk, lrow + c * kKChunk, wave, off, kind,
                   ring_lds + c * (S::ELEMS * 2));
-  const int woff = ((32 * wv + l32) * S::U + half) * 8;
-  const int hoff = ((32 * rb0 + l32) * S::U + half) * 8;
+  // element offsets of this lane's operand rows and units for k-step t:
+  // rows 32 wv + l32 (W) and 32 rb0 + l32 (h), logical unit 2t + half
+  int woff[kKChunk / 16], hoff[kKChunk / 16];
+#pragma unroll
+  for (int t = 0; t < kKChunk / 16; ++t) {
+    woff[t] = ((32 * wv + l32) * S::RU + swz(l32, 2 * t + half)) * 8;
+    hoff[t] = ((32 * rb0 + l32) * S::RU + swz(l32, 2 * t + half)) * 8;
+  }
   for (int ci = 0; ci < n_chunks; ++ci) {
     screen_wait<S::LPW, AHEAD>(n_chunks - 1 - ci);
     ring_barrier();
@@ -242,13 +254,13 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
     const uint16_t* st = ring[ci % S::NST];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + woff + 16 * t);
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + woff[t]);
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
-        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff + rb * 32 * S::U * 8 + 16 * t);
+        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff[t] + rb * 32 * S::RU * 8);
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
         if (kLo) {
-          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff + rb * 32 * S::U * 8 + 16 * t);
+          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff[t] + rb * 32 * S::RU * 8);
           acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lf, acc[rb], 0, 0, 0);
         }
       }
@@ -273,6 +285,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
     return;                                   // k_screen_reduce folds the splits
   }
 
+  __syncthreads();                            // every wavefront is done with the ring
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     float vals[16];
