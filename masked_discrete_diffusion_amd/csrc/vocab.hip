@@ -314,6 +314,179 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   }
 }
 
+// ------------------------------------------- screen, wide vocabulary tiles --
+// For large vocabularies the h rows are the bigger stream (a 128 x 128 block
+// moves the W tile once and its h tile, hi and lo, once per vocab tile), so a
+// block takes 512 vocab columns: 8 wavefronts = 4 vocab groups (one 128-column
+// partial tile each, 4 MFMA blocks wide) x 2 row groups.  Hidden goes in
+// 32-wide stages (LDS rows of 4 16-byte units, unit u of row r stored at
+// u ^ ((r >> 2) & 3): conflict-free operand reads), 3-4 stages deep.  Each
+// wavefront holds complete 128-column tiles of its rows, so the epilogue's
+// per-tile partials need no cross-wavefront reduction.
+constexpr int kWideTile = 512;
+constexpr int kWideK = 32;
+
+template <int RB, bool kLo>
+struct WideStage {
+  static constexpr int NW = 8;
+  static constexpr int RBW = RB / 2;                              // row blocks per wavefront
+  static constexpr int RU = kWideK / 8;                           // units per LDS row
+  static constexpr int W_BLOCKS = kWideTile * RU / kWave;         // 32
+  static constexpr int H_BLOCKS = 32 * RB * RU / kWave;
+  static constexpr int BLOCKS = W_BLOCKS + H_BLOCKS * (kLo ? 2 : 1);
+  static constexpr int LPW = BLOCKS / NW;
+  static_assert(BLOCKS % NW == 0, "DMA blocks must split evenly over the wavefronts");
+  static constexpr int ELEMS = BLOCKS * kWave * 8;
+  static constexpr int H_OFF = W_BLOCKS * kWave * 8;
+  static constexpr int L_OFF = H_OFF + H_BLOCKS * kWave * 8;
+  static constexpr int NST = 160 * 1024 / (ELEMS * 2) >= 4 ? 4 : 160 * 1024 / (ELEMS * 2);
+  static_assert(NST >= 3, "the ring must hold three stages");
+};
+
+__device__ inline int swz4(int r, int u) { return u ^ ((r >> 2) & 3); }
+
+template <int RB, bool kLo>
+__global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, int M, int n_split) {
+  using S = WideStage<RB, kLo>;
+  constexpr int RBW = S::RBW;
+  constexpr int AHEAD = S::NST - 1;
+  __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
+
+  const int vw = blockIdx.x;                     // 512-column tile
+  const int mt = blockIdx.y;
+  const int split = blockIdx.z;
+  const int v0 = vw * kWideTile;
+  const int m0 = mt * 32 * RB;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int vg = wave % 4;                       // 128-column partial tile of this wavefront
+  const int rb0 = (wave / 4) * RBW;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32, l32 = lane % 32;
+  const int k_len = g.hidden / n_split;
+  const int k_beg = split * k_len;
+  const int n_chunks = k_len / kWideK;
+  const uint16_t* wrow = static_cast<const uint16_t*>(a.w) + (int64_t)v0 * g.hidden + k_beg;
+  const uint16_t* hrow = a.hhi + (int64_t)m0 * g.hidden + k_beg;
+  const uint16_t* lrow = kLo ? a.hlo + (int64_t)m0 * g.hidden + k_beg : hrow;
+
+  floatx16 acc[4][RBW];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[vb][rb][e] = 0.f;
+
+  // DMA units: lane l of block blk fills physical unit q = 64 blk + l
+  uint32_t off[S::LPW];
+  int kind[S::LPW];
+#pragma unroll
+  for (int i = 0; i < S::LPW; ++i) {
+    const int blk = wave * S::LPW + i;
+    if (blk < S::W_BLOCKS) {
+      const int q = blk * kWave + lane;
+      const int r = q / S::RU, u = swz4(r, q % S::RU);
+      off[i] = (uint32_t)((min(v0 + r, g.V - 1) - v0) * g.hidden + u * 8) * 2u;
+      kind[i] = 0;
+    } else {
+      const int hb = (blk - S::W_BLOCKS) % S::H_BLOCKS;
+      const int q = hb * kWave + lane;
+      const int r = q / S::RU, u = swz4(r, q % S::RU);
+      off[i] = (uint32_t)(r * g.hidden + u * 8) * 2u;
+      kind[i] = blk - S::W_BLOCKS >= S::H_BLOCKS ? 2 : 1;
+    }
+  }
+  const uint32_t ring_lds = lds_addr(&ring[0][0]);
+  auto issue = [&](int c, uint32_t stage) {
+#pragma unroll
+    for (int i = 0; i < S::LPW; ++i) {
+      const int blk = wave * S::LPW + i;
+      const uint16_t* base = kind[i] == 1 ? hrow : (kind[i] == 2 ? lrow : wrow);
+      dma16_at(base + c * kWideK, off[i], stage + blk * 1024u);
+    }
+  };
+  for (int c = 0; c < AHEAD && c < n_chunks; ++c) issue(c, ring_lds + c * (S::ELEMS * 2));
+  // operand element offsets for k-step t (2 per stage): logical unit 2t + half
+  int woff[2], hoff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    woff[t] = ((128 * vg + l32) * S::RU + swz4(l32, 2 * t + half)) * 8;
+    hoff[t] = ((32 * rb0 + l32) * S::RU + swz4(l32, 2 * t + half)) * 8;
+  }
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    screen_wait<S::LPW, AHEAD>(n_chunks - 1 - ci);
+    ring_barrier();
+    const int nxt = ci + AHEAD;
+    if (nxt < n_chunks) issue(nxt, ring_lds + (nxt % S::NST) * (S::ELEMS * 2));
+    const uint16_t* st = ring[ci % S::NST];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 wf[4];
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) wf[vb] = *reinterpret_cast<const bf16x8*>(st + woff[t] + vb * 32 * S::RU * 8);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff[t] + rb * 32 * S::RU * 8);
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+          acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[vb], hf, acc[vb][rb], 0, 0, 0);
+        if (kLo) {
+          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff[t] + rb * 32 * S::RU * 8);
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb)
+            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[vb], lf, acc[vb][rb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // lane holds z for row m0 + 32(rb0 + rb) + l32 and vocab v0 + 128 vg + 32 vb + 8jj + 4half + ii
+  const int vt = vw * (kWideTile / kVocabTile) + vg;      // 128-column tile index
+  if (n_split > 1) {
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        const int r = m0 + 32 * (rb0 + rb) + l32;
+        if (r < M) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int v = v0 + 128 * vg + 32 * vb + 8 * jj + 4 * half;
+            if (v < a.v_pad) {
+              floatx4 q = {acc[vb][rb][4 * jj], acc[vb][rb][4 * jj + 1], acc[vb][rb][4 * jj + 2],
+                           acc[vb][rb][4 * jj + 3]};
+              *reinterpret_cast<floatx4*>(a.zpart + ((int64_t)split * M + r) * a.v_pad + v) = q;
+            }
+          }
+        }
+      }
+    return;
+  }
+  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = m0 + 32 * (rb0 + rb) + l32;
+    Top2 tt;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+      float vals[16];
+      int idx[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int jj = e / 4, ii = e % 4;
+        const int v = v0 + 128 * vg + 32 * vb + 8 * jj + 4 * half + ii;
+        idx[e] = v;
+        vals[e] = v < g.V ? acc[vb][rb][e] : kNegInf;
+        if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[vb][rb][e];
+      }
+      const Top2 t = summarize<16>(vals, idx);
+      tt = vb == 0 ? t : top2_merge(tt, t);
+    }
+    tt = top2_merge(tt, top2_shfl_xor(tt, 32));
+    if (half == 0 && vt < n_vt && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, tt);
+  }
+}
+
 // Fold the hidden-split partial logits of one 128-vocab tile for 32 rows:
 // thread t: row t/8, vocab columns 16(t%8) .. +16; splits summed in order.
 __global__ __launch_bounds__(256) void k_screen_reduce(Geometry g, VocabArgs a, int M, int n_split) {
@@ -642,9 +815,29 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   const int mt_rows = 32 * rb;
   const int m_tiles = (M + mt_rows - 1) / mt_rows;
+  const int n_wide = (g.V + kWideTile - 1) / kWideTile;
+  // wide vocabulary tiles when they alone give (nearly) a block per compute unit
+  const bool wide = (rb == 4 || (rb == 2 && a.hlo)) && n_wide * m_tiles >= kScreenTargetBlocks * 7 / 8;
   VocabArgs pa = a;
   pa.m_pad = ((M + 63) / 64) * 64;
   if (m_tiles * mt_rows > pa.m_pad) pa.m_pad = m_tiles * mt_rows;
+  if (wide) {
+    const int64_t n8w = (int64_t)pa.m_pad * g.hidden / 8;
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8w + 255) / 256)), dim3(256), 0, s, g, pa, M);
+    hipError_t ew = hipGetLastError();
+    if (ew != hipSuccess) return ew;
+    dim3 wgrid(n_wide, m_tiles, 1);
+    if (rb == 4) {
+      if (a.hlo) hipLaunchKernelGGL((k_screen_wide<4, true>), wgrid, dim3(512), 0, s, g, pa, M, 1);
+      else hipLaunchKernelGGL((k_screen_wide<4, false>), wgrid, dim3(512), 0, s, g, pa, M, 1);
+    } else {
+      hipLaunchKernelGGL((k_screen_wide<2, true>), wgrid, dim3(512), 0, s, g, pa, M, 1);
+    }
+    ew = hipGetLastError();
+    if (ew != hipSuccess) return ew;
+    hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
+    return hipGetLastError();
+  }
   int n_split = 1;
   const int chunks = g.hidden / kKChunk;
   while (n_split < 8 && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks && chunks % (n_split * 2) == 0 &&

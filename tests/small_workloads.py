@@ -58,3 +58,22 @@ def gpu_small_semi_ar(index=112, **kw):
 
 def gpu_small_fp32(index=113, **kw):
     return gpu_small_d128(index=index, name="gpu_small_fp32", precision="fp32", **kw)
+
+
+# Vocabularies large enough for the 512-column screen tiles (at least 224
+# of them): semi-autoregressive (hi/lo screening, 64- and 128-row tiles) and a
+# fixed schedule (hi only, 128-row tiles).  hidden 256 keeps the oracle fast.
+def gpu_wide_semi_ar(index=115, **kw):
+    base = dict(name="gpu_wide_semi_ar", index=index, batch=8, n_heads=2, n_kv_heads=1, head_dim=128,
+                vocab=120000, prompt_len=24, gen_len=32, n_registers=4, n_steps=8,
+                schedule="semi_ar", block=16, steps_per_block=4, order="confidence", precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+def gpu_wide_fixed(index=116, **kw):
+    base = dict(name="gpu_wide_fixed", index=index, batch=8, n_heads=2, n_kv_heads=2, head_dim=128,
+                vocab=115000, prompt_len=30, gen_len=32, n_registers=4, n_steps=2,
+                schedule="fixed", per_step=16, order="random", precision="bf16")
+    base.update(kw)
+    return Config(**base)

@@ -16,7 +16,8 @@ import pytest
 from mdm_inputs import make_workload
 from oracle.numerics import table_values
 from oracle.step import Model, SequenceOracle, run_workload
-from small_workloads import gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar
+from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_wide_fixed,
+                             gpu_wide_semi_ar)
 from mdm_inputs import get_config
 
 pytestmark = pytest.mark.gpu
@@ -112,6 +113,17 @@ def _check_generation(cfg, wl, run):
             g["logits"].reshape(-1, cfg.vocab), zref, rtol, atol, f"logits step {k}"))
     assert np.array_equal(seq, res.tokens), "final sequences differ"
     _say(f"  worst abs errors: {worst}")
+
+
+@pytest.mark.parametrize("cfgfn", [gpu_wide_semi_ar, gpu_wide_fixed], ids=["wide_semi_ar", "wide_fixed"])
+def test_wide_vocab_tiles_match_oracle(cfgfn):
+    """Vocabularies of 115k-120k take the 512-column screen tiles (with and
+    without the hi/lo split of h, 64- and 128-row tiles); the generation must
+    match the oracle like the small workloads."""
+    cfg = cfgfn()
+    _say(f"wide vocab parity: {cfg.name}")
+    wl, run = _runner(cfg)
+    _check_generation(cfg, wl, run)
 
 
 def test_score_jump_falls_back_to_rescaled_path():
