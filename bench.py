@@ -176,9 +176,15 @@ def cpu_baseline(cfg, budget_s):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"sequence 0 of {cfg.name}: prompt prefetch + sampling steps 1..{steps} of "
-                      f"{cfg.n_steps} ({tokens} tokens) in {dt:.1f} s, float64 NumPy"}
+                      f"{cfg.n_steps} ({tokens} tokens) in {dt:.1f} s, float64 NumPy on {cpu}"}
 
 
 def main():
