@@ -159,7 +159,7 @@ def cpu_baseline(cfg, budget_s):
     wl = make_workload(cfg)
     model = Model.from_workload(wl)
     t0 = time.perf_counter()
-    seq = SequenceOracle(model, wl.prompt_ids[0])
+    seq = SequenceOracle(model, wl.prompt_ids[0], wl.prompt_pos[0])
     seq.prefill()
     d = (np.empty(0, np.int64), np.empty(0, np.int64))
     tokens = 0

@@ -112,13 +112,13 @@ class SparseStepRunner:
         self.stream = torch.cuda.current_stream(dev)
         self.ctx = L.mdm_sparse_step_init(self.mc, self.bufs, self.stream.cuda_stream)
 
-        B, P, Lg = cfg.batch, cfg.prompt_len, cfg.gen_len
+        B = cfg.batch
         i32 = dict(dtype=torch.int32, device=dev)
         self.prompt_tok = torch.from_numpy(wl.prompt_ids.astype(np.int32)).to(dev)
-        self.prompt_pos = torch.arange(P, **i32).repeat(B, 1).contiguous()
+        self.prompt_pos = torch.from_numpy(np.ascontiguousarray(wl.prompt_pos, dtype=np.int32)).to(dev)
         self.order = (torch.from_numpy(wl.order.astype(np.int32)).to(dev) if wl.order is not None
                       else torch.zeros(B, 1, **i32))
-        self.block_pos = (P + torch.arange(Lg, **i32)).repeat(B, 1).contiguous()
+        self.block_pos = torch.from_numpy(np.ascontiguousarray(wl.gen_pos, dtype=np.int32)).to(dev)
         self.d_tok = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
         self.d_pos = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
         self.rem = [torch.zeros(B * max_decode, **i32) for _ in range(2)]
@@ -127,7 +127,7 @@ class SparseStepRunner:
         self.conf = torch.zeros(B * max_decode, dtype=torch.float32, device=dev)
         self.token = torch.zeros(B * max_decode, **i32)
         seq0 = np.full((B, cfg.seq_len), cfg.vocab, dtype=np.int32)
-        seq0[:, :P] = wl.prompt_ids
+        np.put_along_axis(seq0, wl.prompt_pos.astype(np.int64), wl.prompt_ids, axis=1)
         self.seq0 = torch.from_numpy(seq0).to(dev)
         self.seq_tokens = self.seq0.clone()
 

@@ -34,6 +34,10 @@ class Config:
     per_step: int = 0          # fixed schedule: tokens per step
     block: int = 0             # semi-AR block size
     steps_per_block: int = 0   # semi-AR sub-steps per block
+    block_order: str = "ltr"   # semi-AR: "ltr" (left to right) | "random" (seeded block order)
+    infill_spans: int = 0      # > 0: the generated positions are this many masked spans
+                               # placed inside the sequence (text infilling), the clean
+                               # prompt tokens fill the other positions
     rope_theta: float = 10000.0
     description: str = ""
 

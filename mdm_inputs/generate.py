@@ -107,6 +107,15 @@ class Workload:
     order: Optional[np.ndarray]      # int32 [B][L] absolute positions, or None
     counts: np.ndarray               # int32 [n_steps]: decode counts (C) per step
     semi_ar: list = field(default_factory=list)   # [SemiARStep] for semi-AR text
+    prompt_pos: Optional[np.ndarray] = None       # int32 [B][P] positions of the prompt tokens
+    gen_pos: Optional[np.ndarray] = None          # int32 [B][L] masked positions, ascending
+
+    def __post_init__(self):
+        cfg = self.cfg
+        if self.prompt_pos is None:
+            self.prompt_pos = np.tile(np.arange(cfg.prompt_len, dtype=np.int32), (cfg.batch, 1))
+        if self.gen_pos is None:
+            self.gen_pos = np.tile(np.arange(cfg.prompt_len, cfg.seq_len, dtype=np.int32), (cfg.batch, 1))
 
     @property
     def is_bf16(self) -> bool:
@@ -115,8 +124,32 @@ class Workload:
 
 def _seed_streams(cfg: Config):
     ss = np.random.SeedSequence([SEED_ROOT, cfg.index])
-    kids = ss.spawn(7)
+    kids = ss.spawn(8)      # the 8th stream (text variants) leaves the first 7 unchanged
     return [np.random.default_rng(k) for k in kids]
+
+
+def infill_positions(seq_len: int, gen_len: int, n_spans: int, rng: np.random.Generator):
+    """(clean, masked) positions: `gen_len` masked positions in `n_spans`
+    non-empty spans placed at random inside [0, seq_len), with at least one
+    clean position before every span."""
+    n_clean = seq_len - gen_len
+    if n_spans < 1 or n_spans > gen_len or n_spans > n_clean:
+        raise ValueError("infill spans do not fit")
+    cuts = np.sort(rng.choice(np.arange(1, gen_len), n_spans - 1, replace=False)) if n_spans > 1 else []
+    lengths = np.diff(np.concatenate([[0], cuts, [gen_len]])).astype(np.int64)
+    # clean tokens before each span (>= 1) and after the last one (>= 0)
+    gaps = np.ones(n_spans + 1, dtype=np.int64)
+    gaps[-1] = 0
+    extra = n_clean - int(gaps.sum())
+    gaps += np.bincount(rng.integers(0, n_spans + 1, size=extra), minlength=n_spans + 1)
+    masked = np.zeros(seq_len, dtype=bool)
+    at = 0
+    for j in range(n_spans):
+        at += int(gaps[j])
+        masked[at:at + int(lengths[j])] = True
+        at += int(lengths[j])
+    pos = np.arange(seq_len, dtype=np.int32)
+    return pos[~masked], pos[masked]
 
 
 def _normal_bf16(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
@@ -140,14 +173,16 @@ def _counts(cfg: Config) -> np.ndarray:
     raise ValueError(cfg.schedule)
 
 
-def semi_ar_plan(cfg: Config) -> list:
-    """Blocks left to right; each block is unmasked over `steps_per_block`
-    sub-steps of block/steps_per_block tokens each."""
+def semi_ar_plan(cfg: Config, block_seq=None) -> list:
+    """Blocks left to right (or in `block_seq` order); each block is unmasked
+    over `steps_per_block` sub-steps of block/steps_per_block tokens each.
+    Block j holds the generated positions [j*block, (j+1)*block) in position
+    order."""
     if cfg.gen_len % cfg.block or cfg.block % cfg.steps_per_block:
         raise ValueError("block sizes do not divide")
     per = cfg.block // cfg.steps_per_block
     plan = []
-    for b in range(cfg.gen_len // cfg.block):
+    for b in (range(cfg.gen_len // cfg.block) if block_seq is None else block_seq):
         for s in range(cfg.steps_per_block):
             plan.append(SemiARStep(block=b, sub=s, n_cand=cfg.block - s * per, n_select=per))
     if len(plan) != cfg.n_steps:
@@ -162,7 +197,7 @@ def make_workload(cfg: Config, tables: bool = True) -> Workload:
     ids, counts and orders are still drawn from their own streams, so they do
     not depend on this flag.
     """
-    r_tq, r_tk, r_tv, r_w, r_prompt, r_order, r_emb = _seed_streams(cfg)
+    r_tq, r_tk, r_tv, r_w, r_prompt, r_order, r_emb, r_text = _seed_streams(cfg)
     rows, hd, kvd = cfg.table_rows, cfg.hidden, cfg.n_kv_heads * cfg.head_dim
     if not tables:
         dt = np.uint16 if cfg.precision == "bf16" else np.float32
@@ -200,6 +235,20 @@ def make_workload(cfg: Config, tables: bool = True) -> Workload:
     if order is not None:
         order = (order + cfg.prompt_len).astype(np.int32)
 
-    plan = semi_ar_plan(cfg) if cfg.schedule == "semi_ar" else []
+    block_seq = None
+    if cfg.block_order == "random":
+        if cfg.schedule != "semi_ar":
+            raise ValueError("a block order needs the semi-AR schedule")
+        block_seq = r_text.permutation(cfg.gen_len // cfg.block).tolist()
+    elif cfg.block_order != "ltr":
+        raise ValueError(cfg.block_order)
+    prompt_pos = gen_pos = None
+    if cfg.infill_spans:
+        if order is not None:
+            raise ValueError("infilling is defined for the semi-AR schedule")
+        pairs = [infill_positions(cfg.seq_len, cfg.gen_len, cfg.infill_spans, r_text) for _ in range(cfg.batch)]
+        prompt_pos = np.stack([c for c, _ in pairs]).astype(np.int32)
+        gen_pos = np.stack([m for _, m in pairs]).astype(np.int32)
+    plan = semi_ar_plan(cfg, block_seq) if cfg.schedule == "semi_ar" else []
     return Workload(cfg=cfg, tq=tq, tk=tk, tv=tv, w_vocab=w, prompt_ids=prompt,
-                    order=order, counts=_counts(cfg), semi_ar=plan)
+                    order=order, counts=_counts(cfg), semi_ar=plan, prompt_pos=prompt_pos, gen_pos=gen_pos)

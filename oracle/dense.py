@@ -21,19 +21,20 @@ from .masks import block_mask
 from .step import Model
 
 
-def build_rows(model: Model, prompt_ids, clean_groups, masked_groups):
+def build_rows(model: Model, prompt_ids, clean_groups, masked_groups, prompt_pos=None):
     """Rows of the dense training-form sequence.
 
     clean_groups:  [(tokens, positions)] for blocks 1..M (decode history)
     masked_groups: [positions] for blocks M+1..M+N; each block is followed by
                    its own copy of the R registers.
     Returns ids, positions, block ids and, per masked block, the row indices
-    of its masked tokens and of its registers.
+    of its masked tokens and of its registers.  The prompt sits at positions
+    0 .. P-1 unless `prompt_pos` gives them (text infilling).
     """
     ids, pos, blk = [], [], []
     p = len(prompt_ids)
     ids += list(prompt_ids)
-    pos += list(range(p))
+    pos += list(range(p)) if prompt_pos is None else [int(x) for x in prompt_pos]
     blk += [0] * p
     for j, (tok, ps) in enumerate(clean_groups, start=1):
         ids += list(tok)

@@ -19,7 +19,12 @@ Readings (where the pages are silent):
 * registers are re-fed at every step and never cached;
 * the prompt is in the cache before step 1 and nothing enters at step 1;
   the last step's tokens are not appended;
-* the cache keeps tokens in the order they enter it (append order).
+* the cache keeps tokens in the order they enter it (append order);
+* text infilling: the clean tokens may sit anywhere in the sequence (their
+  positions are given), the masked positions are the rest; semi-AR block j
+  holds the j-th `block` masked positions in position order, and blocks may
+  be decoded in any order (page 3, section 3.2: the network sees only the
+  clean tokens and the positions it decodes, so neither changes the step).
 """
 
 from __future__ import annotations
@@ -112,7 +117,7 @@ class StepOut:
 class SequenceOracle:
     """One sequence: its dense form X, its KV cache (append order) per layer."""
 
-    def __init__(self, model: Model, prompt_ids: np.ndarray):
+    def __init__(self, model: Model, prompt_ids: np.ndarray, prompt_pos=None):
         self.m = model
         self.layers = 1 if model.layer2 is None else 2
         cap = model.seq_len + model.n_registers
@@ -124,7 +129,9 @@ class SequenceOracle:
         self.cache_pos: list = []
         self.x = np.full(model.seq_len, model.mask_id, dtype=np.int64)
         p = len(prompt_ids)
-        self.x[:p] = prompt_ids
+        self.prompt_pos = (np.arange(p, dtype=np.int64) if prompt_pos is None
+                           else np.asarray(prompt_pos, dtype=np.int64))
+        self.x[self.prompt_pos] = prompt_ids
         self.prompt_ids = np.asarray(prompt_ids, dtype=np.int64)
 
     # -- the cache -----------------------------------------------------------
@@ -134,9 +141,8 @@ class SequenceOracle:
         self.v[layer][self.n:self.n + n] = v
 
     def prefill(self):
-        """Prefetch the prompt into the cache (positions 0 .. P-1)."""
-        p = len(self.prompt_ids)
-        self.forward(self.prompt_ids, np.arange(p), np.empty(0, np.int64), prefill=True)
+        """Prefetch the prompt (the clean tokens) into the cache."""
+        self.forward(self.prompt_ids, self.prompt_pos, np.empty(0, np.int64), prefill=True)
 
     # -- one forward over the query set [D | C | R] -----------------------------
     def forward(self, d_tok, d_pos, c_pos, prefill: bool = False) -> StepOut:
@@ -210,8 +216,8 @@ def step_candidates(wl, k, b, remaining):
     if cfg.schedule == "semi_ar":
         st = wl.semi_ar[k]
         if st.sub == 0:
-            start = cfg.prompt_len + st.block * cfg.block
-            return np.arange(start, start + cfg.block, dtype=np.int64)
+            start = st.block * cfg.block
+            return wl.gen_pos[b, start:start + cfg.block].astype(np.int64)
         return remaining[b]
     c0 = int(np.sum(wl.counts[:k]))
     return wl.order[b, c0:c0 + int(wl.counts[k])].astype(np.int64)
@@ -224,7 +230,7 @@ def run_workload(wl, batches=None, n_steps: Optional[int] = None, keep_steps=(),
     batches = list(range(cfg.batch)) if batches is None else list(batches)
     model = model or Model.from_workload(wl, precision=precision)
     n_steps = cfg.n_steps if n_steps is None else n_steps
-    seqs = [SequenceOracle(model, wl.prompt_ids[b]) for b in batches]
+    seqs = [SequenceOracle(model, wl.prompt_ids[b], wl.prompt_pos[b]) for b in batches]
     for s in seqs:
         s.prefill()
     d_state = [(np.empty(0, np.int64), np.empty(0, np.int64)) for _ in batches]

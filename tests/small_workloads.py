@@ -21,6 +21,14 @@ def tiny_semi_ar(index=101, **kw):
     return Config(**base)
 
 
+def tiny_infill(index=102, **kw):
+    """Semi-AR text infilling: three masked spans inside the sequence, blocks in
+    a seeded random order."""
+    base = dict(name="tiny_infill", infill_spans=3, block_order="random", block=4, steps_per_block=2)
+    base.update(kw)
+    return tiny_semi_ar(index=index, **base)
+
+
 def reduced(name, **kw):
     """A named workload with fewer steps/positions (same head shapes)."""
     return get_config(name).replace(**kw)
@@ -77,3 +85,11 @@ def gpu_wide_fixed(index=116, **kw):
                 schedule="fixed", per_step=16, order="random", precision="bf16")
     base.update(kw)
     return Config(**base)
+
+
+# Text variants on the HIP path: infilling (four masked spans inside the
+# sequence) with semi-AR blocks decoded in a seeded random order.
+def gpu_text_infill(index=117, **kw):
+    base = dict(name="gpu_text_infill", infill_spans=4, block_order="random")
+    base.update(kw)
+    return gpu_small_semi_ar(index=index, **base)

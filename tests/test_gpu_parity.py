@@ -16,8 +16,8 @@ import pytest
 from mdm_inputs import make_workload
 from oracle.numerics import table_values
 from oracle.step import Model, SequenceOracle, run_workload
-from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_wide_fixed,
-                             gpu_wide_semi_ar)
+from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_text_infill,
+                             gpu_wide_fixed, gpu_wide_semi_ar)
 from mdm_inputs import get_config
 
 pytestmark = pytest.mark.gpu
@@ -122,6 +122,18 @@ def test_wide_vocab_tiles_match_oracle(cfgfn):
     match the oracle like the small workloads."""
     cfg = cfgfn()
     _say(f"wide vocab parity: {cfg.name}")
+    wl, run = _runner(cfg)
+    _check_generation(cfg, wl, run)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(precision="fp32")], ids=["bf16", "fp32"])
+def test_text_infill_random_block_order_matches_oracle(kw):
+    """Text variants: the clean tokens sit between four masked spans (their
+    keys enter the cache at scattered positions) and the semi-AR blocks are
+    decoded in a seeded random order.  Only the positions handed to the calls
+    change; decisions, unmask order and outputs must match the oracle."""
+    cfg = gpu_text_infill(**kw)
+    _say(f"text infill parity: {cfg.name} {cfg.precision}")
     wl, run = _runner(cfg)
     _check_generation(cfg, wl, run)
 

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from mdm_inputs import CONFIGS, cosine_counts, get_config, make_workload, stratified_order_2d
-from mdm_inputs.generate import semi_ar_plan
+from mdm_inputs.generate import infill_positions, semi_ar_plan
 
 
 @pytest.mark.parametrize("L", [1024, 4096])
@@ -68,3 +68,30 @@ def test_config_table():
     assert [c.name for c in CONFIGS] == ["c1_tiny", "c2_t2i_1k", "c3_t2i_4k", "c4_edit", "c5_text_semi_ar"]
     c5 = get_config(4)
     assert c5.group == 4 and c5.hidden == 4096 and c5.table_rows == 128000 + 1 + 64
+
+
+@pytest.mark.parametrize("seq_len,gen_len,spans", [(21, 16, 3), (40, 16, 1), (12, 6, 6), (200, 150, 17)])
+def test_infill_positions_partition(seq_len, gen_len, spans):
+    rng = np.random.default_rng(seq_len * 7 + spans)
+    clean, masked = infill_positions(seq_len, gen_len, spans, rng)
+    assert masked.size == gen_len and clean.size == seq_len - gen_len
+    assert np.array_equal(np.sort(np.concatenate([clean, masked])), np.arange(seq_len))
+    m = np.zeros(seq_len, bool)
+    m[masked] = True
+    starts = np.nonzero(m & ~np.concatenate([[False], m[:-1]]))[0]
+    assert starts.size == spans and starts.min() >= 1       # every span follows a clean token
+
+
+def test_text_variant_workload():
+    from small_workloads import tiny_infill
+    cfg = tiny_infill()
+    wl = make_workload(cfg, tables=False)
+    assert wl.prompt_pos.shape == (cfg.batch, cfg.prompt_len) and wl.gen_pos.shape == (cfg.batch, cfg.gen_len)
+    for b in range(cfg.batch):
+        assert np.array_equal(np.sort(np.concatenate([wl.prompt_pos[b], wl.gen_pos[b]])), np.arange(cfg.seq_len))
+    blocks = [st.block for st in wl.semi_ar if st.sub == 0]
+    assert sorted(blocks) == list(range(cfg.gen_len // cfg.block))
+    # the extra seed stream leaves the tables, prompt and plan sizes of the plain config unchanged
+    plain = make_workload(cfg.replace(infill_spans=0, block_order="ltr"), tables=False)
+    assert np.array_equal(plain.prompt_ids, wl.prompt_ids)
+    assert np.array_equal(plain.prompt_pos[0], np.arange(cfg.prompt_len))

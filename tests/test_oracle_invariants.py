@@ -24,7 +24,7 @@ from oracle import attention, dense, masks, rope, sparse_repr
 from oracle.logits import decide
 from oracle.numerics import round_storage, table_values
 from oracle.step import Model, SequenceOracle, run_workload
-from small_workloads import tiny_bf16, tiny_semi_ar, workload
+from small_workloads import tiny_bf16, tiny_infill, tiny_semi_ar, workload
 
 
 def _layer2(cfg, seed=7):
@@ -45,7 +45,8 @@ def _history(res, k, i):
 
 
 @pytest.mark.parametrize("layers,precision,cfgfn", [
-    (1, "bf16", tiny_bf16), (2, "none", tiny_bf16), (1, "bf16", tiny_semi_ar), (2, "none", tiny_semi_ar)])
+    (1, "bf16", tiny_bf16), (2, "none", tiny_bf16), (1, "bf16", tiny_semi_ar), (2, "none", tiny_semi_ar),
+    (1, "bf16", tiny_infill), (2, "none", tiny_infill)])
 def test_incremental_equals_dense_block_mask(layers, precision, cfgfn):
     cfg = cfgfn()
     wl = workload(cfg)
@@ -56,7 +57,8 @@ def test_incremental_equals_dense_block_mask(layers, precision, cfgfn):
         rec = res.records[k]
         for i, b in enumerate(res.batches):
             hist = _history(res, k, i)
-            ids, pos, blk, m, spans = dense.build_rows(model, wl.prompt_ids[b], hist, [rec.c_pos[i]])
+            ids, pos, blk, m, spans = dense.build_rows(model, wl.prompt_ids[b], hist, [rec.c_pos[i]],
+                                                       prompt_pos=wl.prompt_pos[b])
             outs = dense.dense_forward(model, ids, pos, blk, m)
             last = outs[-1]
             n_d = rec.d_pos[i].size
@@ -99,12 +101,12 @@ def test_two_masked_blocks_simulate_two_paths():
             assert np.allclose(out.o[:n_d], last[blk == m], rtol=1e-11, atol=1e-12)
 
 
-@pytest.mark.parametrize("cfgfn", [tiny_bf16, tiny_semi_ar])
+@pytest.mark.parametrize("cfgfn", [tiny_bf16, tiny_semi_ar, tiny_infill])
 def test_sparse_state_round_trips_every_step(cfgfn):
     cfg = cfgfn()
     wl = workload(cfg)
     model = Model.from_workload(wl)
-    seqs = [SequenceOracle(model, wl.prompt_ids[b]) for b in range(cfg.batch)]
+    seqs = [SequenceOracle(model, wl.prompt_ids[b], wl.prompt_pos[b]) for b in range(cfg.batch)]
     res = run_workload(wl)
     # replay the decisions and check the cache <-> dense sequence correspondence
     for i, s in enumerate(seqs):
@@ -161,3 +163,39 @@ def test_bruteforce_step_matches():
     assert np.allclose(z, r1.z, rtol=1e-12, atol=1e-12)
     tok = decide(z)[0]
     assert np.array_equal(tok, r1.token[0])
+
+
+def test_bruteforce_infill_step_matches():
+    """Infilling: the clean tokens sit between the masked spans.  The second
+    step of the first decoded block, rebuilt from scratch with the prompt at
+    its scattered positions, matches the incremental loop."""
+    cfg = tiny_infill(n_heads=2, n_kv_heads=1, head_dim=8, vocab=20, n_registers=2)
+    wl = workload(cfg)
+    assert not np.array_equal(wl.prompt_pos[0], np.arange(cfg.prompt_len))
+    model = Model.from_workload(wl)
+    res = run_workload(wl, batches=[0], n_steps=2, keep_steps=[0, 1], model=model)
+    r0, r1 = res.records
+    sel = r0.selected[0]
+    o, z = _bruteforce_step(model, wl.prompt_ids[0], wl.prompt_pos[0], r0.token[0][sel], r0.c_pos[0][sel],
+                            r1.c_pos[0])
+    assert np.allclose(o, r1.o[0], rtol=1e-12, atol=1e-13)
+    assert np.allclose(z, r1.z, rtol=1e-12, atol=1e-12)
+
+
+def test_infill_generation_keeps_prompt_and_follows_block_order():
+    """Page 3, section 3.2: the clean tokens are never re-decoded; every masked
+    position is unmasked exactly once, block by block in the drawn order, each
+    block within its own sub-steps."""
+    cfg = tiny_infill()
+    wl = workload(cfg)
+    res = run_workload(wl)
+    n_blocks = cfg.gen_len // cfg.block
+    seen_blocks = [st.block for st in wl.semi_ar if st.sub == 0]
+    assert sorted(seen_blocks) == list(range(n_blocks)) and seen_blocks != list(range(n_blocks))
+    for i, b in enumerate(res.batches):
+        assert np.array_equal(res.tokens[i][wl.prompt_pos[b]], wl.prompt_ids[b])
+        got = np.concatenate([u[i] for u in res.unmask])
+        assert np.array_equal(np.sort(got), wl.gen_pos[b])
+        for k, st in enumerate(wl.semi_ar):
+            blk = wl.gen_pos[b][st.block * cfg.block:(st.block + 1) * cfg.block]
+            assert set(res.unmask[k][i].tolist()) <= set(blk.tolist())
