@@ -198,6 +198,45 @@ int32_t mdm_cache_len(const mdm_ctx* ctx);
  * MDM_E_DEVICE if any kernel met an out-of-range token id or position. */
 mdm_status mdm_device_status(mdm_ctx* ctx);
 
+/* ---- training-form attention under the block mask -----------------------
+ * Page 1 (papernotes.org), key design 3; page 3 (paperlayer.ai), sections 3.3
+ * and 7.3: training reproduces the incremental cache in one parallel forward.
+ * Every row of a sequence carries a block id.  With M = n_clean_blocks[b]
+ * (the prompt is block 0, clean tokens are blocks 1..M, masked tokens blocks
+ * M+1..M+N, each masked block followed by its own copy of the registers under
+ * the same id), a row of block i <= M sees the keys of blocks j <= i; a row of
+ * block i > M sees its own block and every block j <= M.  Ids are labels: rows
+ * may come in any order, any int32 values are allowed, and every row sees at
+ * least itself.
+ *
+ * Inputs are the layer's RoPE'd activations (this call applies no RoPE):
+ *   q       bf16 [B][n][H][head_dim]
+ *   k, v    bf16 [B][n][H_kv][head_dim]
+ *   blocks  int32 [B][n]
+ *   n_clean_blocks  int32 [B]
+ * Output: out fp32 [B][n][H][head_dim] = softmax(q k^T / sqrt(head_dim)) v
+ * over the visible keys (query head h uses kv head h / (H / H_kv)).
+ * q, k, v and out must be 16-byte aligned; the workspace (caller-owned,
+ * mdm_block_attention_workspace_bytes, 4-byte aligned) holds per-tile block-id
+ * ranges.  head_dim must be 128 and n at most 16384 (MDM_E_UNSUPPORTED);
+ * MDM_E_ARG for NULL pointers, non-positive sizes, H not a multiple of H_kv or
+ * misalignment; MDM_E_SHAPE for a short workspace.  No context: the call is
+ * enqueued on `stream` (a hipStream_t, NULL = the default stream) and errors
+ * are reported by mdm_last_error(NULL). */
+typedef struct {
+  int32_t batch;
+  int32_t n_rows;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+} mdm_block_attn_shape;
+
+size_t mdm_block_attention_workspace_bytes(const mdm_block_attn_shape* shape);
+
+mdm_status mdm_block_attention(const mdm_block_attn_shape* shape, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Release the host context (device buffers stay the caller's). */
 void mdm_sparse_step_destroy(mdm_ctx* ctx);
 

@@ -58,6 +58,16 @@ class MdmBuffers(ctypes.Structure):
     ]
 
 
+class MdmBlockAttnShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_rows", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -79,6 +89,9 @@ _SIGS = {
     "mdm_sparse_step_destroy": (None, [_P]),
     "mdm_last_error": (ctypes.c_char_p, [_P]),
     "mdm_status_string": (ctypes.c_char_p, [_I32]),
+    "mdm_block_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MdmBlockAttnShape)]),
+    "mdm_block_attention": (_I32, [ctypes.POINTER(MdmBlockAttnShape), _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]),
 }
 
 
@@ -180,3 +193,14 @@ def mdm_sparse_step_destroy(ctx):
 
 def mdm_last_error(ctx=None) -> str:
     return load().mdm_last_error(ctx).decode()
+
+
+def mdm_block_attention_workspace_bytes(shape: MdmBlockAttnShape) -> int:
+    return load().mdm_block_attention_workspace_bytes(ctypes.byref(shape))
+
+
+def mdm_block_attention(shape: MdmBlockAttnShape, q, k, v, blocks, n_clean_blocks, out, workspace,
+                        workspace_bytes: int, stream=None):
+    _check(load().mdm_block_attention(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(blocks),
+                                      _ptr(n_clean_blocks), _ptr(out), _ptr(workspace), workspace_bytes,
+                                      _ptr(stream)))

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmdm_sparse.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["append.hip", "attention.hip", "vocab.hip", "select.hip", "api.cpp"]
+SOURCES = ["append.hip", "attention.hip", "block_attention.hip", "vocab.hip", "select.hip", "api.cpp"]
 ARCH = os.environ.get("MDM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -398,6 +398,46 @@ mdm_status mdm_device_status(mdm_ctx* ctx) {
   return MDM_OK;
 }
 
+namespace {
+constexpr int kBlockAttnHeadDim = 128;
+bool block_shape_ok(const mdm_block_attn_shape* s) {
+  return s && s->batch > 0 && s->n_rows > 0 && s->n_heads > 0 && s->n_kv_heads > 0 &&
+         s->n_heads % s->n_kv_heads == 0;
+}
+size_t block_ws_bytes(const mdm_block_attn_shape* s) {
+  return (size_t)s->batch * ((s->n_rows + kKeyTile - 1) / kKeyTile) * 2 * sizeof(int32_t);
+}
+}  // namespace
+
+size_t mdm_block_attention_workspace_bytes(const mdm_block_attn_shape* shape) {
+  return block_shape_ok(shape) ? block_ws_bytes(shape) : 0;
+}
+
+mdm_status mdm_block_attention(const mdm_block_attn_shape* s, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!block_shape_ok(s))
+    return fail(nullptr, MDM_E_ARG, "block attention: sizes must be positive and n_heads a multiple of n_kv_heads");
+  if (s->head_dim != kBlockAttnHeadDim)
+    return fail(nullptr, MDM_E_UNSUPPORTED, "block attention: head_dim %d (only 128)", s->head_dim);
+  if (s->n_rows > kBlockAttnMaxTiles * kKeyTile)
+    return fail(nullptr, MDM_E_UNSUPPORTED, "block attention: %d rows (at most %d)", s->n_rows,
+                kBlockAttnMaxTiles * kKeyTile);
+  if (!q || !k || !v || !blocks || !n_clean_blocks || !out || !workspace)
+    return fail(nullptr, MDM_E_ARG, "block attention: a required pointer is NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16)
+    return fail(nullptr, MDM_E_ARG, "block attention: q, k, v and out must be 16-byte aligned");
+  if ((uintptr_t)workspace % 4) return fail(nullptr, MDM_E_ARG, "block attention: workspace must be 4-byte aligned");
+  if (workspace_bytes < block_ws_bytes(s))
+    return fail(nullptr, MDM_E_SHAPE, "block attention: workspace has %zu bytes, needs %zu", workspace_bytes,
+                block_ws_bytes(s));
+  BlockAttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.blk = blocks; a.n_clean = n_clean_blocks; a.out = out;
+  a.ranges = static_cast<int32_t*>(workspace);
+  a.B = s->batch; a.n = s->n_rows; a.H = s->n_heads; a.Hkv = s->n_kv_heads;
+  return hip_check(nullptr, launch_block_attention(a, static_cast<hipStream_t>(stream)), "block attention launch");
+}
+
 void mdm_sparse_step_destroy(mdm_ctx* ctx) { delete ctx; }
 
 const char* mdm_last_error(const mdm_ctx* ctx) { return ctx ? ctx->err.c_str() : g_last_error.c_str(); }

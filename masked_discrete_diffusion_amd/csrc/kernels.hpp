@@ -119,4 +119,19 @@ hipError_t launch_select(const Geometry& g, const SelectArgs& a, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
 
+// Training-form (block-mask) attention, bf16 in, fp32 out, head_dim 128.
+constexpr int kBlockAttnMaxTiles = 256;   // rows per sequence <= 256 * 64
+struct BlockAttnArgs {
+  const void* q;            // bf16 [B][n][H][128]
+  const void* k;            // bf16 [B][n][H_kv][128]
+  const void* v;            // bf16 [B][n][H_kv][128]
+  const int32_t* blk;       // [B][n] block id of every row
+  const int32_t* n_clean;   // [B] number of clean blocks M
+  float* out;               // [B][n][H][128]
+  int32_t* ranges;          // workspace [B][ceil(n/64)][2]
+  int B, n, H, Hkv;
+  int nbk, real_blocks;     // set by the launcher
+};
+hipError_t launch_block_attention(BlockAttnArgs a, hipStream_t s);
+
 }  // namespace mdm

@@ -93,3 +93,27 @@ def gpu_text_infill(index=117, **kw):
     base = dict(name="gpu_text_infill", infill_spans=4, block_order="random")
     base.update(kw)
     return gpu_small_semi_ar(index=index, **base)
+
+
+# Training-form (block-mask) attention: ragged block boundaries, grouped
+# heads, rows in block order and shuffled, fewer rows than one key tile.
+def ba_small(index=130, **kw):
+    from mdm_inputs.training import TrainAttnConfig
+    base = dict(name="ba_small", index=index, batch=2, n_heads=4, n_kv_heads=2, head_dim=128, prompt_len=37,
+                gen_len=300, n_registers=5, clean_blocks=3, masked_blocks=4)
+    base.update(kw)
+    return TrainAttnConfig(**base)
+
+
+BA_CASES = {
+    "ragged_gqa2": lambda: ba_small(),
+    "shuffled_rows": lambda: ba_small(index=131, n_heads=2, n_kv_heads=2, shuffle_rows=True),
+    "under_one_tile_gqa8": lambda: ba_small(index=132, batch=3, n_heads=8, n_kv_heads=1, prompt_len=5,
+                                            gen_len=30, n_registers=3, clean_blocks=2, masked_blocks=2),
+    "aligned_text_gqa4": lambda: ba_small(index=133, n_heads=8, n_kv_heads=2, prompt_len=64, gen_len=256,
+                                          n_registers=16, clean_blocks=4, masked_blocks=4),
+    "all_masked": lambda: ba_small(index=134, n_heads=2, n_kv_heads=1, prompt_len=20, gen_len=150,
+                                   n_registers=7, clean_blocks=0, masked_blocks=5, mask_ratio=1.0),
+    "single_head_long": lambda: ba_small(index=135, batch=1, n_heads=1, n_kv_heads=1, prompt_len=100,
+                                         gen_len=1500, n_registers=20, clean_blocks=6, masked_blocks=3),
+}

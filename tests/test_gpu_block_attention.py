@@ -1,0 +1,111 @@
+"""Training-form (block-mask) attention on the GPU against the oracle.
+
+The oracle is attention in float64 (``oracle.attention.attend``) under the
+block rule (``oracle.masks.block_mask``), both pinned by the CPU tests (the
+incremental loop equals the dense block-mask forward; brute force).  Inputs
+are the bf16 values both sides read.  Bars: 2e-2 relative + 1e-2 absolute per
+element (bf16 activations), and max |err| / max |ref| below 4e-3 per head.
+"""
+
+import numpy as np
+import pytest
+
+from mdm_inputs.generate import bf16_bits_to_f32
+from mdm_inputs.training import get_train_config, make_train_attn_inputs
+from oracle.attention import attend
+from oracle.masks import block_mask
+from small_workloads import BA_CASES
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL, TIGHT = 2e-2, 1e-2, 4e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(inp):
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    cfg = inp.cfg
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    q, k, v = t(inp.q), t(inp.k), t(inp.v)
+    blocks = torch.from_numpy(inp.blocks).to(dev)
+    n_clean = torch.from_numpy(inp.n_clean).to(dev)
+    shape = L.MdmBlockAttnShape(batch=cfg.batch, n_rows=cfg.n_rows, n_heads=cfg.n_heads,
+                                n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim)
+    ws_bytes = L.mdm_block_attention_workspace_bytes(shape)
+    ws = torch.zeros(ws_bytes // 4 + 1, dtype=torch.int32, device=dev)
+    out = torch.full((cfg.batch, cfg.n_rows, cfg.n_heads, cfg.head_dim), float("nan"), device=dev)
+    L.mdm_block_attention(shape, q, k, v, blocks, n_clean, out, ws, ws_bytes,
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _check(got, ref, what):
+    err = np.abs(got - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))
+    assert not bad.any(), f"{what}: {int(bad.sum())}/{bad.size} outside tolerance, max abs err {np.nanmax(err):.3g}"
+    for h in range(ref.shape[1]):
+        rel = np.max(np.abs(got[:, h] - ref[:, h])) / np.max(np.abs(ref[:, h]))
+        assert rel <= TIGHT, f"{what} head {h}: max err / max ref = {rel:.3g}"
+    return float(np.max(err))
+
+
+@pytest.mark.parametrize("case", list(BA_CASES))
+def test_block_attention_matches_oracle(case):
+    cfg = BA_CASES[case]()
+    _say(f"block attention parity: {case} B={cfg.batch} n={cfg.n_rows} H={cfg.n_heads}/{cfg.n_kv_heads}")
+    inp = make_train_attn_inputs(cfg)
+    out = _run(inp)
+    worst = 0.0
+    for b in range(cfg.batch):
+        blk = inp.blocks[b]
+        vis = block_mask(blk, blk, int(inp.n_clean[b]))
+        ref = attend(_f64(inp.q[b]), _f64(inp.k[b]), _f64(inp.v[b]), vis)
+        worst = max(worst, _check(out[b], ref, f"{case} b {b}"))
+    _say(f"  worst abs error {worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["train_t2i_4k", "train_text"])
+def test_block_attention_full_size_sampled_rows(name):
+    """The full training workloads, in the launch configuration the benchmark
+    times, checked on sampled rows (every head) that the oracle computes one
+    by one: the first and last rows, rows at block boundaries and random rows."""
+    cfg = get_train_config(name)
+    _say(f"block attention full size: {name} B={cfg.batch} n={cfg.n_rows}")
+    inp = make_train_attn_inputs(cfg)
+    out = _run(inp)
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(7)
+    for b in range(cfg.batch):
+        blk = inp.blocks[b]
+        edges = np.nonzero(np.diff(blk))[0]
+        rows = np.unique(np.concatenate([[0, cfg.n_rows - 1], edges, edges + 1,
+                                         rng.choice(cfg.n_rows, 48, replace=False)]))
+        vis = block_mask(blk[rows], blk, int(inp.n_clean[b]))
+        ref = attend(_f64(inp.q[b][rows]), _f64(inp.k[b]), _f64(inp.v[b]), vis)
+        _check(out[b][rows], ref, f"{name} b {b}")
+
+
+def test_block_attention_rejects_bad_arguments_without_launch():
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    shape = L.MdmBlockAttnShape(batch=1, n_rows=64, n_heads=2, n_kv_heads=1, head_dim=128)
+    t = torch.zeros(64 * 2 * 128, dtype=torch.int16, device="cuda")
+    o = torch.zeros(64 * 2 * 128, dtype=torch.float32, device="cuda")
+    i = torch.zeros(64, dtype=torch.int32, device="cuda")
+    with pytest.raises(L.MdmError) as e:
+        L.mdm_block_attention(shape, t, t, t, i, i, o, i, 4, None)
+    assert e.value.status == L.MDM_E_SHAPE
+    with pytest.raises(L.MdmError) as e:
+        L.mdm_block_attention(L.MdmBlockAttnShape(batch=1, n_rows=64, n_heads=2, n_kv_heads=1, head_dim=64),
+                              t, t, t, i, i, o, i, 256, None)
+    assert e.value.status == L.MDM_E_UNSUPPORTED
