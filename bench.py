@@ -24,6 +24,12 @@ cpu_baseline: the CPU oracle (float64 NumPy) timed on this host on a bounded
           sample: sequence 0 of the same workload, from the prompt through as
           many sampling steps as fit in the time budget.
 
+Training-form attention (the block-mask forward of the same method):
+    python bench.py --block-attention [--workload train_t2i_4k|train_text]
+        one JSON line: algorithmic TFLOP/s of mdm_block_attention against the
+        bf16 MFMA peak, timed with HIP events over K launches, and the CPU
+        oracle on a bounded sample.
+
 Profiling helpers (used to produce profiles/):
     python bench.py --profile-steps N         N eager generations, nothing else
     python bench.py --copy-calibration        one plain 1 GiB device copy
@@ -187,6 +193,129 @@ def cpu_baseline(cfg, budget_s):
                       f"{cfg.n_steps} ({tokens} tokens) in {dt:.1f} s, float64 NumPy on {cpu}"}
 
 
+def block_attention_pairs(blocks, m):
+    """Visible (query, key) pairs of one sequence under the block rule, from
+    the block sizes: a clean block i sees blocks j <= i, a masked block i
+    sees itself and blocks j <= m."""
+    ids, sizes = np.unique(blocks, return_counts=True)
+    clean = ids <= m
+    total = 0
+    for i, sz in zip(ids, sizes):
+        seen = sizes[ids <= i].sum() if i <= m else sizes[clean].sum() + sz
+        total += int(sz) * int(seen)
+    return total
+
+
+def block_attention_bench(args):
+    """Training-form attention (mdm_block_attention) on one training batch:
+    W untimed launches, then K launches bracketed by HIP events on the stream
+    they run on.  value = algorithmic TFLOP/s = 4 d H * visible pairs per
+    launch / mean launch time (MFMA-bound: the contraction over a 64-key tile
+    does 128 FLOP per byte of K and V read)."""
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    from mdm_inputs.training import get_train_config, make_train_attn_inputs
+
+    cfg = get_train_config(args.workload if args.workload.startswith("train_") else "train_t2i_4k")
+    inp = make_train_attn_inputs(cfg)
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    q, k, v = t(inp.q), t(inp.k), t(inp.v)
+    blocks = torch.from_numpy(inp.blocks).to(dev)
+    n_clean = torch.from_numpy(inp.n_clean).to(dev)
+    shape = L.MdmBlockAttnShape(batch=cfg.batch, n_rows=cfg.n_rows, n_heads=cfg.n_heads,
+                                n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim)
+    ws_bytes = L.mdm_block_attention_workspace_bytes(shape)
+    ws = torch.zeros(ws_bytes // 4 + 1, dtype=torch.int32, device=dev)
+    out = torch.empty((cfg.batch, cfg.n_rows, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        L.mdm_block_attention(shape, q, k, v, blocks, n_clean, out, ws, ws_bytes, stream.cuda_stream)
+
+    print(f"[bench] {cfg.name}: batch {cfg.batch}, {cfg.n_rows} rows, inputs ready", file=sys.stderr, flush=True)
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            launch()
+        torch.cuda.synchronize()
+        print(f"[bench] profiled {args.profile_steps} launches", file=sys.stderr, flush=True)
+        return
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        launch()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    pairs = sum(block_attention_pairs(inp.blocks[b], int(inp.n_clean[b])) for b in range(cfg.batch))
+    flops = 4.0 * cfg.head_dim * cfg.n_heads * pairs
+    nbytes = 2.0 * cfg.batch * cfg.n_rows * cfg.head_dim * (cfg.n_heads + 2 * cfg.n_kv_heads) \
+        + 4.0 * cfg.batch * cfg.n_rows * cfg.n_heads * cfg.head_dim
+    tflops = flops / (ms / 1e3) / 1e12
+    res = {
+        "metric": "training-form block-mask attention, algorithmic TFLOP/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "rows": cfg.n_rows, "prompt_tokens": cfg.prompt_len,
+                   "generated_tokens": cfg.gen_len, "registers_per_masked_block": cfg.n_registers,
+                   "clean_blocks": cfg.clean_blocks, "masked_blocks": cfg.masked_blocks,
+                   "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "mdm_block_attention: k_tile_ranges + k_block_attn",
+                     "visible_pairs_per_head": pairs, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = block_attention_cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+def block_attention_cpu_baseline(inp, budget_s):
+    """The oracle (float64 NumPy attention under the block mask) on sequence 0,
+    one query head after another until the budget is spent."""
+    from threadpoolctl import threadpool_info
+    from mdm_inputs.generate import bf16_bits_to_f32
+    from oracle.attention import attend
+    from oracle.masks import block_mask
+
+    cfg = inp.cfg
+    blk = inp.blocks[0]
+    m = int(inp.n_clean[0])
+    G = cfg.n_heads // cfg.n_kv_heads
+    f64 = lambda a: bf16_bits_to_f32(a).astype(np.float64)
+    t0 = time.perf_counter()
+    vis = block_mask(blk, blk, m)
+    heads = 0
+    for h in range(cfg.n_heads):
+        kvh = h // G
+        attend(f64(inp.q[0][:, h:h + 1]), f64(inp.k[0][:, kvh:kvh + 1]), f64(inp.v[0][:, kvh:kvh + 1]), vis)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.head_dim * heads * block_attention_pairs(blk, m)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence 0 of {cfg.name}: {heads} of {cfg.n_heads} query heads "
+                      f"({cfg.n_rows} rows each) in {dt:.1f} s, float64 NumPy"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +328,8 @@ def main():
                     help="run only this many eager generations (for profilers) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of 1 GiB (counter calibration) and exit")
+    ap.add_argument("--block-attention", action="store_true",
+                    help="time the training-form block-mask attention (workload train_t2i_4k or train_text)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
                     help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR: write the attention traffic summary")
     args = ap.parse_args()
@@ -219,6 +350,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(f"[bench] copied {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+        return
+    if args.block_attention:
+        block_attention_bench(args)
         return
     from masked_discrete_diffusion_amd import _lib as L
     from masked_discrete_diffusion_amd.sampler import SparseStepRunner

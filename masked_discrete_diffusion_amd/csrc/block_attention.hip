@@ -20,8 +20,11 @@
 // Per tile: K and V go from HBM to LDS by LDS-DMA (global_load_lds_dwordx4)
 // through a 4-deep ring, both in their natural [key][d] layout with 16-byte
 // units XOR-swizzled per row.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q^T
-// in registers), fp32 online softmax with a lazily raised reference maximum,
-// P in bf16, O^T += V^T P^T.  The V^T operand comes straight from the
+// in registers), fp32 softmax at a fixed reference (each row's maximum over
+// the wavefront's first seen tile), P in bf16, O^T += V^T P^T; the scores of
+// tile i + 1 are issued next to the softmax of tile i.  A row sum that
+// reaches 2^50 (a later score far above the reference) sends the block
+// through a second pass with a running maximum, which gives the same softmax.  The V^T operand comes straight from the
 // natural-layout V tile through the LDS transpose read ds_read_b64_tr_b16:
 // within each 16 lanes, lane j receives element j%4 of the 64-bit words that
 // lanes 4e + j/4 addressed (e = 0..3), so lanes that address 4 consecutive
@@ -37,19 +40,20 @@ namespace mdm {
 namespace {
 
 constexpr int kD = 128;                              // head dim
-constexpr int kBaWaves = 8;
+constexpr int kRB = 1;                                // 32-row MFMA blocks per wavefront
+constexpr int kBaWaves = 8 / kRB;                     // wavefronts per block (256 rows)
+constexpr int kRowsPerWave = 32 * kRB;
 constexpr int kBaThreads = kBaWaves * kWave;
 constexpr int kBaStages = 4;                          // LDS ring depth (tiles)
-constexpr int kBaAhead = 3;                           // tiles loaded ahead of the one computed
+constexpr int kBaAhead = 2;                           // tiles loaded ahead of the one being scored
 constexpr int kRowBytes = kD * 2;                     // one K or V row in LDS (16 units, no padding)
 constexpr int kTileBytes = kKeyTile * kRowBytes;      // 16 KiB
 constexpr int kDmaBlocks = 2 * kTileBytes / 1024;     // 32 wave-wide 1 KiB loads per K+V tile
 constexpr int kLpw = kDmaBlocks / kBaWaves;           // loads per wavefront per tile
 static_assert(kDmaBlocks % kBaWaves == 0, "K and V loads split evenly over the wavefronts");
-static_assert(kBaStages >= kBaAhead + 1, "the slot of tile i + ahead must be free at step i");
+static_assert(kBaStages >= kBaAhead + 2, "tiles i (PV) and i + 1 (scores) stay while i + 1 + ahead loads");
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.f;                   // raise the reference only past 2^8
 constexpr float kRefFloor = -3.0e38f;                 // finite start for the reference
 
 enum : int { kUnseen = 0, kSeen = 1, kPartly = 2 };
@@ -148,6 +152,14 @@ __device__ inline uint32_t dma_src(int blk, int lane, bool is_k, int rs, int las
   return (uint32_t)(min(r, last_row) * rs + 16 * (p ^ sw));
 }
 
+// A pointer every lane holds the same value of, in scalar registers.
+__device__ inline const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const uint16_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 struct BaCtx {
   const uint16_t* kbase;    // keys of (b, kvh) at row 0
   const uint16_t* vbase;
@@ -156,13 +168,13 @@ struct BaCtx {
   uint32_t ring_k, ring_v;  // LDS byte addresses of the two rings
 };
 
-// Issue this wavefront's DMA loads of tile t into ring slot s.  Wavefronts
-// 0-3 load K, 4-7 load V, 4 wave-wide loads each.
+// Issue this wavefront's DMA loads of tile t into ring slot s.  The first
+// half of the wavefronts loads K, the second half V, kLpw wave-wide loads each.
 __device__ inline void issue_tile(const BaCtx& c, int t, int s, int wave, const uint32_t (&off)[kLpw], int lane) {
-  const bool is_k = wave < 4;
-  const int key0 = t * kKeyTile;
-  const uint16_t* base = (is_k ? c.kbase : c.vbase) + (int64_t)key0 * (c.rs / 2);
-  const uint32_t dst = (is_k ? c.ring_k : c.ring_v) + s * kTileBytes + (wave & 3) * kLpw * 1024;
+  const bool is_k = wave < kBaWaves / 2;
+  const int key0 = __builtin_amdgcn_readfirstlane(t) * kKeyTile;
+  const uint16_t* base = uniform_ptr((is_k ? c.kbase : c.vbase) + (int64_t)key0 * (c.rs / 2));
+  const uint32_t dst = (is_k ? c.ring_k : c.ring_v) + s * kTileBytes + (wave % (kBaWaves / 2)) * kLpw * 1024;
   if (key0 + kKeyTile <= c.n) {
 #pragma unroll
     for (int i = 0; i < kLpw; ++i) dma16_at(base, off[i], dst + i * 1024);
@@ -170,31 +182,17 @@ __device__ inline void issue_tile(const BaCtx& c, int t, int s, int wave, const 
     // last, partial tile: rows past n re-read row n-1 (masked later)
     const int last = c.n - 1 - key0;
 #pragma unroll
-    for (int i = 0; i < kLpw; ++i) dma16_at(base, dma_src((wave & 3) * kLpw + i, lane, is_k, c.rs, last), dst + i * 1024);
+    for (int i = 0; i < kLpw; ++i)
+      dma16_at(base, dma_src((wave % (kBaWaves / 2)) * kLpw + i, lane, is_k, c.rs, last), dst + i * 1024);
   }
 }
 
-// Wait for tile i's loads (this wavefront's; the barrier covers everyone's),
+// Wait for a tile's loads (this wavefront's; the barrier covers everyone's)
 // when `younger` later tiles of this wavefront may stay in flight.
 __device__ inline void wait_tile(int younger) {
-  static_assert(kBaAhead == 3, "waits are spelled out for three tiles ahead");
-  if (younger >= 2) ring_wait<2 * kLpw>();
-  else if (younger == 1) ring_wait<kLpw>();
+  static_assert(kBaAhead == 2, "waits are spelled out for two tiles ahead");
+  if (younger >= 1) ring_wait<kLpw>();
   else ring_wait<0>();
-}
-
-// S^T of one 32-key half hk: lane holds keys 8j + 4(lane >> 5) + i (e = 4j + i)
-// of the half for row lane & 31.
-__device__ inline floatx16 s_half(uint32_t ks, const LaneOffsets& lo, const bf16x8 (&qf)[8], int hk) {
-  floatx16 sv;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) sv[e] = 0.f;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const bf16x8 kf = lds_read_b128(ks + lo.k[t] + hk * 32 * kRowBytes);
-    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv, 0, 0, 0);
-  }
-  return sv;
 }
 
 __device__ inline float max3(float a, float b, float c) {
@@ -209,15 +207,41 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Scores of keys this row may not see become -inf (exp2 gives exactly 0).
-__device__ inline void mask_half(floatx16& sv, const int32_t* kblk, int key0, int n, int qb, int m) {
+// Scores of one tile for the wavefront's rows: s[rb][hk] = S^T of row block
+// rb (rows 32rb + lane & 31) and 32-key half hk; lane holds keys
+// 8j + 4(lane >> 5) + i (e = 4j + i) of the half.  Each K operand read from
+// LDS feeds every row block.
+typedef floatx16 TileS[kRB][2];
+__device__ inline void tile_scores(uint32_t ks, const LaneOffsets& lo, const bf16x8 (&qf)[kRB][8], TileS& s) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[rb][hk][e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const bf16x8 kf = lds_read_b128(ks + lo.k[t] + hk * 32 * kRowBytes);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) s[rb][hk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][t], s[rb][hk], 0, 0, 0);
+    }
+}
+
+// Scores of keys a row may not see become -inf (exp2 gives exactly 0).
+__device__ inline void mask_tile(TileS& s, const int32_t* kblk, int key0, int n, const int (&qb)[kRB], int m) {
   const int h = (__lane_id() >> 5) & 1;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int key = key0 + 8 * (e / 4) + 4 * h + (e % 4);
-    const int kb = kblk[min(key, n - 1)];
-    sv[e] = (key < n && block_visible(qb, kb, m)) ? sv[e] : -__builtin_inff();
-  }
+  for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + 32 * hk + 8 * (e / 4) + 4 * h + (e % 4);
+      const int kb = kblk[min(key, n - 1)];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        s[rb][hk][e] = (key < n && block_visible(qb[rb], kb, m)) ? s[rb][hk][e] : -__builtin_inff();
+    }
 }
 
 __device__ inline float tile_max(const floatx16& s0, const floatx16& s1) {
@@ -241,27 +265,113 @@ __device__ inline float exp_half(floatx16& sv, float m_ref, float sc) {
   return sum;
 }
 
-// O^T += V^T P^T for half hk of the tile in ring slot vs.  K-step u takes the
-// lane's p values 8u..8u+7 = keys 16u + 4(lane >> 5) + {0..3} and
-// 16u + 8 + 4(lane >> 5) + {0..3}; the two transpose reads deliver V at
-// exactly those keys.
-__device__ inline void pv_half(const floatx16& p, uint32_t vs, const LaneOffsets& lo, floatx16 (&acc)[4], int hk) {
+// O^T += V^T P^T for every row block over the tile in ring slot vs.  K-step
+// (hk, u) takes the lane's p values 8u..8u+7 of half hk = keys
+// 32hk + 16u + 4(lane >> 5) + {0..3} and 32hk + 16u + 8 + 4(lane >> 5) + {0..3};
+// the two transpose reads deliver V at exactly those keys, and each V
+// operand feeds every row block.
+__device__ inline void tile_pv(const TileS& p, uint32_t vs, const LaneOffsets& lo, floatx16 (&acc)[kRB][4]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 w;
+  for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(p[8 * u + 2 * q], p[8 * u + 2 * q + 1]);
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 pb[kRB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint32_t a = vs + lo.v[db] + (32 * hk + 16 * u) * kRowBytes;
-      const short4v r0 = lds_read_tr(a);
-      const short4v r1 = lds_read_tr(a + 8 * kRowBytes);
-      const short8v vv = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb, acc[db], 0, 0, 0);
+      for (int rb = 0; rb < kRB; ++rb) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(p[rb][hk][8 * u + 2 * q], p[rb][hk][8 * u + 2 * q + 1]);
+        pb[rb] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t a = vs + lo.v[db] + (32 * hk + 16 * u) * kRowBytes;
+        const short4v r0 = lds_read_tr(a);
+        const short4v r1 = lds_read_tr(a + 8 * kRowBytes);
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[rb], acc[rb][db], 0, 0, 0);
+      }
     }
+}
+
+// Online softmax of a tile's scores and O += P V with the running row
+// maximum as the reference, rescaling O and l on every tile (no branch, so
+// no merge of accumulator definitions).  Used by the recompute pass only.
+__device__ inline void tile_softmax_pv(TileS& s, uint32_t vs, const LaneOffsets& lo, floatx16 (&acc)[kRB][4],
+                                       float (&m_ref)[kRB], float (&l_run)[kRB], float sc) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float m_new = fmaxf(m_ref[rb], tile_max(s[rb][0], s[rb][1]) * sc);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);
+    l_run[rb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
+    m_ref[rb] = m_new;
+    l_run[rb] += exp_half(s[rb][0], m_ref[rb], sc) + exp_half(s[rb][1], m_ref[rb], sc);
   }
+  tile_pv(s, vs, lo, acc);
+}
+
+// Fixed-reference variant: p = exp2(s * sc - m_ref) with the reference never
+// raised, no maximum taken, no rescale.
+__device__ inline void tile_exp_pv_fixed(TileS& s, uint32_t vs, const LaneOffsets& lo, floatx16 (&acc)[kRB][4],
+                                         const float (&m_ref)[kRB], float (&l_run)[kRB], float sc) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) l_run[rb] += exp_half(s[rb][0], m_ref[rb], sc) + exp_half(s[rb][1], m_ref[rb], sc);
+  tile_pv(s, vs, lo, acc);
+}
+
+// A fully seen tile at the fixed reference, in one basic block: the scores
+// of both 32-key halves are issued first, then the exp of half 0 runs under
+// the MFMAs of half 1, and the exp of half 1 under the PV MFMAs of half 0.
+__device__ inline void tile_fixed_fused(uint32_t ks, uint32_t vs, const LaneOffsets& lo, const bf16x8 (&qf)[kRB][8],
+                                        floatx16 (&acc)[kRB][4], const float (&m_ref)[kRB], float (&l_run)[kRB],
+                                        float sc) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  TileS s;
+  tile_scores(ks, lo, qf, s);
+#pragma unroll
+  for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 pb[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        float sum = 0.f;
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][hk][8 * u + 2 * q], sc, -m_ref[rb]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][hk][8 * u + 2 * q + 1], sc, -m_ref[rb]));
+          sum += p0 + p1;
+          w[q] = pack_bf16x2(p0, p1);
+        }
+        l_run[rb] += sum;
+        pb[rb] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t a = vs + lo.v[db] + (32 * hk + 16 * u) * kRowBytes;
+        const short4v r0 = lds_read_tr(a);
+        const short4v r1 = lds_read_tr(a + 8 * kRowBytes);
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[rb], acc[rb][db], 0, 0, 0);
+      }
+    }
+}
+
+// Row sums stay below 2^kOverflowLog2 on the fixed-reference pass (then
+// every p did, and O = sum p v stays far inside fp32); a NaN fails too.
+constexpr float kOverflowLog2 = 50.f;
+
+__device__ inline int tile_class(const uint16_t* cls, int t, int wave) {
+  return __builtin_amdgcn_readfirstlane((cls[t] >> (2 * wave)) & 3);
 }
 
 __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
@@ -269,7 +379,7 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
   __shared__ int s_qrange[kBaWaves][2];
   __shared__ uint16_t s_cls[kBlockAttnMaxTiles];
   __shared__ uint16_t s_list[kBlockAttnMaxTiles];
-  __shared__ int s_count;
+  __shared__ int s_count, s_count_all;
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -281,21 +391,32 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
   const int bh = lb / a.nbk;
   const int cb = a.nbk - 1 - lb % a.nbk;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  const int n = a.n, n_rc = (n + 31) / 32, n_tiles = (n + kKeyTile - 1) / kKeyTile;
+  const int n = a.n, n_rc = (n + kRowsPerWave - 1) / kRowsPerWave, n_tiles = (n + kKeyTile - 1) / kKeyTile;
   const int chunk = cb * kBaWaves + wave;
   const int g = chunk % G, rc = chunk / G;
   const bool active = rc < n_rc;
   const int head = kvh * G + g;
-  const int row = rc * 32 + (lane & 31);
-  const bool row_ok = active && row < n;
-  const int rowc = min(row, n - 1);
   const int32_t* blk = a.blk + (int64_t)b * n;
   const int m = a.n_clean[b];
-  const int qb = blk[rowc];
+  int rowc[kRB], qb[kRB];
+  bool row_ok[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int row = rc * kRowsPerWave + 32 * rb + (lane & 31);
+    row_ok[rb] = active && row < n;
+    rowc[rb] = min(row, n - 1);
+    qb[rb] = blk[rowc[rb]];
+  }
 
   {
-    const int qmin = wave_min_i32(row_ok ? qb : INT_MAX);
-    const int qmax = wave_max_i32(row_ok ? qb : INT_MIN);
+    int lo_q = INT_MAX, hi_q = INT_MIN;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      lo_q = min(lo_q, row_ok[rb] ? qb[rb] : INT_MAX);
+      hi_q = max(hi_q, row_ok[rb] ? qb[rb] : INT_MIN);
+    }
+    const int qmin = wave_min_i32(lo_q);
+    const int qmax = wave_max_i32(hi_q);
     if (lane == 0) {
       s_qrange[wave][0] = active ? qmin : 1;
       s_qrange[wave][1] = active ? qmax : 0;     // empty range: every tile unseen
@@ -316,20 +437,34 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
     s_cls[t] = (uint16_t)word;
   }
   __syncthreads();
+  // Tile list: first the tiles every active wavefront sees whole (the
+  // branch-free main loop), then the remaining tiles some wavefront sees;
+  // each part in key order.
   if (wave == 0) {
+    uint32_t all = 0;
+#pragma unroll
+    for (int w = 0; w < kBaWaves; ++w) {
+      const bool on = s_qrange[w][0] <= s_qrange[w][1];
+      all |= (on ? (uint32_t)kSeen : 0u) << (2 * w);
+    }
     int cnt = 0;
-    for (int t0 = 0; t0 < n_tiles; t0 += kWave) {
-      const int t = t0 + lane;
-      const bool nz = t < n_tiles && s_cls[t] != 0;
-      const uint64_t mask = __ballot(nz);
-      const int pos = cnt + __builtin_popcountll(mask & ((1ull << lane) - 1ull));
-      if (nz) s_list[pos] = (uint16_t)t;
-      cnt += __builtin_popcountll(mask);
+    for (int part = 0; part < 2; ++part) {
+      for (int t0 = 0; t0 < n_tiles; t0 += kWave) {
+        const int t = t0 + lane;
+        const uint32_t w = t < n_tiles ? s_cls[t] : 0u;
+        const bool pick = part == 0 ? (w == all) : (w != 0 && w != all);
+        const uint64_t mask = __ballot(pick);
+        const int pos = cnt + __builtin_popcountll(mask & ((1ull << lane) - 1ull));
+        if (pick) s_list[pos] = (uint16_t)t;
+        cnt += __builtin_popcountll(mask);
+      }
+      if (part == 0 && lane == 0) s_count_all = cnt;
     }
     if (lane == 0) s_count = cnt;
   }
   __syncthreads();
-  const int nt = s_count;
+  const int nt = __builtin_amdgcn_readfirstlane(s_count);
+  const int n_all = __builtin_amdgcn_readfirstlane(s_count_all);
 
   BaCtx c;
   c.rs = a.Hkv * kD * 2;
@@ -340,77 +475,119 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
   c.ring_v = c.ring_k + kBaStages * kTileBytes;
   uint32_t off[kLpw];
 #pragma unroll
-  for (int i = 0; i < kLpw; ++i) off[i] = dma_src((wave & 3) * kLpw + i, lane, wave < 4, c.rs, kKeyTile - 1);
+  for (int i = 0; i < kLpw; ++i)
+    off[i] = dma_src((wave % (kBaWaves / 2)) * kLpw + i, lane, wave < kBaWaves / 2, c.rs, kKeyTile - 1);
 
+  auto start_ring = [&]() {
+    for (int i = 0; i < kBaAhead && i < nt; ++i) issue_tile(c, s_list[i], i, wave, off, lane);
+  };
   // prologue loads, then Q^T fragments (row, dims 16t + 8(lane >> 5)..+7)
-  for (int i = 0; i < kBaAhead && i < nt; ++i) issue_tile(c, s_list[i], i, wave, off, lane);
-  bf16x8 qf[8];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * n + rowc) * a.H + head) * kD;
+  start_ring();
+  bf16x8 qf[kRB][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t + 8 * (lane >> 5));
+  for (int rb = 0; rb < kRB; ++rb) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((int64_t)b * n + rowc[rb]) * a.H + head) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qf[rb][t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t + 8 * (lane >> 5));
   }
   const LaneOffsets lo = lane_offsets(lane);
   const float sc = kLog2e / sqrtf((float)kD);
-  floatx16 acc[4];
+  floatx16 acc[kRB][4];
+  float m_ref[kRB], l_run[kRB];
+  auto reset = [&]() {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
-  float m_ref = kRefFloor, l_run = 0.f;
-
-  for (int i = 0; i < nt; ++i) {
-    wait_tile(min(nt - 1 - i, kBaAhead - 1));
-    ring_barrier();
-    if (i + kBaAhead < nt) issue_tile(c, s_list[i + kBaAhead], (i + kBaAhead) % kBaStages, wave, off, lane);
-    const int t = s_list[i];
-    const int cls = __builtin_amdgcn_readfirstlane((s_cls[t] >> (2 * wave)) & 3);
-    if (cls == kUnseen) continue;
-    const int slot = i % kBaStages;
-    const uint32_t ks = c.ring_k + slot * kTileBytes, vs = c.ring_v + slot * kTileBytes;
-    floatx16 s0 = s_half(ks, lo, qf, 0);
-    floatx16 s1 = s_half(ks, lo, qf, 1);
-    if (cls == kPartly) {
-      mask_half(s0, blk, t * kKeyTile, n, qb, m);
-      mask_half(s1, blk, t * kKeyTile + 32, n, qb, m);
-    }
-    const float mt = tile_max(s0, s1) * sc;
-    // The rare rescale path repeats the exp and PV code, so that no branch
-    // merges two definitions of the accumulators in front of the MFMAs.
-    if (__builtin_expect(__any(mt > m_ref + kRescaleLog2), 0)) {
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
+    for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-      m_ref = m_new;
-      l_run += exp_half(s0, m_ref, sc);
-      pv_half(s0, vs, lo, acc, 0);
-      l_run += exp_half(s1, m_ref, sc);
-      pv_half(s1, vs, lo, acc, 1);
-    } else {
-      l_run += exp_half(s0, m_ref, sc);
-      pv_half(s0, vs, lo, acc, 0);
-      l_run += exp_half(s1, m_ref, sc);
-      pv_half(s1, vs, lo, acc, 1);
+        for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
+      m_ref[rb] = kRefFloor;
+      l_run[rb] = 0.f;
+    }
+  };
+  reset();
+
+  // Ring step of tile i: wait for it (own loads, then the barrier for
+  // everyone's) and issue tile i + 2.  The barrier also ends every
+  // wavefront's use of tile i - 2, whose slot receives tile i + 2.
+  auto ring_step = [&](int i) -> int {
+    wait_tile(min(nt - 1 - i, kBaAhead - 1));
+    ring_barrier();
+    if (i + kBaAhead < nt) issue_tile(c, s_list[i + kBaAhead], (i + kBaAhead) % kBaStages, wave, off, lane);
+    return tile_class(s_cls, s_list[i], wave);
+  };
+  // Scores of tile i when this wavefront's rows see it, masked when partly.
+  auto scores = [&](int i, int cls, TileS& s) {
+    if (cls != kUnseen) {
+      tile_scores(c.ring_k + (i % kBaStages) * kTileBytes, lo, qf, s);
+      if (cls == kPartly) mask_tile(s, blk, s_list[i] * kKeyTile, n, qb, m);
+    }
+  };
+
+  // Fast pass.  The reference of each row is the maximum over the
+  // wavefront's first tile and is never raised, so no loop carries a rescale
+  // branch.  Phase 1: the tiles every wavefront sees whole, one basic block
+  // each (the first peeled to set the reference); phase 2: the others.
+  TileS sA;
+  bool have_ref = false;
+  if (n_all > 0) {
+    const int cls = ring_step(0);
+    scores(0, cls, sA);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) m_ref[rb] = tile_max(sA[rb][0], sA[rb][1]) * sc;
+    have_ref = true;
+    tile_exp_pv_fixed(sA, c.ring_v, lo, acc, m_ref, l_run, sc);
+    for (int i = 1; i < n_all; ++i) {
+      ring_step(i);
+      tile_fixed_fused(c.ring_k + (i % kBaStages) * kTileBytes, c.ring_v + (i % kBaStages) * kTileBytes, lo, qf,
+                       acc, m_ref, l_run, sc);
+    }
+  }
+  for (int i = n_all; i < nt; ++i) {
+    const int cls = ring_step(i);
+    if (cls == kUnseen) continue;
+    scores(i, cls, sA);
+    if (!have_ref) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) m_ref[rb] = tile_max(sA[rb][0], sA[rb][1]) * sc;
+      have_ref = true;
+    }
+    tile_exp_pv_fixed(sA, c.ring_v + (i % kBaStages) * kTileBytes, lo, acc, m_ref, l_run, sc);
+  }
+  bool over = false;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) over = over || (row_ok[rb] && !(l_run[rb] < 0x1p50f));
+  static_assert(kOverflowLog2 == 50.f, "the bound above is 2^kOverflowLog2");
+  // A row sum reached the bound (or a row saw no key of its first tile):
+  // the whole block recomputes with a running maximum.  The barrier of the
+  // vote ends every wavefront's use of the ring.
+  if (__syncthreads_or(over ? 1 : 0)) {
+    reset();
+    start_ring();
+    for (int i = 0; i < nt; ++i) {
+      const int cls = ring_step(i);
+      scores(i, cls, sA);
+      if (cls != kUnseen) tile_softmax_pv(sA, c.ring_v + (i % kBaStages) * kTileBytes, lo, acc, m_ref, l_run, sc);
     }
   }
 
   // O = acc / l; lane holds dims 32db + 8j + 4(lane >> 5) + i of its row
-  const float inv = 1.f / halves_sum(l_run);
-  if (row_ok) {
-    float* orow = a.out + (((int64_t)b * n + row) * a.H + head) * kD + 4 * (lane >> 5);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float inv = 1.f / halves_sum(l_run[rb]);
+    if (row_ok[rb]) {
+      float* orow = a.out + (((int64_t)b * n + rc * kRowsPerWave + 32 * rb + (lane & 31)) * a.H + head) * kD +
+                    4 * (lane >> 5);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        floatx4 o;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc[db][4 * j + i] * inv;
-        *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * j) = o;
-      }
+        for (int j = 0; j < 4; ++j) {
+          floatx4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[rb][db][4 * j + e] * inv;
+          *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * j) = o;
+        }
+    }
   }
 }
 
@@ -421,7 +598,7 @@ hipError_t launch_block_attention(BlockAttnArgs a, hipStream_t s) {
   if (a.n <= 0 || n_tiles > kBlockAttnMaxTiles || a.Hkv <= 0 || a.H % a.Hkv) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tile_ranges, dim3(n_tiles, a.B), dim3(kWave), 0, s, a.blk, a.n, n_tiles, a.ranges);
   const int G = a.H / a.Hkv;
-  const int n_rc = (a.n + 31) / 32;
+  const int n_rc = (a.n + kRowsPerWave - 1) / kRowsPerWave;
   a.nbk = (G * n_rc + kBaWaves - 1) / kBaWaves;
   a.real_blocks = a.B * a.Hkv * a.nbk;
   const int grid = (a.real_blocks + 7) / 8 * 8;

@@ -74,6 +74,32 @@ def test_block_attention_matches_oracle(case):
     _say(f"  worst abs error {worst:.3g}")
 
 
+def test_block_attention_score_jump_takes_the_recompute_pass():
+    """Keys of the last masked block scaled by 64 (exact in bf16) give its
+    rows scores far above the reference of their first tile; the row sums
+    pass 2^50 and the block recomputes with a running maximum.  The result
+    must still match the oracle."""
+    cfg = BA_CASES["ragged_gqa2"]().replace(index=136, name="ba_score_jump")
+    inp = make_train_attn_inputs(cfg)
+    from mdm_inputs.generate import bf16_bits_from_f32
+    for b in range(cfg.batch):
+        last = inp.blocks[b] == inp.blocks[b].max()
+        k32 = bf16_bits_to_f32(inp.k[b][last]) * np.float32(64.0)
+        inp.k[b][last] = bf16_bits_from_f32(k32)
+    out = _run(inp)
+    for b in range(cfg.batch):
+        blk = inp.blocks[b]
+        vis = block_mask(blk, blk, int(inp.n_clean[b]))
+        q, k = _f64(inp.q[b]), _f64(inp.k[b])
+        ref = attend(q, k, _f64(inp.v[b]), vis)
+        # the jump is real: rows of the last block score its keys more than
+        # 2^50 above the keys of the first tile (log2 units, head 0)
+        last = np.nonzero(blk == blk.max())[0]
+        s = q[last, 0] @ k[:, 0].T / np.sqrt(cfg.head_dim) * np.log2(np.e)
+        assert np.max(s[:, last].max(axis=1) - s[:, :64].max(axis=1)) > 50
+        _check(out[b], ref, f"score jump b {b}")
+
+
 @pytest.mark.parametrize("name", ["train_t2i_4k", "train_text"])
 def test_block_attention_full_size_sampled_rows(name):
     """The full training workloads, in the launch configuration the benchmark
