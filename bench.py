@@ -276,7 +276,7 @@ def block_attention_bench(args):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "mdm_block_attention: k_tile_ranges + k_block_attn",
-                     "visible_pairs_per_head": pairs, "algorithmic_flops_per_launch": flops,
+                     "visible_pairs_per_query_head": pairs, "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes,
                      "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
     }

@@ -383,13 +383,16 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  // blocks of one (sequence, kv head) on one XCD; heavier (later) rows first
-  const int per_xcd = gridDim.x / 8;
-  const int lb = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // Heaviest first over the whole grid: rows later in the sequence see more
+  // tiles (clean blocks are causal, masked blocks come last), so the blocks
+  // of the last row chunks of every (sequence, kv head) are dispatched
+  // first and the light ones fill the tail.
+  const int lb = blockIdx.x;
   if (lb >= a.real_blocks) return;
   const int G = a.H / a.Hkv;
-  const int bh = lb / a.nbk;
-  const int cb = a.nbk - 1 - lb % a.nbk;
+  const int n_bh = a.B * a.Hkv;
+  const int bh = lb % n_bh;
+  const int cb = a.nbk - 1 - lb / n_bh;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int n = a.n, n_rc = (n + kRowsPerWave - 1) / kRowsPerWave, n_tiles = (n + kKeyTile - 1) / kKeyTile;
   const int chunk = cb * kBaWaves + wave;
@@ -601,8 +604,7 @@ hipError_t launch_block_attention(BlockAttnArgs a, hipStream_t s) {
   const int n_rc = (a.n + kRowsPerWave - 1) / kRowsPerWave;
   a.nbk = (G * n_rc + kBaWaves - 1) / kBaWaves;
   a.real_blocks = a.B * a.Hkv * a.nbk;
-  const int grid = (a.real_blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL(k_block_attn, dim3(grid), dim3(kBaThreads), 0, s, a);
+  hipLaunchKernelGGL(k_block_attn, dim3(a.real_blocks), dim3(kBaThreads), 0, s, a);
   return hipGetLastError();
 }
 
