@@ -198,6 +198,64 @@ int32_t mdm_cache_len(const mdm_ctx* ctx);
  * MDM_E_DEVICE if any kernel met an out-of-range token id or position. */
 mdm_status mdm_device_status(mdm_ctx* ctx);
 
+/* ---- upper layers --------------------------------------------------------
+ * A model of L >= 2 attention layers without W_o, MLP or norms: layer l >= 2
+ * takes the previous layer's head outputs h_{l-1} of every query row and
+ * projects them, [q | k | v] = h_{l-1} W_l^T, with q and k RoPE'd at the row's
+ * position and all three rounded to bf16.  Each layer has its own cache; the
+ * rows decoded at step k-1 enter every layer's cache at step k, which is what
+ * makes the cache reuse of page 1 (overall framework: cached representations
+ * are not polluted by the masked rows) load-bearing: layer l's cached keys
+ * were computed from layer l-1 outputs of a D row, which saw only the cache.
+ * bf16 precision only.  A step with L layers:
+ *   mdm_kv_append(D); mdm_step_attention(...) -> h_1
+ *   for l = 2..L: mdm_layer_project(l, h_{l-1}, ...); mdm_layer_attention(l, ...) -> h_l
+ *   mdm_subset_logits_confidence(C rows of h_L)
+ * Prefill: mdm_kv_append(prompt); mdm_step_attention(D = prompt, n_decode = 0)
+ * -> h_1; then per upper layer mdm_layer_project(D = prompt) (and, below the
+ * top layer, mdm_layer_attention) so that every layer caches the prompt. */
+typedef struct {
+  int32_t n_layers;        /* L, 2..16                                                   */
+  const void* w_upper;     /* bf16 [L-1][(H + 2 H_kv) d][H d]: W_l of layers 2..L, rows  */
+                           /* are the q heads, then the k heads, then the v heads        */
+  void* k_cache_upper;     /* bf16 [L-1][B][H_kv][slots][d]   (layout of k_cache)        */
+  void* v_cache_upper;     /* bf16 [L-1][B][H_kv][slots/64][d][64] (layout of v_cache)   */
+  void* workspace;         /* mdm_upper_workspace_bytes() bytes, 256-byte aligned        */
+  size_t workspace_bytes;
+} mdm_upper_layers;
+
+/* Bytes of the upper layers' workspace (packed h, the projected rows, the
+ * queries and the C|R keys/values of one layer call); 0 if invalid or not bf16. */
+size_t mdm_upper_workspace_bytes(const mdm_config* cfg);
+
+/* Register the upper layers' weights, caches and workspace with ctx (caller-
+ * owned, read and written by the calls below).  Resets their cache lengths.
+ * MDM_E_UNSUPPORTED unless bf16; MDM_E_ARG for NULL, misaligned or n_layers
+ * outside 2..16; MDM_E_SHAPE for a short workspace. */
+mdm_status mdm_attach_upper_layers(mdm_ctx* ctx, const mdm_upper_layers* up);
+
+/* Layer `layer` (2..L) projection of one step's query rows.  Row r of
+ * sequence b is h_prev[b*h_batch_stride + r*H*d .. +H*d) (fp32) for r in
+ * [0, n_q), n_q = n_new_cached + n_decode + R, rows in the order D | C | R
+ * (the output layout of the attention calls; h_batch_stride 0 means n_q*H*d).
+ * Positions: D rows d_pos[b*d_stride + r], C rows c_pos[b*c_stride + j],
+ * registers seq_len + j.  The D rows' k and v are appended to the layer's
+ * cache (its length grows by n_new_cached); the C|R rows' k and v and every
+ * row's q stay in the workspace for the next mdm_layer_attention of this
+ * layer.  h is split into bf16 hi + lo for the MFMA product, so q, k, v are
+ * near-fp32 accurate before their bf16 rounding.  MDM_E_CAPACITY when the
+ * layer's cache would pass seq_len or n_q > seq_len + R; MDM_E_ARG for
+ * n_decode > max_decode and the usual pointer/stride errors. */
+mdm_status mdm_layer_project(mdm_ctx* ctx, int32_t layer, const float* h_prev, int64_t h_batch_stride,
+                             const int32_t* d_pos, int64_t d_stride, int32_t n_new_cached,
+                             const int32_t* c_pos, int64_t c_stride, int32_t n_decode);
+
+/* Layer `layer` attention over its cache and the rows of its latest
+ * projection (which must have had the same n_new_cached and n_decode):
+ * the step-causal mask of mdm_step_attention, output
+ * out[B][n_new_cached + n_decode + R][H*d] (fp32). */
+mdm_status mdm_layer_attention(mdm_ctx* ctx, int32_t layer, int32_t n_new_cached, int32_t n_decode, float* out);
+
 /* ---- training-form attention under the block mask -----------------------
  * Page 1 (papernotes.org), key design 3; page 3 (paperlayer.ai), sections 3.3
  * and 7.3: training reproduces the incremental cache in one parallel forward.

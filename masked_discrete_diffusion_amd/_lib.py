@@ -58,6 +58,17 @@ class MdmBuffers(ctypes.Structure):
     ]
 
 
+class MdmUpperLayers(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32),
+        ("w_upper", ctypes.c_void_p),
+        ("k_cache_upper", ctypes.c_void_p),
+        ("v_cache_upper", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class MdmBlockAttnShape(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -89,6 +100,10 @@ _SIGS = {
     "mdm_sparse_step_destroy": (None, [_P]),
     "mdm_last_error": (ctypes.c_char_p, [_P]),
     "mdm_status_string": (ctypes.c_char_p, [_I32]),
+    "mdm_upper_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MdmConfig)]),
+    "mdm_attach_upper_layers": (_I32, [_P, ctypes.POINTER(MdmUpperLayers)]),
+    "mdm_layer_project": (_I32, [_P, _I32, _P, _I64, _P, _I64, _I32, _P, _I64, _I32]),
+    "mdm_layer_attention": (_I32, [_P, _I32, _I32, _I32, _P]),
     "mdm_block_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MdmBlockAttnShape)]),
     "mdm_block_attention": (_I32, [ctypes.POINTER(MdmBlockAttnShape), _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]),
@@ -204,3 +219,21 @@ def mdm_block_attention(shape: MdmBlockAttnShape, q, k, v, blocks, n_clean_block
     _check(load().mdm_block_attention(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(blocks),
                                       _ptr(n_clean_blocks), _ptr(out), _ptr(workspace), workspace_bytes,
                                       _ptr(stream)))
+
+
+def mdm_upper_workspace_bytes(cfg: MdmConfig) -> int:
+    return load().mdm_upper_workspace_bytes(ctypes.byref(cfg))
+
+
+def mdm_attach_upper_layers(ctx, up: MdmUpperLayers):
+    _check(load().mdm_attach_upper_layers(ctx, ctypes.byref(up)), ctx)
+
+
+def mdm_layer_project(ctx, layer: int, h_prev, h_batch_stride: int, d_pos, d_stride: int, n_new_cached: int,
+                      c_pos, c_stride: int, n_decode: int):
+    _check(load().mdm_layer_project(ctx, layer, _ptr(h_prev), h_batch_stride, _ptr(d_pos), d_stride, n_new_cached,
+                                    _ptr(c_pos), c_stride, n_decode), ctx)
+
+
+def mdm_layer_attention(ctx, layer: int, n_new_cached: int, n_decode: int, out):
+    _check(load().mdm_layer_attention(ctx, layer, n_new_cached, n_decode, _ptr(out)), ctx)

@@ -105,6 +105,38 @@ Layout layout_of(const mdm_config* c) {
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxLayers = 16;
+
+// Workspace of the upper layers (one region, reused by every layer in turn).
+struct UpperLayout {
+  size_t hhi, hlo, z, qbuf, tk, tvt, total;
+  int m_cap, n_pad, q_rows, t_pad;
+};
+
+UpperLayout upper_layout_of(const mdm_config* c) {
+  UpperLayout U{};
+  const int hidden = c->n_heads * c->head_dim;
+  const int n_proj = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  U.q_rows = c->seq_len + c->n_registers;                  // rows of one call: the prompt at most, + R
+  U.m_cap = (int)align_up((size_t)c->batch * U.q_rows, 128);
+  U.n_pad = (int)align_up((size_t)n_proj, kVocabTile);
+  U.t_pad = (int)align_up((size_t)c->max_decode + c->n_registers, kKeyTile);
+  size_t off = 0;
+  U.hhi = off; off = align_up(off + (size_t)U.m_cap * hidden * 2, kAlign);
+  U.hlo = off; off = align_up(off + (size_t)U.m_cap * hidden * 2, kAlign);
+  U.z = off; off = align_up(off + (size_t)U.m_cap * U.n_pad * 4, kAlign);
+  U.qbuf = off; off = align_up(off + (size_t)c->batch * c->n_heads * U.q_rows * c->head_dim * 2, kAlign);
+  const size_t tb = (size_t)c->batch * c->n_kv_heads * U.t_pad * c->head_dim * 2;
+  U.tk = off; off = align_up(off + tb, kAlign);
+  U.tvt = off; off = align_up(off + tb, kAlign);
+  U.total = off;
+  return U;
+}
+
+}  // namespace
+
 struct mdm_ctx {
   mdm_config cfg;
   mdm_buffers buf;
@@ -114,7 +146,15 @@ struct mdm_ctx {
   int len;
   int q_rows;     // rows of the latest append whose queries are in the workspace, or -1
   std::string err;
+  // upper layers (mdm_attach_upper_layers)
+  bool has_upper = false;
+  mdm_upper_layers up{};
+  UpperLayout U{};
+  int len_up[kMaxLayers + 1] = {};
+  int proj_nd[kMaxLayers + 1] = {};     // rows of the layer's latest projection (D, C), -1 if none
+  int proj_nc[kMaxLayers + 1] = {};
   char* ws() const { return static_cast<char*>(buf.workspace); }
+  char* uws() const { return static_cast<char*>(up.workspace); }
 };
 
 namespace {
@@ -186,6 +226,7 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
   ctx->L = L;
   ctx->len = 0;
   ctx->q_rows = -1;
+  for (int l = 0; l <= kMaxLayers; ++l) ctx->proj_nd[l] = ctx->proj_nc[l] = -1;
   Geometry& g = ctx->g;
   g.B = cfg->batch; g.H = cfg->n_heads; g.Hkv = cfg->n_kv_heads; g.D = cfg->head_dim; g.V = cfg->vocab;
   g.seq_len = cfg->seq_len; g.R = cfg->n_registers; g.slots = (int)slots_of(cfg);
@@ -377,7 +418,132 @@ mdm_status mdm_sparse_step_reset(mdm_ctx* ctx) {
   if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
   ctx->len = 0;
   ctx->q_rows = -1;
+  for (int l = 0; l <= kMaxLayers; ++l) {
+    ctx->len_up[l] = 0;
+    ctx->proj_nd[l] = ctx->proj_nc[l] = -1;
+  }
   return MDM_OK;
+}
+
+size_t mdm_upper_workspace_bytes(const mdm_config* cfg) {
+  if (!config_ok(cfg, nullptr) || cfg->precision != MDM_BF16) return 0;
+  return upper_layout_of(cfg).total;
+}
+
+mdm_status mdm_attach_upper_layers(mdm_ctx* ctx, const mdm_upper_layers* up) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (!up) return fail(ctx, MDM_E_ARG, "upper layers are NULL");
+  if (ctx->cfg.precision != MDM_BF16) return fail(ctx, MDM_E_UNSUPPORTED, "upper layers need the bf16 precision");
+  if (up->n_layers < 2 || up->n_layers > kMaxLayers)
+    return fail(ctx, MDM_E_ARG, "n_layers %d out of range 2..%d", up->n_layers, kMaxLayers);
+  if (!up->w_upper || !up->k_cache_upper || !up->v_cache_upper || !up->workspace)
+    return fail(ctx, MDM_E_ARG, "a required upper-layer pointer is NULL");
+  if (((uintptr_t)up->w_upper | (uintptr_t)up->k_cache_upper | (uintptr_t)up->v_cache_upper) % 16)
+    return fail(ctx, MDM_E_ARG, "upper-layer weights and caches must be 16-byte aligned");
+  if ((uintptr_t)up->workspace % kAlign) return fail(ctx, MDM_E_ARG, "upper workspace must be 256-byte aligned");
+  const UpperLayout U = upper_layout_of(&ctx->cfg);
+  if (up->workspace_bytes < U.total)
+    return fail(ctx, MDM_E_SHAPE, "upper workspace has %zu bytes, needs %zu", up->workspace_bytes, U.total);
+  ctx->up = *up;
+  ctx->U = U;
+  ctx->has_upper = true;
+  for (int l = 0; l <= kMaxLayers; ++l) {
+    ctx->len_up[l] = 0;
+    ctx->proj_nd[l] = ctx->proj_nc[l] = -1;
+  }
+  return MDM_OK;
+}
+
+namespace {
+size_t upper_cache_elems(const mdm_ctx* ctx) {
+  return (size_t)ctx->cfg.batch * ctx->cfg.n_kv_heads * ctx->g.slots * ctx->cfg.head_dim;
+}
+mdm_status upper_layer_ok(mdm_ctx* ctx, int32_t layer) {
+  if (!ctx->has_upper) return fail(ctx, MDM_E_ARG, "no upper layers attached");
+  if (layer < 2 || layer > ctx->up.n_layers)
+    return fail(ctx, MDM_E_ARG, "layer %d out of range 2..%d", layer, ctx->up.n_layers);
+  return MDM_OK;
+}
+}  // namespace
+
+mdm_status mdm_layer_project(mdm_ctx* ctx, int32_t layer, const float* h_prev, int64_t h_batch_stride,
+                             const int32_t* d_pos, int64_t d_stride, int32_t n_new_cached, const int32_t* c_pos,
+                             int64_t c_stride, int32_t n_decode) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  mdm_status st = upper_layer_ok(ctx, layer);
+  if (st != MDM_OK) return st;
+  if (!h_prev) return fail(ctx, MDM_E_ARG, "h_prev is NULL");
+  if (n_new_cached < 0 || n_decode < 0) return fail(ctx, MDM_E_ARG, "row counts must be >= 0");
+  if (n_new_cached > 0 && !d_pos) return fail(ctx, MDM_E_ARG, "d_pos is NULL");
+  if (n_decode > 0 && !c_pos) return fail(ctx, MDM_E_ARG, "c_pos is NULL");
+  if (n_decode > ctx->cfg.max_decode)
+    return fail(ctx, MDM_E_ARG, "n_decode %d exceeds max_decode %d", n_decode, ctx->cfg.max_decode);
+  if (d_stride == 0) d_stride = n_new_cached;
+  if (c_stride == 0) c_stride = n_decode;
+  if (d_stride < n_new_cached || c_stride < n_decode) return fail(ctx, MDM_E_ARG, "stride smaller than row count");
+  const int n_q = n_new_cached + n_decode + ctx->cfg.n_registers;
+  const int hidden = ctx->g.hidden;
+  if (h_batch_stride == 0) h_batch_stride = (int64_t)n_q * hidden;
+  if (h_batch_stride < (int64_t)n_q * hidden) return fail(ctx, MDM_E_ARG, "h_batch_stride smaller than the rows");
+  if ((uintptr_t)h_prev % 16 || h_batch_stride % 4) return fail(ctx, MDM_E_ARG, "h rows must be 16-byte aligned");
+  if (n_q > ctx->U.q_rows) return fail(ctx, MDM_E_CAPACITY, "%d rows exceed seq_len + R", n_q);
+  if ((int64_t)ctx->len_up[layer] + n_new_cached > ctx->cfg.seq_len)
+    return fail(ctx, MDM_E_CAPACITY, "layer %d cache length %d + %d exceeds seq_len %d", layer, ctx->len_up[layer],
+                n_new_cached, ctx->cfg.seq_len);
+  if (n_q == 0) return MDM_OK;
+  const UpperLayout& U = ctx->U;
+  const size_t w_elems = (size_t)(ctx->cfg.n_heads + 2 * ctx->cfg.n_kv_heads) * ctx->cfg.head_dim * hidden;
+  ProjArgs p{};
+  p.w = static_cast<const uint16_t*>(ctx->up.w_upper) + (size_t)(layer - 2) * w_elems;
+  p.h = h_prev;
+  p.h_stride = h_batch_stride;
+  p.n_d = n_new_cached; p.n_c = n_decode; p.n_q = n_q;
+  p.d_pos = d_pos; p.d_stride = d_stride; p.c_pos = c_pos; p.c_stride = c_stride;
+  p.hhi = reinterpret_cast<uint16_t*>(ctx->uws() + U.hhi);
+  p.hlo = reinterpret_cast<uint16_t*>(ctx->uws() + U.hlo);
+  p.z = reinterpret_cast<float*>(ctx->uws() + U.z);
+  p.n_pad = U.n_pad;
+  p.rope_cos = rope_cos(ctx); p.rope_sin = rope_sin(ctx);
+  p.qbuf = ctx->uws() + U.qbuf; p.qbuf_rows = U.q_rows;
+  p.kc = static_cast<uint16_t*>(ctx->up.k_cache_upper) + (size_t)(layer - 2) * upper_cache_elems(ctx);
+  p.vc = static_cast<uint16_t*>(ctx->up.v_cache_upper) + (size_t)(layer - 2) * upper_cache_elems(ctx);
+  p.slot0 = ctx->len_up[layer];
+  p.tk = ctx->uws() + U.tk; p.tvt = ctx->uws() + U.tvt; p.t_pad = U.t_pad;
+  p.err = err_word(ctx);
+  st = hip_check(ctx, launch_project(ctx->g, p, ctx->stream), "projection launch");
+  if (st != MDM_OK) return st;
+  ctx->len_up[layer] += n_new_cached;
+  ctx->proj_nd[layer] = n_new_cached;
+  ctx->proj_nc[layer] = n_decode;
+  return MDM_OK;
+}
+
+mdm_status mdm_layer_attention(mdm_ctx* ctx, int32_t layer, int32_t n_new_cached, int32_t n_decode, float* out) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  mdm_status st = upper_layer_ok(ctx, layer);
+  if (st != MDM_OK) return st;
+  if (!out) return fail(ctx, MDM_E_ARG, "out is NULL");
+  if (ctx->proj_nd[layer] != n_new_cached || ctx->proj_nc[layer] != n_decode)
+    return fail(ctx, MDM_E_ARG, "layer %d: the latest projection had %d new and %d decoded rows, not %d and %d",
+                layer, ctx->proj_nd[layer], ctx->proj_nc[layer], n_new_cached, n_decode);
+  const int n_r = ctx->cfg.n_registers;
+  if (n_new_cached + n_decode + n_r == 0) return MDM_OK;
+  AttnArgs a{};
+  a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
+  a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
+  a.qtab = ctx->ws() + ctx->L.qtab; a.qtab_rows = ctx->L.ktab_rows;
+  a.qbuf = ctx->uws() + ctx->U.qbuf; a.qbuf_rows = ctx->U.q_rows;
+  a.mvt = ctx->ws() + ctx->L.mvt; a.rvt = ctx->ws() + ctx->L.rvt; a.r_pad = ctx->U.t_pad;
+  a.part_o = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_o);
+  a.part_ml = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_ml);
+  a.kc = static_cast<uint16_t*>(ctx->up.k_cache_upper) + (size_t)(layer - 2) * upper_cache_elems(ctx);
+  a.vc = static_cast<uint16_t*>(ctx->up.v_cache_upper) + (size_t)(layer - 2) * upper_cache_elems(ctx);
+  a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
+  a.out = out; a.err = err_word(ctx);
+  // C and R rows see the same keys: one transient segment of n_decode + R keys
+  a.n_d = n_new_cached; a.n_c = 0; a.n_r = n_decode + n_r; a.S = ctx->len_up[layer];
+  a.tk = ctx->uws() + ctx->U.tk; a.tvt = ctx->uws() + ctx->U.tvt; a.t_pad = ctx->U.t_pad;
+  return hip_check(ctx, launch_attention(ctx->g, a, ctx->stream), "layer attention launch");
 }
 
 int32_t mdm_cache_len(const mdm_ctx* ctx) { return ctx ? ctx->len : -1; }

@@ -184,6 +184,67 @@ __global__ __launch_bounds__(256) void k_value_tables(Geometry g, const uint16_t
   rvt[i] = j < g.R ? tv[(int64_t)(g.V + 1 + j) * kvd + col] : (uint16_t)0;
 }
 
+// Upper layers: the projected rows z [M][n_pad] (fp32, row m = (b, r) with
+// r < n_q) become RoPE'd bf16 queries and keys and bf16 values, scattered to
+// where the layer's attention reads them (see ProjArgs).  Thread: 8
+// consecutive features of one row (a 16-byte unit of the output).
+__global__ __launch_bounds__(256) void k_rope_scatter(Geometry g, ProjArgs a) {
+  const int m = blockIdx.y;
+  const int b = m / a.n_q, r = m % a.n_q;
+  const int unit = blockIdx.x * blockDim.x + threadIdx.x;
+  const int D = g.D, hd = g.H * g.D, kd = g.Hkv * g.D;
+  if (unit * 8 >= hd + 2 * kd) return;
+  const int n0 = unit * 8;
+  int pos;
+  if (r < a.n_d) pos = a.d_pos[(int64_t)b * a.d_stride + r];
+  else if (r < a.n_d + a.n_c) pos = a.c_pos[(int64_t)b * a.c_stride + (r - a.n_d)];
+  else pos = g.seq_len + (r - a.n_d - a.n_c);
+  if (pos < 0 || pos >= g.max_pos) { flag_error(a.err, kErrPos); pos = 0; }
+  const float* zr = a.z + (int64_t)m * a.n_pad + n0;
+  const floatx4 x0 = reinterpret_cast<const floatx4*>(zr)[0];
+  const floatx4 x1 = reinterpret_cast<const floatx4*>(zr)[1];
+  const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  u16x8 y;
+  if (n0 < hd + kd) {
+    const int j = (n0 < hd ? n0 : n0 - hd) % D;            // first dim (even): pairs j/2 .. j/2 + 3
+    const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + j / 2;
+    const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + j / 2;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      double r0, r1;
+      rope_pair(x[2 * p], x[2 * p + 1], cs[p], sn[p], r0, r1);
+      y[2 * p] = f64_to_bf16(r0);
+      y[2 * p + 1] = f64_to_bf16(r1);
+    }
+    if (n0 < hd) {
+      const int h = n0 / D;
+      *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(a.qbuf) + (((int64_t)b * g.H + h) * a.qbuf_rows + r) * D + j) = y;
+      return;
+    }
+    const int kvh = (n0 - hd) / D;
+    uint16_t* dst = r < a.n_d
+        ? static_cast<uint16_t*>(a.kc) + (((int64_t)b * g.Hkv + kvh) * g.slots + a.slot0 + r) * D + j
+        : static_cast<uint16_t*>(a.tk) + (((int64_t)b * g.Hkv + kvh) * a.t_pad + (r - a.n_d)) * D + j;
+    *reinterpret_cast<u16x8*>(dst) = y;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = f32_to_bf16(x[e]);
+  const int kvh = (n0 - hd - kd) / D, j = (n0 - hd - kd) % D;
+  if (r < a.n_d) {
+    const int slot = a.slot0 + r;
+    uint16_t* dst = static_cast<uint16_t*>(a.vc) +
+                    ((((int64_t)b * g.Hkv + kvh) * (g.slots / kKeyTile) + slot / kKeyTile) * D + j) * kKeyTile +
+                    slot % kKeyTile;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e * kKeyTile] = y[e];
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(a.tvt) + (((int64_t)b * g.Hkv + kvh) * D + j) * a.t_pad + (r - a.n_d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[(int64_t)e * a.t_pad] = y[e];
+  }
+}
+
 __global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -210,6 +271,12 @@ hipError_t launch_value_tables(const Geometry& g, const void* tv, void* mvt, voi
   hipLaunchKernelGGL(k_value_tables, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
                      static_cast<const uint16_t*>(tv), static_cast<uint16_t*>(mvt), static_cast<uint16_t*>(rvt),
                      r_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_scatter(const Geometry& g, const ProjArgs& a, int M, hipStream_t s) {
+  const int units = (g.H + 2 * g.Hkv) * g.D / 8;
+  hipLaunchKernelGGL(k_rope_scatter, dim3((units + 255) / 256, M), dim3(256), 0, s, g, a);
   return hipGetLastError();
 }
 

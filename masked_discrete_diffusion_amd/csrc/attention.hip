@@ -172,6 +172,7 @@ struct KvSrc {
   const uint16_t* mvt;    // mask-token value units [D][8]
   const uint16_t* rvt;    // register values [D][r_pad]
   const int* kidx;        // LDS: key-table row of each C key
+  int k2row0;             // key-table row of the first segment-2 key (seq_len; 0 in transient mode)
 };
 
 // Byte offsets, per lane, of this wavefront's DMA units for a cache tile,
@@ -212,7 +213,7 @@ __device__ inline void tile_dma(const AttnArgs& a, const Geometry& g, const KvSr
   int ln = lane;
   asm volatile("" : "+v"(ln));
   const uint16_t* kbase = tr.seg == 0 ? src.kc + (int64_t)tr.base * D
-                                      : src.ktab + (int64_t)(g.seq_len + tr.base) * D;   // seg 2 (seg 1 below)
+                                      : src.ktab + (int64_t)(src.k2row0 + tr.base) * D;   // seg 2 (seg 1 below)
   const uint16_t* vbase = src.vc + (int64_t)tr.base * D;                               // seg 0: V^T tile
 #pragma unroll
   for (int i = 0; i < T::LPW; ++i) {
@@ -662,6 +663,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   src.mvt = static_cast<const uint16_t*>(a.mvt) + (int64_t)kvh * D * 8;
   src.rvt = static_cast<const uint16_t*>(a.rvt) + (int64_t)kvh * D * a.r_pad;
   src.kidx = kidx;
+  src.k2row0 = g.seq_len;
+  if (a.tk) {
+    // upper layer: the C|R keys of this step, per (sequence, kv head)
+    src.ktab = static_cast<const uint16_t*>(a.tk) + ((int64_t)b * g.Hkv + kvh) * a.t_pad * D;
+    src.rvt = static_cast<const uint16_t*>(a.tvt) + ((int64_t)b * g.Hkv + kvh) * D * a.t_pad;
+    src.k2row0 = 0;
+  }
 
   // stream order: full tiles, then the segments' partial last tiles
   TileOrder ord;
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
       if (row < a.n_d && !a.qbuf) {
         rotate = true;
         ri = query_row(g, a, b, row);
-      } else if (row < a.n_d) {
+      } else if (row < a.n_d || a.tk) {
         qrow = static_cast<const uint16_t*>(a.qbuf) + (((int64_t)b * g.H + h) * a.qbuf_rows + row) * D;
       } else {
         int pos;

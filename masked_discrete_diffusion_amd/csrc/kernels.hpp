@@ -82,6 +82,13 @@ struct AttnArgs {
   int* err;
   int n_d, n_c, n_r;   // query rows: D | C | R
   int S;               // cache length including D
+  // Upper-layer (transient) mode, bf16 only: queries of every row from qbuf;
+  // the keys/values of the C|R rows from tk [B][H_kv][t_pad][d] and
+  // tvt [B][H_kv][d][t_pad] (the launcher passes them as one segment of
+  // n_c + n_r keys after the cache).
+  const void* tk;
+  const void* tvt;
+  int t_pad;
 };
 hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s);
 
@@ -100,8 +107,44 @@ struct VocabArgs {
   float* conf;              // [M]
   int32_t* token;           // [M]
   int m_pad;
+  int emit;                 // nonzero: the screen writes the raw product to zpart [M][v_pad] and stops
 };
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
+
+// Upper layers: y = h_prev W^T for every query row (h_prev fp32, split into
+// bf16 hi + lo; W bf16 [N][hidden] with N = (H + 2 H_kv) d, rows q | k | v),
+// then RoPE at the row's position and scatter: q of every row to qbuf
+// [B][H][qbuf_rows][d]; k and v of the D rows into the layer's cache at slot
+// slot0 + r (keys [B][H_kv][slots][d], values transposed in 64-slot tiles);
+// k and v of the C|R rows (index j = r - n_d) to tk [B][H_kv][t_pad][d] and
+// tvt [B][H_kv][d][t_pad].
+struct ProjArgs {
+  const void* w;
+  const float* h;
+  int64_t h_stride;
+  int n_d, n_c, n_q;        // n_q = n_d + n_c + R rows per sequence
+  const int32_t* d_pos;
+  int64_t d_stride;
+  const int32_t* c_pos;
+  int64_t c_stride;
+  uint16_t* hhi;            // [m_pad][hidden]
+  uint16_t* hlo;
+  float* z;                 // [m_pad][n_pad]
+  int n_pad;                // N rounded up to the vocab tile
+  const float* rope_cos;
+  const float* rope_sin;
+  void* qbuf;
+  int qbuf_rows;
+  void* kc;
+  void* vc;
+  int slot0;
+  void* tk;
+  void* tvt;
+  int t_pad;
+  int* err;
+};
+hipError_t launch_project(const Geometry& g, const ProjArgs& a, hipStream_t s);
+hipError_t launch_rope_scatter(const Geometry& g, const ProjArgs& a, int M, hipStream_t s);
 
 struct SelectArgs {
   const int32_t* cand_pos;

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   }
 
   // lane holds z for row m0 + 32(rb0 + rb) + l32 and vocab v0 + 32wv + 8jj + 4half + ii
-  if (n_split > 1) {
+  if (n_split > 1 || a.emit) {
     float* zp = a.zpart;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
         }
       }
     }
-    return;                                   // k_screen_reduce folds the splits
+    return;                                   // k_screen_reduce folds the splits (or the caller reads z)
   }
 
   __syncthreads();                            // every wavefront is done with the ring
@@ -866,6 +866,39 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
   return hipGetLastError();
+}
+
+hipError_t launch_project(const Geometry& g, const ProjArgs& p, hipStream_t s) {
+  const int M = g.B * p.n_q;
+  if (M <= 0) return hipSuccess;
+  // the screen as a plain product: "vocabulary" = the N projection rows
+  Geometry gp = g;
+  gp.V = (g.H + 2 * g.Hkv) * g.D;
+  VocabArgs va{};
+  va.w = p.w;
+  va.h = p.h;
+  va.h_stride = p.h_stride;
+  va.n_c = p.n_q;
+  va.hhi = p.hhi;
+  va.hlo = p.hlo;
+  va.zpart = p.z;
+  va.v_pad = p.n_pad;
+  va.emit = 1;
+  const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  const int mt_rows = 32 * rb;
+  const int m_tiles = (M + mt_rows - 1) / mt_rows;
+  va.m_pad = m_tiles * mt_rows;
+  const int64_t n8 = (int64_t)va.m_pad * g.hidden / 8;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gp, va, M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(p.n_pad / kVocabTile, m_tiles, 1);
+  if (rb == 1) hipLaunchKernelGGL((k_screen_bf16<1, 1, true>), grid, dim3(ScreenStage<1, 1, true>::THREADS), 0, s, gp, va, M, 1);
+  else if (rb == 2) hipLaunchKernelGGL((k_screen_bf16<2, 2, true>), grid, dim3(ScreenStage<2, 2, true>::THREADS), 0, s, gp, va, M, 1);
+  else hipLaunchKernelGGL((k_screen_bf16<4, 2, true>), grid, dim3(ScreenStage<4, 2, true>::THREADS), 0, s, gp, va, M, 1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rope_scatter(g, p, M, s);
 }
 
 }  // namespace mdm

@@ -7,6 +7,10 @@ Per sampling step k (page 3, section 3.2):
     mdm_subset_logits_confidence(h of C_k)  logits, confidence and argmax for C_k only
     mdm_unmask_select(C_k)                  unmask (pre-generated order or confidence)
 
+With upper layers (layer l >= 2 projects layer l-1's outputs), every step
+runs mdm_layer_project + mdm_layer_attention per upper layer after the first
+attention, and the logits read the last layer's output.
+
 The prompt is appended before step 1.  PyTorch only provides device memory
 and streams; every step of the path runs in the library's kernels.  All
 shapes are fixed by the workload's plan, so one whole generation can be
@@ -122,8 +126,27 @@ class SparseStepRunner:
         self.d_tok = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
         self.d_pos = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
         self.rem = [torch.zeros(B * max_decode, **i32) for _ in range(2)]
-        self.n_q_max = max(p.n_d + p.n_c for p in self.plan) + cfg.n_registers
-        self.out = torch.zeros(B * self.n_q_max * cfg.hidden, dtype=torch.float32, device=dev)
+        self.layers = cfg.layers
+        rows = max(p.n_d + p.n_c for p in self.plan)
+        if self.layers > 1:
+            rows = max(rows, cfg.prompt_len)          # the prefill's first-layer rows feed layer 2
+        self.n_q_max = rows + cfg.n_registers
+        # layer outputs: layer l writes outs[(l - 1) % 2]; the logits read the last one
+        n_out = 1 if self.layers == 1 else 2
+        self.outs = [torch.zeros(B * self.n_q_max * cfg.hidden, dtype=torch.float32, device=dev)
+                     for _ in range(n_out)]
+        self.out = self.outs[(self.layers - 1) % n_out]
+        if self.layers > 1:
+            w = np.stack(wl.layer_w)                  # [L-1][(H + 2 H_kv) d][H d] bf16 bits
+            self.w_upper = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dev)
+            self.k_upper = torch.zeros((self.layers - 1) * kv_elems, dtype=edt, device=dev)
+            self.v_upper = torch.zeros((self.layers - 1) * kv_elems, dtype=edt, device=dev)
+            self.uws_bytes = L.mdm_upper_workspace_bytes(self.mc)
+            self.upper_ws = torch.zeros(self.uws_bytes // 4 + 64, dtype=torch.int32, device=dev)
+            self.up = L.MdmUpperLayers(n_layers=self.layers, w_upper=self.w_upper.data_ptr(),
+                                       k_cache_upper=self.k_upper.data_ptr(), v_cache_upper=self.v_upper.data_ptr(),
+                                       workspace=self.upper_ws.data_ptr(), workspace_bytes=self.uws_bytes)
+            L.mdm_attach_upper_layers(self.ctx, self.up)
         self.conf = torch.zeros(B * max_decode, dtype=torch.float32, device=dev)
         self.token = torch.zeros(B * max_decode, **i32)
         seq0 = np.full((B, cfg.seq_len), cfg.vocab, dtype=np.int32)
@@ -156,8 +179,22 @@ class SparseStepRunner:
         return self.rem[st.c_off].data_ptr(), st.n_c
 
     def prefill(self):
+        cfg = self.cfg
+        P = cfg.prompt_len
         L.mdm_sparse_step_reset(self.ctx)
-        L.mdm_kv_append(self.ctx, self.prompt_tok, self.prompt_pos, self.cfg.prompt_len, self.cfg.prompt_len)
+        L.mdm_kv_append(self.ctx, self.prompt_tok, self.prompt_pos, P, P)
+        if self.layers > 1:
+            # every upper layer caches the prompt: the first layer's outputs of
+            # the prompt rows (they see the prompt only) feed layer 2, and so on
+            L.mdm_step_attention(self.ctx, self.prompt_tok, self.prompt_pos, P, P, None, 0, 0, self.outs[0])
+            self._upper(P, self.prompt_pos, P, None, 0, 0, prefill=True)
+
+    def _upper(self, n_d, d_pos, d_stride, c_ptr, c_stride, n_c, prefill=False):
+        for layer in range(2, self.layers + 1):
+            src, dst = self.outs[(layer - 2) % 2], self.outs[(layer - 1) % 2]
+            L.mdm_layer_project(self.ctx, layer, src, 0, d_pos, d_stride, n_d, c_ptr, c_stride, n_c)
+            if not (prefill and layer == self.layers):
+                L.mdm_layer_attention(self.ctx, layer, n_d, n_c, dst)
 
     def step(self, k: int, logits: Optional[torch.Tensor] = None):
         st = self.plan[k]
@@ -167,7 +204,9 @@ class SparseStepRunner:
             L.mdm_kv_append(ctx, self.d_tok[st.d_buf], self.d_pos[st.d_buf], st.n_d, st.n_d)
         c_ptr, c_stride = self._c_src(st)
         L.mdm_step_attention(ctx, self.d_tok[st.d_buf], self.d_pos[st.d_buf], st.n_d, st.n_d,
-                             c_ptr, c_stride, st.n_c, self.out)
+                             c_ptr, c_stride, st.n_c, self.outs[0])
+        if self.layers > 1:
+            self._upper(st.n_d, self.d_pos[st.d_buf], st.n_d, c_ptr, c_stride, st.n_c)
         n_q = st.n_d + st.n_c + cfg.n_registers
         h_ptr = self.out.data_ptr() + 4 * st.n_d * cfg.hidden
         L.mdm_subset_logits_confidence(ctx, h_ptr, n_q * cfg.hidden, st.n_c, self.conf, self.token, logits)

@@ -38,6 +38,8 @@ class Config:
     infill_spans: int = 0      # > 0: the generated positions are this many masked spans
                                # placed inside the sequence (text infilling), the clean
                                # prompt tokens fill the other positions
+    layers: int = 1            # attention layers; layer l > 1 projects the previous
+                               # layer's head outputs with its own weights (bf16 only)
     rope_theta: float = 10000.0
     description: str = ""
 
@@ -58,6 +60,11 @@ class Config:
     @property
     def mask_id(self) -> int:
         return self.vocab
+
+    @property
+    def proj_rows(self) -> int:
+        """Output features of an upper layer's projection: q heads, k heads, v heads."""
+        return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
 
     @property
     def group(self) -> int:

@@ -109,6 +109,7 @@ class Workload:
     semi_ar: list = field(default_factory=list)   # [SemiARStep] for semi-AR text
     prompt_pos: Optional[np.ndarray] = None       # int32 [B][P] positions of the prompt tokens
     gen_pos: Optional[np.ndarray] = None          # int32 [B][L] masked positions, ascending
+    layer_w: list = field(default_factory=list)   # upper layers' projections [proj_rows][hidden] bf16
 
     def __post_init__(self):
         cfg = self.cfg
@@ -124,7 +125,7 @@ class Workload:
 
 def _seed_streams(cfg: Config):
     ss = np.random.SeedSequence([SEED_ROOT, cfg.index])
-    kids = ss.spawn(8)      # the 8th stream (text variants) leaves the first 7 unchanged
+    kids = ss.spawn(9)      # later streams (text variants, upper layers) leave the first ones unchanged
     return [np.random.default_rng(k) for k in kids]
 
 
@@ -197,7 +198,7 @@ def make_workload(cfg: Config, tables: bool = True) -> Workload:
     ids, counts and orders are still drawn from their own streams, so they do
     not depend on this flag.
     """
-    r_tq, r_tk, r_tv, r_w, r_prompt, r_order, r_emb, r_text = _seed_streams(cfg)
+    r_tq, r_tk, r_tv, r_w, r_prompt, r_order, r_emb, r_text, r_layers = _seed_streams(cfg)
     rows, hd, kvd = cfg.table_rows, cfg.hidden, cfg.n_kv_heads * cfg.head_dim
     if not tables:
         dt = np.uint16 if cfg.precision == "bf16" else np.float32
@@ -222,6 +223,22 @@ def make_workload(cfg: Config, tables: bool = True) -> Workload:
         w = (r_w.standard_normal((cfg.vocab, hd)) * std).astype(np.float32)
     else:
         raise ValueError(cfg.precision)
+
+    # upper layers: W_l [proj_rows][hidden] bf16, rows = q heads | k heads | v heads,
+    # N(0, 1) * 2 / sqrt(hidden): the head outputs of a layer are averages of
+    # O(1) values over many keys (rms ~0.3), and this gain keeps each layer's
+    # output at the first layer's scale (rms ratio 1.1-1.3 on the test shapes),
+    # so the last layer's confidences are not saturated
+    layer_w = []
+    if cfg.layers > 1:
+        if cfg.precision != "bf16":
+            raise ValueError("upper layers are defined for bf16 workloads")
+        for _ in range(cfg.layers - 1):
+            if tables:
+                x = r_layers.standard_normal((cfg.proj_rows, hd), dtype=np.float32) * np.float32(2.0 / math.sqrt(hd))
+                layer_w.append(bf16_bits_from_f32(x))
+            else:
+                layer_w.append(np.empty((0, hd), np.uint16))
 
     prompt = r_prompt.integers(0, cfg.vocab, size=(cfg.batch, cfg.prompt_len)).astype(np.int32)
 
@@ -251,4 +268,5 @@ def make_workload(cfg: Config, tables: bool = True) -> Workload:
         gen_pos = np.stack([m for _, m in pairs]).astype(np.int32)
     plan = semi_ar_plan(cfg, block_seq) if cfg.schedule == "semi_ar" else []
     return Workload(cfg=cfg, tq=tq, tk=tk, tv=tv, w_vocab=w, prompt_ids=prompt,
-                    order=order, counts=_counts(cfg), semi_ar=plan, prompt_pos=prompt_pos, gen_pos=gen_pos)
+                    order=order, counts=_counts(cfg), semi_ar=plan, prompt_pos=prompt_pos, gen_pos=gen_pos,
+                    layer_w=layer_w)

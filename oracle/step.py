@@ -12,9 +12,11 @@ same R tokens at every step.
 
 Readings (where the pages are silent):
 
-* one attention layer whose q/k/v rows are table lookups by token id (an
-  optional second layer, projections of the first layer's output, exists only
-  for the cache-consistency invariant); h = the concatenated head outputs;
+* layer 1's q/k/v rows are table lookups by token id; an optional second
+  layer projects the first layer's output (q, k, v = h1 W, no W_o, MLP or
+  norm; RoPE at the row's position; q, k and v rounded to the storage type,
+  since the cache holds what later steps read); h = the concatenated head
+  outputs of the last layer;
 * the mask token is one shared table row (id V); register r is row V+1+r;
 * registers are re-fed at every step and never cached;
 * the prompt is in the cache before step 1 and nothing enters at step 1;
@@ -66,6 +68,12 @@ class Model:
     @classmethod
     def from_workload(cls, wl, precision: Optional[str] = None, layer2=None):
         cfg = wl.cfg
+        if layer2 is None and getattr(wl, "layer_w", None):
+            if len(wl.layer_w) != 1:
+                raise ValueError("the oracle models at most two layers")
+            w2 = table_values(wl.layer_w[0])                  # [q | k | v rows][hidden]
+            hq, hk = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+            layer2 = (w2[:hq].T, w2[hq:hq + hk].T, w2[hq + hk:].T)
         return cls(n_heads=cfg.n_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
                    vocab=cfg.vocab, n_registers=cfg.n_registers, seq_len=cfg.seq_len,
                    tq=wl.tq, tk=wl.tk, tv=wl.tv, w=table_values(wl.w_vocab),
@@ -104,7 +112,8 @@ class Model:
         q = (h1 @ wq).reshape(n, h, d)
         k = (h1 @ wk).reshape(n, hk, d)
         v = (h1 @ wv).reshape(n, hk, d)
-        return self._rot(q, pos), self._rot(k, pos), v
+        # the cache holds what later steps read: v in the storage type too
+        return self._rot(q, pos), self._rot(k, pos), round_storage(v, self.precision)
 
 
 @dataclass

@@ -117,3 +117,22 @@ BA_CASES = {
     "single_head_long": lambda: ba_small(index=135, batch=1, n_heads=1, n_kv_heads=1, prompt_len=100,
                                          gen_len=1500, n_registers=20, clean_blocks=6, masked_blocks=3),
 }
+
+
+# Two attention layers (layer 2 projects layer 1's outputs; its own cache).
+def tiny_two_layer(index=103, **kw):
+    base = dict(name="tiny_two_layer", layers=2)
+    base.update(kw)
+    return tiny_bf16(index=index, **base)
+
+
+def gpu_two_layer(index=118, **kw):
+    base = dict(name="gpu_two_layer", layers=2)
+    base.update(kw)
+    return gpu_small_bf16(index=index, head_dim=128, **base)
+
+
+def gpu_two_layer_semi_ar(index=119, **kw):
+    base = dict(name="gpu_two_layer_semi_ar", layers=2, n_heads=4, n_kv_heads=2, vocab=1200)
+    base.update(kw)
+    return gpu_small_semi_ar(index=index, **base)

@@ -5,9 +5,14 @@ Bars (written here, applied element by element):
 * bf16 path: attention outputs, confidences and screened logits within
   2e-2 relative + 1e-2 absolute; fp32 path: 1e-5 relative + 1e-5 absolute;
 * a tighter diagnostic on attention outputs (max |err| / max |ref|) that a
-  mask bug would break even where the loose bar would not;
+  mask bug would break even where the loose bar would not (2e-4; 4e-3 with
+  two layers, where a layer-2 key or value computed in fp32 may round to the
+  bf16 neighbour of the oracle's float64 value: one bf16 ulp, 2^-8);
 * keys written to the cache: bit-exact (the RoPE rule rounds once from an
-  exact double).
+  exact double);
+* two layers: the logits of a row may further move by ||W_v||_1 times the
+  output bound 2^-8 max|O| (an output that moved by one bf16 ulp of a layer-2
+  value moves logit v by at most the l1 norm of vocab row v times that).
 """
 
 import numpy as np
@@ -17,13 +22,14 @@ from mdm_inputs import make_workload
 from oracle.numerics import table_values
 from oracle.step import Model, SequenceOracle, run_workload
 from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_text_infill,
-                             gpu_wide_fixed, gpu_wide_semi_ar)
+                             gpu_two_layer, gpu_two_layer_semi_ar, gpu_wide_fixed, gpu_wide_semi_ar)
 from mdm_inputs import get_config
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
 TIGHT = {"bf16": 2e-4, "fp32": 1e-5}
+TIGHT_UPPER = 2.0 ** -8
 
 
 def _say(msg):
@@ -89,28 +95,60 @@ def test_generation_matches_oracle(cfgfn):
     _check_generation(cfg, wl, run)
 
 
-def _check_generation(cfg, wl, run):
+def _check_generation(cfg, wl, run, ties=False):
+    """ties=True (upper layers): a decision of the two sides may differ only
+    where the oracle's own margin is within the tolerance (a top-1/top-2 logit
+    margin within the logits bar, or a confidence swap across the selection
+    cut within the confidence bar): both decisions are then correct at the
+    stated precision.  The generations part there, and the comparison stops."""
     steps = list(range(cfg.n_steps))
     recs, seq = run.generate_recorded(keep_o=steps, keep_logits=steps)
     run.close()
     res = run_workload(wl, keep_steps=steps)
     rtol, atol = TOL[cfg.precision]
-    accurate = cfg.schedule == "semi_ar"
+    accurate = bool(run.mc.accurate_conf)
     worst = {"o": 0.0, "conf": 0.0, "logits": 0.0}
+    parted = None
     for k, (g, r) in enumerate(zip(recs, res.records)):
         for b in range(cfg.batch):
-            assert np.array_equal(g["token"][b], r.token[b]), f"step {k} b {b}: decoded tokens differ"
             sel = r.selected[b]
-            assert np.array_equal(g["sel_pos"][b], r.c_pos[b][sel]), f"step {k} b {b}: unmask order differs"
+            same_tok = np.array_equal(g["token"][b], r.token[b])
+            same_sel = np.array_equal(g["sel_pos"][b], r.c_pos[b][sel])
+            if ties and not (same_tok and same_sel):
+                parted = parted or (k, b)
+                if not same_tok:
+                    bad = np.nonzero(g["token"][b] != r.token[b])[0]
+                    w_l1 = np.abs(table_values(wl.w_vocab)).sum(axis=1).max()
+                    z_bar = atol + rtol * np.max(np.abs(r.z)) + TIGHT_UPPER * w_l1 * np.max(np.abs(r.o[b]))
+                    assert np.all(r.margin[b][bad] <= 2 * z_bar), f"step {k} b {b}: tokens differ beyond a tie"
+                else:
+                    conf = r.conf64[b]
+                    cut_lo = np.min(conf[sel])
+                    got = np.isin(r.c_pos[b], g["sel_pos"][b])
+                    swapped = conf[got ^ np.isin(np.arange(conf.size), sel)]
+                    bar = 2 * (atol + rtol * cut_lo)
+                    assert np.all(np.abs(swapped - cut_lo) <= bar), f"step {k} b {b}: selection differs beyond a tie"
+                continue
+            assert same_tok, f"step {k} b {b}: decoded tokens differ"
+            assert same_sel, f"step {k} b {b}: unmask order differs"
             assert np.array_equal(g["sel_tok"][b], r.token[b][sel])
             worst["conf"] = max(worst["conf"], assert_close(g["conf"][b], r.conf64[b], rtol, atol, f"conf step {k}"))
             o_ref = r.o[b]
             worst["o"] = max(worst["o"], assert_close(g["o"][b], o_ref, rtol, atol, f"O step {k} b {b}"))
             rel = np.max(np.abs(g["o"][b] - o_ref)) / np.max(np.abs(o_ref))
-            assert rel <= TIGHT[cfg.precision], f"O step {k} b {b}: max err / max ref = {rel:.3g}"
+            tight = TIGHT[cfg.precision] if cfg.layers == 1 else TIGHT_UPPER
+            assert rel <= tight, f"O step {k} b {b}: max err / max ref = {rel:.3g}"
+        if parted:
+            _say(f"  the generations part at step {k} (sequence {parted[1]}) on a tie within the tolerance")
+            return
         zref = r.z if (cfg.precision == "fp32" or accurate) else r.z_mirror
+        z_atol = atol
+        if cfg.layers > 1:
+            w_l1 = np.abs(table_values(wl.w_vocab)).sum(axis=1)               # [V]
+            o_max = max(np.max(np.abs(r.o[b])) for b in range(cfg.batch))
+            z_atol = atol + w_l1[None, :] * TIGHT_UPPER * o_max
         worst["logits"] = max(worst["logits"], assert_close(
-            g["logits"].reshape(-1, cfg.vocab), zref, rtol, atol, f"logits step {k}"))
+            g["logits"].reshape(-1, cfg.vocab), zref, rtol, z_atol, f"logits step {k}"))
     assert np.array_equal(seq, res.tokens), "final sequences differ"
     _say(f"  worst abs errors: {worst}")
 
@@ -136,6 +174,20 @@ def test_text_infill_random_block_order_matches_oracle(kw):
     _say(f"text infill parity: {cfg.name} {cfg.precision}")
     wl, run = _runner(cfg)
     _check_generation(cfg, wl, run)
+
+
+@pytest.mark.parametrize("cfgfn", [gpu_two_layer, gpu_two_layer_semi_ar], ids=["fixed", "semi_ar_gqa"])
+def test_two_layer_generation_matches_oracle(cfgfn):
+    """Layer 2 projects layer 1's outputs of every query row (RoPE'd q, k and
+    v rounded to bf16), keeps its own cache of the decoded rows and attends
+    under the same step-causal mask; the decisions, unmask order and the last
+    layer's outputs must match the oracle's two-layer model."""
+    cfg = cfgfn()
+    _say(f"two-layer parity: {cfg.name}")
+    # screened with h split into hi + lo: the last layer's h carries layer-2
+    # rounding, so the screened logits are compared with the exact ones
+    wl, run = _runner(cfg, accurate_conf=True)
+    _check_generation(cfg, wl, run, ties=True)
 
 
 def test_score_jump_falls_back_to_rescaled_path():

@@ -24,7 +24,7 @@ from oracle import attention, dense, masks, rope, sparse_repr
 from oracle.logits import decide
 from oracle.numerics import round_storage, table_values
 from oracle.step import Model, SequenceOracle, run_workload
-from small_workloads import tiny_bf16, tiny_infill, tiny_semi_ar, workload
+from small_workloads import tiny_bf16, tiny_infill, tiny_semi_ar, tiny_two_layer, workload
 
 
 def _layer2(cfg, seed=7):
@@ -46,11 +46,12 @@ def _history(res, k, i):
 
 @pytest.mark.parametrize("layers,precision,cfgfn", [
     (1, "bf16", tiny_bf16), (2, "none", tiny_bf16), (1, "bf16", tiny_semi_ar), (2, "none", tiny_semi_ar),
-    (1, "bf16", tiny_infill), (2, "none", tiny_infill)])
+    (1, "bf16", tiny_infill), (2, "none", tiny_infill), (2, "bf16", tiny_two_layer)])
 def test_incremental_equals_dense_block_mask(layers, precision, cfgfn):
     cfg = cfgfn()
     wl = workload(cfg)
-    layer2 = _layer2(cfg) if layers == 2 else None
+    # a two-layer workload brings its own layer-2 weights (bf16 storage)
+    layer2 = _layer2(cfg) if layers == 2 and cfg.layers == 1 else None
     model = Model.from_workload(wl, precision=precision, layer2=layer2)
     res = run_workload(wl, keep_steps=range(cfg.n_steps), model=model)
     for k in range(cfg.n_steps):
@@ -199,3 +200,20 @@ def test_infill_generation_keeps_prompt_and_follows_block_order():
         for k, st in enumerate(wl.semi_ar):
             blk = wl.gen_pos[b][st.block * cfg.block:(st.block + 1) * cfg.block]
             assert set(res.unmask[k][i].tolist()) <= set(blk.tolist())
+
+
+def test_two_layer_workload_reaches_the_second_layer():
+    """The workload's layer-2 weights are used, and they matter: the last
+    layer's output differs from the first layer's, and the k/v of layer 2 are
+    stored in bf16 (rounding them again changes nothing)."""
+    cfg = tiny_two_layer()
+    wl = workload(cfg)
+    model = Model.from_workload(wl)
+    assert model.layer2 is not None
+    seq = SequenceOracle(model, wl.prompt_ids[0], wl.prompt_pos[0])
+    seq.prefill()
+    out = seq.forward(np.empty(0, np.int64), np.empty(0, np.int64), wl.order[0, :4])
+    assert len(out.o_layers) == 2 and not np.allclose(out.o_layers[0], out.o_layers[1])
+    from oracle.numerics import round_bf16
+    assert np.array_equal(round_bf16(seq.v[1][:seq.n]), seq.v[1][:seq.n])
+    assert np.array_equal(round_bf16(seq.k[1][:seq.n]), seq.k[1][:seq.n])
