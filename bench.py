@@ -322,6 +322,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_t2i_4k")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="attention layers (upper layers project the previous layer's outputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -359,6 +361,8 @@ def main():
     from mdm_inputs import get_config, make_workload
 
     cfg = get_config(args.workload)
+    if args.layers != 1:
+        cfg = cfg.replace(layers=args.layers)
     wl = make_workload(cfg)
     run = SparseStepRunner(wl, device="cuda:0")
     print(f"[bench] {cfg.name}: batch {cfg.batch}, {cfg.n_steps} steps, workload ready", file=sys.stderr, flush=True)
@@ -393,8 +397,12 @@ def main():
     reps = 3
     att_ms = np.zeros(n)
     log_ms = np.zeros(n)
+    proj_ms = np.zeros(n)
+    up_att_ms = np.zeros(n)
     for _ in range(reps):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        evu = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cfg.layers - 1)]
+               for _ in range(n)]
         run.prefill()
         for k, st in enumerate(run.plan):
             if st.n_d:
@@ -404,6 +412,14 @@ def main():
             L.mdm_step_attention(run.ctx, run.d_tok[st.d_buf], run.d_pos[st.d_buf], st.n_d, st.n_d,
                                  c_ptr, c_stride, st.n_c, run.out)
             ev[k][1].record(stream)
+            for li, layer in enumerate(range(2, cfg.layers + 1)):
+                src, dst = run.outs[(layer - 2) % 2], run.outs[(layer - 1) % 2]
+                evu[k][li][0].record(stream)
+                L.mdm_layer_project(run.ctx, layer, src, 0, run.d_pos[st.d_buf], st.n_d, st.n_d, c_ptr, c_stride,
+                                    st.n_c)
+                evu[k][li][1].record(stream)
+                L.mdm_layer_attention(run.ctx, layer, st.n_d, st.n_c, dst)
+                evu[k][li][2].record(stream)
             n_q = st.n_d + st.n_c + cfg.n_registers
             h_ptr = run.out.data_ptr() + 4 * st.n_d * cfg.hidden
             ev[k][2].record(stream)
@@ -415,8 +431,12 @@ def main():
         torch.cuda.synchronize()
         att_ms += np.array([e[0].elapsed_time(e[1]) for e in ev])
         log_ms += np.array([e[2].elapsed_time(e[3]) for e in ev])
+        proj_ms += np.array([sum(u[0].elapsed_time(u[1]) for u in eu) for eu in evu])
+        up_att_ms += np.array([sum(u[1].elapsed_time(u[2]) for u in eu) for eu in evu])
     att_ms /= reps
     log_ms /= reps
+    proj_ms /= reps
+    up_att_ms /= reps
     L.mdm_device_status(run.ctx)
 
     a_flops, a_bytes = attention_work(cfg, run.plan)
@@ -433,6 +453,20 @@ def main():
                 "algorithmic_bytes_per_call": round(float(a_bytes.mean()), 0),
                 "algorithmic_tflops": round(mfma_tflops, 2),
                 "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if cfg.layers > 1 and proj_ms.sum() > att_ms.sum():
+        # the upper layers' projection dominates: 2 M N hidden FLOP per call
+        # (M = B n_q query rows, N = (H + 2 H_kv) d outputs), MFMA-bound
+        n_up = cfg.layers - 1
+        p_flops = np.array([2.0 * cfg.batch * (st.n_d + st.n_c + cfg.n_registers) * cfg.proj_rows * cfg.hidden
+                            for st in run.plan]) * n_up
+        p_s = proj_ms.sum() / 1e3
+        p_tflops = p_flops.sum() / p_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(p_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "mdm_layer_project: k_pack + k_screen_bf16 (raw product, h hi + lo) + k_rope_scatter",
+                    "calls": n * n_up, "avg_call_us": round(proj_ms.mean() / n_up * 1e3, 2),
+                    "algorithmic_flops_per_call": round(float(p_flops.mean() / n_up), 0),
+                    "first_layer_attention": roofline}
     both_s = att_s + log_ms.sum() / 1e3
     step_frac = (a_flops.sum() + l_flops.sum()) / both_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
 
@@ -452,10 +486,13 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "prompt_tokens": cfg.prompt_len,
                    "image_tokens": cfg.gen_len, "registers": cfg.n_registers, "sampling_steps": cfg.n_steps,
                    "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
-                   "vocab": cfg.vocab, "schedule": cfg.schedule, "order": cfg.order, "parallelism": "none"},
+                   "vocab": cfg.vocab, "schedule": cfg.schedule, "order": cfg.order, "layers": cfg.layers,
+                   "parallelism": "none"},
         "roofline": roofline,
         "step_attn_logits_mfma_frac": round(step_frac, 4),
-        "kernel_ms_per_generation": {"attention": round(att_ms.sum(), 4), "logits": round(log_ms.sum(), 4)},
+        "kernel_ms_per_generation": {"attention": round(att_ms.sum(), 4), "logits": round(log_ms.sum(), 4),
+                                     **({"upper_projection": round(proj_ms.sum(), 4),
+                                         "upper_attention": round(up_att_ms.sum(), 4)} if cfg.layers > 1 else {})},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
