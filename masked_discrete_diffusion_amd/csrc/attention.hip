@@ -104,6 +104,7 @@ struct ChunkPlan {
   int blocks;       // chunk groups per (sequence, kv head)
   int ksplit;       // blocks sharing one chunk group's key tiles (bf16 path)
   int real_blocks;  // B * Hkv * blocks * ksplit (the grid may be padded to a multiple of 8)
+  int pair;         // bf16: chunk groups of four, wavefronts w and w + 4 split the tiles by parity
 };
 
 // Rows [base, end) of chunk ch; is_cr: a chunk of C|R rows (sees every key)
@@ -590,6 +591,125 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
   }
 }
 
+// The result of a wavefront: O = acc / l for its rows, or (key split) the
+// unscaled partial (O, reference, row sum) that k_attn_combine merges.
+template <int D>
+__device__ inline void write_result(const AttnArgs& a, const Geometry& g, const ChunkPlan& cp, const floatx16* acc,
+                                    float m_ref, float l_run, int b, int row, int h, bool rvalid, bool active,
+                                    int logical, int wave, int half, int l32) {
+  constexpr int NDB = D / 32;
+  const float l_tot = halves_sum(l_run);
+  const int n_q = a.n_d + a.n_c + a.n_r;
+  float* o = a.out + ((int64_t)b * n_q + row) * g.hidden + h * D;
+  if (cp.ksplit == 1) {
+    if (rvalid) {
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          floatx4 v;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii] * inv;
+          *reinterpret_cast<floatx4*>(o + 32 * db + 8 * jj + 4 * half) = v;
+        }
+    }
+    return;
+  }
+
+  // split: publish this block's unscaled partial
+  if (!active) return;
+  float* po = a.part_o + ((int64_t)logical * kAttnWaves + wave) * 32 * D + l32 * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      floatx4 v;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii];
+      *reinterpret_cast<floatx4*>(po + 32 * db + 8 * jj + 4 * half) = v;
+    }
+  if (half == 0) {
+    float* pml = a.part_ml + ((int64_t)logical * kAttnWaves + wave) * 64;
+    pml[2 * l32] = m_ref;
+    pml[2 * l32 + 1] = l_tot;
+  }
+}
+
+
+// Pair mode (chunk groups of four): wavefronts w and w + 4 own the same chunk
+// and take the even and the odd tiles of the block's order (parity p = w / 4).
+// A ring step covers two tiles, so the two wavefronts of a SIMD compute at the
+// same time (one in MFMA while the other is in softmax) instead of four
+// wavefronts doing all the work while four only load.  Phases per wavefront:
+//  A. pairs of full tiles it computes (fixed reference in the fast pass, the
+//     first one peeled to set it; no masking, no branch on the accumulators);
+//  B. pairs of full tiles it does not compute (ring steps only);
+//  C. the remaining tiles (an odd last full tile and the partial tiles), on
+//     the lazily rescaled path.
+// The two partial softmax states of a chunk are merged through LDS at the end.
+template <int D, bool FAST>
+__device__ inline void tile_loop_pair(const AttnArgs& a, const Geometry& g, const KvSrc& src, const TileOrder ord,
+                                      const uint32_t (&off)[AttnTile<D>::LPW], uint16_t (*ks)[AttnTile<D>::K_ELEMS],
+                                      uint16_t (*vs)[AttnTile<D>::V_ELEMS], const bf16x8* qf, floatx16* acc,
+                                      float& m_ref, float& l_run, int T0, int T1, int n_comp, int w_end, bool active,
+                                      int parity, int wave, int lane, int krow, int half, int l32, float sc,
+                                      bool& over) {
+  const int nf2 = ord.n_full / 2;                        // pairs made of two full tiles
+  const int c_a = min(nf2, (n_comp - parity + 1) / 2);   // pairs whose tile 2j + p this wavefront computes
+  auto pair_ring = [&](int j) {
+    ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, 2 * j, wave, lane);
+    if (2 * j + 1 < ord.n) ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, 2 * j + 1, wave, lane);
+  };
+  int j = 0;
+  if (FAST && c_a > 0) {
+    pair_ring(0);
+    const int cur = parity % kStages;
+    floatx16 sv = s_half<D>(ks[cur], qf, 0, krow, half);
+    floatx16 sv1 = s_half<D>(ks[cur], qf, 1, krow, half);
+    m_ref = fmaxf(half_max<false>(sv, 0, kKeyTile, half, sc), half_max<false>(sv1, 32, kKeyTile, half, sc));
+    finish_half_fixed<D>(sv, vs[cur], 0, acc, m_ref, l_run, half, l32, sc);
+    finish_half_fixed<D>(sv1, vs[cur], 1, acc, m_ref, l_run, half, l32, sc);
+    for (j = 1; j < c_a; ++j) {
+      pair_ring(j);
+      const int c = (2 * j + parity) % kStages;
+      sv = s_half<D>(ks[c], qf, 0, krow, half);
+      sv1 = s_half<D>(ks[c], qf, 1, krow, half);
+      finish_half_fixed<D>(sv, vs[c], 0, acc, m_ref, l_run, half, l32, sc);
+      finish_half_fixed<D>(sv1, vs[c], 1, acc, m_ref, l_run, half, l32, sc);
+    }
+    over = !(l_run < 0x1p50f);
+  }
+  if (!FAST) {
+    for (; j < c_a; ++j) {
+      pair_ring(j);
+      const int c = (2 * j + parity) % kStages;
+      floatx16 sv = s_half<D>(ks[c], qf, 0, krow, half);
+      finish_half<D, false>(sv, vs[c], 0, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+      sv = s_half<D>(ks[c], qf, 1, krow, half);
+      finish_half<D, false>(sv, vs[c], 1, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+    }
+  }
+  for (j = max(c_a, 0); j < nf2; ++j) pair_ring(j);
+  for (j = nf2; 2 * j < ord.n; ++j) {
+    pair_ring(j);
+    const int i = 2 * j + parity;
+    if (i >= ord.n || !active) continue;
+    // one compute path (a branch between two would merge accumulator
+    // definitions): an odd last full tile takes the masked path with all keys valid
+    const int t = ord.at(i);
+    const bool full = i < ord.n_full;
+    if (full ? i >= n_comp : t >= w_end) continue;
+    const int valid = full ? kKeyTile : tile_ref(a, T0, T1, t).valid;
+    const int c = i % kStages;
+    floatx16 sv = s_half<D>(ks[c], qf, 0, krow, half);
+    finish_half<D, true>(sv, vs[c], 0, valid, acc, m_ref, l_run, half, l32, sc);
+    sv = s_half<D>(ks[c], qf, 1, krow, half);
+    finish_half<D, true>(sv, vs[c], 1, valid, acc, m_ref, l_run, half, l32, sc);
+  }
+  if (FAST) over = over || !(l_run < 0x1p50f);
+}
+
 // Block: kAttnWaves wavefronts, each owning one 32-row chunk of one query head;
 // the chunks of a block belong to query heads of one key/value head, so a
 // K/V tile in LDS feeds every chunk of the block.  Tiles stream through a
@@ -597,7 +717,7 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
 // are in flight.  Each wavefront waits only for its own loads of tile i
 // (vmcnt counts the younger tiles' loads it may leave outstanding), then the
 // barrier makes every wavefront's part of tile i visible.
-template <int D>
+template <int D, bool PAIR>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnArgs a, ChunkPlan cp) {
   using T = AttnTile<D>;
   constexpr int NKS = D / 16;           // k-steps of the QK^T product
@@ -627,7 +747,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   const int c1 = min(G * cp.n_chunks, c0 + cp.per_block);
   bool any_cr = false;
   for (int c = c0; c < c1; ++c) any_cr |= (c % cp.n_chunks) >= cp.chunks_d;
-  const int ch = c0 + wave;
+  const int parity = PAIR ? wave / (kAttnWaves / 2) : 0;
+  const int ch = c0 + (PAIR ? wave % (kAttnWaves / 2) : wave);
   const bool active = ch < c1;
   const int h = kvh * G + (active ? ch / cp.n_chunks : 0);
   int row_base = 0, row_end = 0;
@@ -780,7 +901,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   // wavefronts 4-7 (the second wavefront of each SIMD) run half a tile
   // behind (see tile_loop).
   bool over = false;
-  if (wave >= kAttnWaves / 2)
+  if constexpr (PAIR)
+    tile_loop_pair<D, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active, parity,
+                            wave, lane, krow, half, l32, sc, over);
+  else if (wave >= kAttnWaves / 2)
     tile_loop<D, true, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active, wave,
                              lane, krow, half, l32, sc, over);
   else
@@ -788,60 +912,80 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
                               wave, lane, krow, half, l32, sc, over);
   // A score far above its row's first-tile maximum somewhere in the block:
   // stream the tiles again on the lazily rescaled path.
+  // Only the wavefronts whose own rows failed the check recompute (the others
+  // keep their result and take the ring steps only), so a row's result never
+  // depends on the keys other rows see.
+  const bool redo = __any(over);
+  bool written = false;
   if (__syncthreads_or(over ? 1 : 0)) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
-    m_ref = -1e30f;
-    l_run = 0.f;
-    for (int i = 0; i < kAhead && i < n_my; ++i)
-      tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
-    bool unused = false;
-    if (wave >= kAttnWaves / 2)
-      tile_loop<D, true, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
-                                wave, lane, krow, half, l32, sc, unused);
-    else
-      tile_loop<D, false, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
-                                 wave, lane, krow, half, l32, sc, unused);
-  }
-
-  const float l_tot = halves_sum(l_run);
-  const int n_q = a.n_d + a.n_c + a.n_r;
-  float* o = a.out + ((int64_t)b * n_q + row) * g.hidden + h * D;
-  if (cp.ksplit == 1) {
-    if (rvalid) {
-      const float inv = 1.f / l_tot;
+    if constexpr (PAIR) {
+      // (selects, not a branch: a branch would merge two definitions of the
+      // accumulators); the pair's states merge below, so nothing is written yet
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          floatx4 v;
+        for (int e = 0; e < 16; ++e) acc[db][e] = redo ? 0.f : acc[db][e];
+      m_ref = redo ? -1e30f : m_ref;
+      l_run = redo ? 0.f : l_run;
+    } else {
+      // the wavefronts that keep their result write it now, so that no
+      // accumulator stays live across the second pass
+      if (!redo) {
+        write_result<D>(a, g, cp, acc, m_ref, l_run, b, row, h, rvalid, active, logical, wave, half, l32);
+        written = true;
+      }
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii] * inv;
-          *reinterpret_cast<floatx4*>(o + 32 * db + 8 * jj + 4 * half) = v;
-        }
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+      m_ref = -1e30f;
+      l_run = 0.f;
     }
-    return;
+    for (int i = 0; i < kAhead && i < n_my; ++i)
+      tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
+    const int n_redo = redo ? n_comp : 0;
+    const bool act_redo = active && redo;
+    bool unused = false;
+    if constexpr (PAIR)
+      tile_loop_pair<D, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end, act_redo,
+                               parity, wave, lane, krow, half, l32, sc, unused);
+    else if (wave >= kAttnWaves / 2)
+      tile_loop<D, true, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end, act_redo,
+                                wave, lane, krow, half, l32, sc, unused);
+    else
+      tile_loop<D, false, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end,
+                                 act_redo, wave, lane, krow, half, l32, sc, unused);
   }
 
-  // Split: publish this block's unscaled partial; k_attn_combine merges them.
-  if (!active) return;
-  float* po = a.part_o + ((int64_t)logical * kAttnWaves + wave) * 32 * D + l32 * D;
+  if constexpr (PAIR) {
+    // merge the odd-tile state of wavefront w + 4 into wavefront w (the ring is
+    // free: every wavefront has passed its last ring step)
+    constexpr int PW = kAttnWaves / 2;
+    float* mrg = reinterpret_cast<float*>(&ks[0][0]);         // [PW][16 NDB + 2][64]
+    __syncthreads();
+    if (parity == 1) {
+      float* dst = mrg + (int64_t)(wave - PW) * (16 * NDB + 2) * kWave + lane;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      floatx4 v;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii];
-      *reinterpret_cast<floatx4*>(po + 32 * db + 8 * jj + 4 * half) = v;
+        for (int e = 0; e < 16; ++e) dst[(16 * db + e) * kWave] = acc[db][e];
+      dst[(16 * NDB) * kWave] = m_ref;
+      dst[(16 * NDB + 1) * kWave] = l_run;
     }
-  if (half == 0) {
-    float* pml = a.part_ml + ((int64_t)logical * kAttnWaves + wave) * 64;
-    pml[2 * l32] = m_ref;
-    pml[2 * l32 + 1] = l_tot;
+    __syncthreads();
+    if (parity == 1) return;
+    const float* srcm = mrg + (int64_t)wave * (16 * NDB + 2) * kWave + lane;
+    const float m1 = srcm[(16 * NDB) * kWave], l1 = srcm[(16 * NDB + 1) * kWave];
+    const float m_new = fmaxf(m_ref, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_ref - m_new), a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] = acc[db][e] * a0 + srcm[(16 * db + e) * kWave] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_ref = m_new;
   }
+  if (!written) write_result<D>(a, g, cp, acc, m_ref, l_run, b, row, h, rvalid, active, logical, wave, half, l32);
 }
 
 // Merge of the key-split partials: one 256-thread block per chunk (blockIdx =
@@ -1028,7 +1172,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(Geometry g, AttnArgs a, ChunkP
 hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s) {
   const int n_cr = a.n_c + a.n_r;
   const int rows_per_chunk = g.fp32 ? 64 : 32;
-  ChunkPlan cp;
+  ChunkPlan cp{};
   cp.chunks_d = (a.n_d + rows_per_chunk - 1) / rows_per_chunk;
   cp.n_chunks = cp.chunks_d + (n_cr + rows_per_chunk - 1) / rows_per_chunk;
   if (cp.n_chunks == 0) return hipSuccess;
@@ -1053,6 +1197,7 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     if (g.B * g.Hkv * nb4 <= kAttnSplitBlocks) nb = nb4;
     cp.blocks = nb;
     cp.per_block = (space + nb - 1) / nb;
+    cp.pair = cp.per_block <= kAttnWaves / 2 ? 1 : 0;
     const int groups = g.B * g.Hkv * nb;
     // split the key tiles while the groups leave compute units idle, keeping
     // at least kAttnMinSplitTiles tiles per block
@@ -1064,8 +1209,13 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     cp.ksplit = ks;
     cp.real_blocks = groups * ks;
     dim3 grid((cp.real_blocks + 7) / 8 * 8);
-    if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
-    else hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+    if (cp.pair) {
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+    } else {
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+    }
     if (ks > 1) {
       const dim3 cgrid(groups * kAttnWaves);
 #define MDM_COMBINE(KS)                                                                                 \

@@ -562,13 +562,17 @@ __global__ void __launch_bounds__(kBaThreads) k_block_attn(BlockAttnArgs a) {
   for (int rb = 0; rb < kRB; ++rb) over = over || (row_ok[rb] && !(l_run[rb] < 0x1p50f));
   static_assert(kOverflowLog2 == 50.f, "the bound above is 2^kOverflowLog2");
   // A row sum reached the bound (or a row saw no key of its first tile):
-  // the whole block recomputes with a running maximum.  The barrier of the
-  // vote ends every wavefront's use of the ring.
+  // the tiles stream again and those rows recompute with a running maximum.
+  // The barrier of the vote ends every wavefront's use of the ring.
+  // Only the wavefronts whose own rows failed recompute; the others keep
+  // their result and take the ring steps only.
+  const bool redo = __any(over);
   if (__syncthreads_or(over ? 1 : 0)) {
-    reset();
+    if (redo) reset();
     start_ring();
     for (int i = 0; i < nt; ++i) {
-      const int cls = ring_step(i);
+      int cls = ring_step(i);
+      if (!redo) cls = kUnseen;
       scores(i, cls, sA);
       if (cls != kUnseen) tile_softmax_pv(sA, c.ring_v + (i % kBaStages) * kTileBytes, lo, acc, m_ref, l_run, sc);
     }
