@@ -100,3 +100,39 @@ def test_calls_on_null_context_fail_cleanly():
         assert e.value.status == L.MDM_E_ARG
     assert L.mdm_cache_len(null) == -1
     assert L.status_string(L.MDM_E_CAPACITY) == "MDM_E_CAPACITY"
+
+
+def test_upper_layer_calls_validate_on_the_host():
+    null = ctypes.c_void_p()
+    for fn, args in [(L.mdm_attach_upper_layers, (L.MdmUpperLayers(),)),
+                     (L.mdm_layer_project, (2, None, 0, None, 0, 0, None, 0, 0)),
+                     (L.mdm_layer_attention, (2, 0, 0, None))]:
+        with pytest.raises(L.MdmError) as e:
+            fn(null, *args)
+        assert e.value.status == L.MDM_E_ARG
+    c = _cfg()
+    ub = L.mdm_upper_workspace_bytes(c)
+    assert ub > 0 and ub % 256 == 0
+    assert L.mdm_upper_workspace_bytes(_cfg(precision=L.MDM_FP32)) == 0    # bf16 only
+
+
+def test_block_attention_validates_on_the_host():
+    fake = 1 << 20                                    # never dereferenced: rejected first
+    ok = dict(batch=2, n_rows=300, n_heads=4, n_kv_heads=2, head_dim=128)
+    shape = L.MdmBlockAttnShape(**ok)
+    need = L.mdm_block_attention_workspace_bytes(shape)
+    assert need == 2 * 5 * 2 * 4                      # [B][ceil(n/64)][2] int32
+    cases = [
+        (dict(ok, n_heads=3), fake, need, L.MDM_E_ARG),
+        (dict(ok, n_rows=0), fake, need, L.MDM_E_ARG),
+        (dict(ok, head_dim=64), fake, need, L.MDM_E_UNSUPPORTED),
+        (dict(ok, n_rows=16385), fake, need, L.MDM_E_UNSUPPORTED),
+        (ok, None, need, L.MDM_E_ARG),
+        (ok, fake + 8, need, L.MDM_E_ARG),              # q misaligned
+        (ok, fake, need - 4, L.MDM_E_SHAPE),
+    ]
+    for kw, q, ws, status in cases:
+        with pytest.raises(L.MdmError) as e:
+            L.mdm_block_attention(L.MdmBlockAttnShape(**kw), q, fake, fake, fake, fake, fake, fake, ws, None)
+        assert e.value.status == status, (kw, q, ws)
+    assert L.mdm_block_attention_workspace_bytes(L.MdmBlockAttnShape(**dict(ok, n_heads=3))) == 0
