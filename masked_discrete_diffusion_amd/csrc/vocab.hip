@@ -352,9 +352,17 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
   constexpr int AHEAD = S::NST - 1;
   __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
 
-  const int vw = blockIdx.x;                     // 512-column tile
-  const int mt = blockIdx.y;
-  const int split = blockIdx.z;
+  // 1-D grid, XCD-aware: blocks i and i + 8k run on one XCD, and the row
+  // tiles of a 512-column tile take consecutive slots of one XCD, so they
+  // stream the same W rows at about the same time and the second read is an
+  // L2 hit instead of another pass over HBM (W is 1 GB for a 128k vocabulary).
+  const int n_m = (M + 32 * RB - 1) / (32 * RB);
+  const int n_vw = (g.V + kWideTile - 1) / kWideTile;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int mt = slot % n_m;
+  const int vw = (slot / n_m) * 8 + xcd;          // 512-column tile
+  if (vw >= n_vw) return;
+  const int split = 0;
   const int v0 = vw * kWideTile;
   const int m0 = mt * 32 * RB;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -826,7 +834,7 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8w + 255) / 256)), dim3(256), 0, s, g, pa, M);
     hipError_t ew = hipGetLastError();
     if (ew != hipSuccess) return ew;
-    dim3 wgrid(n_wide, m_tiles, 1);
+    dim3 wgrid((unsigned)(((n_wide + 7) / 8) * 8 * m_tiles));
     if (rb == 4) {
       if (a.hlo) hipLaunchKernelGGL((k_screen_wide<4, true>), wgrid, dim3(512), 0, s, g, pa, M, 1);
       else hipLaunchKernelGGL((k_screen_wide<4, false>), wgrid, dim3(512), 0, s, g, pa, M, 1);
