@@ -156,6 +156,15 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print(json.dumps(t))
 
 
+def cpu_threads(n):
+    """Context that caps the BLAS thread pools at n threads (n <= 0: no cap)."""
+    import contextlib
+    if n <= 0:
+        return contextlib.nullcontext()
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=n)
+
+
 def cpu_baseline(cfg, budget_s):
     from threadpoolctl import threadpool_info
     from mdm_inputs import make_workload
@@ -282,7 +291,8 @@ def block_attention_bench(args):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = block_attention_cpu_baseline(inp, args.cpu_seconds)
+        with cpu_threads(args.cpu_threads):
+            res["cpu_baseline"] = block_attention_cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(res))
 
 
@@ -326,6 +336,8 @@ def main():
                     help="attention layers (upper layers project the previous layer's outputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="limit the CPU baseline's BLAS threads (0: as many as the host gives)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many eager generations (for profilers) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -496,7 +508,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        with cpu_threads(args.cpu_threads):
+            out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     run.close()
     print(json.dumps(out))
 
