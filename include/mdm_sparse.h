@@ -188,6 +188,33 @@ mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand
                              int32_t n_select, int32_t mode, int32_t* out_tok, int32_t* out_pos,
                              int32_t* rem_pos, int32_t* seq_tokens);
 
+/* One whole sampling step when the unmasking order is fixed beforehand (page 3,
+ * section 3.2: image tokens are unmasked in a pre-generated order, so every
+ * decoded position is unmasked), in three fewer launches than the separate
+ * calls.  The results are those of the sequence
+ *   mdm_step_attention(ctx, D rows, n_new_cached, c_pos, c_stride, n_decode, out);
+ *   mdm_subset_logits_confidence(ctx, C rows of out, ..., n_decode, conf, token, logits_or_null);
+ *   mdm_unmask_select(ctx, c_pos, c_stride, conf, token, n_decode, n_decode,
+ *                     MDM_SELECT_ORDER, ..., seq_tokens);
+ *   if (commit) mdm_kv_append(ctx, token, c_pos, ..., n_decode);
+ * bit for bit: the attention also writes the bf16 split of the C rows'
+ * outputs for the logits, and the merge of the logits writes each decided
+ * token at its position (seq_tokens[b][pos], if non-NULL) and, with commit
+ * non-zero, appends the row's key and queries to the cache (slot len + c for
+ * candidate c; its value follows in one more launch), so that the n_decode
+ * rows are the D rows (n_new_cached) of the next call.  Leave commit 0 on the
+ * last step of a generation.
+ * n_new_cached: 0, or the row count of the preceding commit (this call's or
+ * mdm_kv_append's) on this context, whose queries the context kept; their
+ * token ids and positions are not needed.  out [B][n_q][H*d] fp32 (16-byte
+ * aligned), conf/token [B][n_decode], logits_or_null as in
+ * mdm_subset_logits_confidence.  Errors as in the four calls; MDM_E_ARG if
+ * n_new_cached is not 0 or that row count; MDM_E_UNSUPPORTED for the fp32
+ * precision or with upper layers attached (use the separate calls). */
+mdm_status mdm_order_step(mdm_ctx* ctx, int32_t n_new_cached, const int32_t* c_pos, int64_t c_stride,
+                          int32_t n_decode, int32_t commit, float* out, float* conf, int32_t* token,
+                          int32_t* seq_tokens, float* logits_or_null);
+
 /* Start a new generation: cache length 0 (the buffers are reused). */
 mdm_status mdm_sparse_step_reset(mdm_ctx* ctx);
 

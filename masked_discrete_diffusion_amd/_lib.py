@@ -94,6 +94,7 @@ _SIGS = {
     "mdm_step_attention": (_I32, [_P, _P, _P, _I64, _I32, _P, _I64, _I32, _P]),
     "mdm_subset_logits_confidence": (_I32, [_P, _P, _I64, _I32, _P, _P, _P]),
     "mdm_unmask_select": (_I32, [_P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "mdm_order_step": (_I32, [_P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "mdm_sparse_step_reset": (_I32, [_P]),
     "mdm_cache_len": (_I32, [_P]),
     "mdm_device_status": (_I32, [_P]),
@@ -188,6 +189,12 @@ def mdm_unmask_select(ctx, cand_pos, cand_stride: int, conf, token, n_cand: int,
                       out_tok, out_pos, rem_pos=None, seq_tokens=None):
     _check(load().mdm_unmask_select(ctx, _ptr(cand_pos), cand_stride, _ptr(conf), _ptr(token), n_cand, n_select,
                                     mode, _ptr(out_tok), _ptr(out_pos), _ptr(rem_pos), _ptr(seq_tokens)), ctx)
+
+
+def mdm_order_step(ctx, n_new_cached: int, c_pos, c_stride: int, n_decode: int, commit: bool, out, conf, token,
+                   seq_tokens=None, logits=None):
+    _check(load().mdm_order_step(ctx, n_new_cached, _ptr(c_pos), c_stride, n_decode, 1 if commit else 0, _ptr(out),
+                                 _ptr(conf), _ptr(token), _ptr(seq_tokens), _ptr(logits)), ctx)
 
 
 def mdm_sparse_step_reset(ctx):

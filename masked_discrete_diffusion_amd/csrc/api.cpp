@@ -250,6 +250,15 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
     st = hip_check(ctx, hipMemcpyAsync(ctx->ws() + L.rope_sin, sn.data(), sn.size() * sizeof(float),
                                        hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
   if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 1, ctx->stream), "clear error flag");
+  // The packed logits rows start at zero: rows past a step's count are read
+  // by the screen (their logits are never used) and must hold finite values.
+  const size_t hwords = g.fp32 ? 0 : (size_t)L.m_pad * g.hidden / 2;
+  if (st == MDM_OK && hwords)
+    st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.hhi), 0, (int)hwords, ctx->stream),
+                   "clear packed rows");
+  if (st == MDM_OK && hwords && cfg->accurate_conf)
+    st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(ctx->ws() + L.hlo), 0, (int)hwords, ctx->stream),
+                   "clear packed rows");
   if (st == MDM_OK) {
     // Key table: the mask token rotated at every position 0..seq_len-1, then the
     // registers at seq_len..seq_len+R-1 (their keys never change).
@@ -327,6 +336,49 @@ mdm_status mdm_kv_append(mdm_ctx* ctx, const int32_t* tok, const int32_t* pos, i
   return st;
 }
 
+namespace {
+
+// Launch arguments of a step attention (validated by the caller).
+AttnArgs step_attn_args(mdm_ctx* ctx, const int32_t* d_tok, const int32_t* d_pos, int64_t d_stride,
+                        int32_t n_new_cached, const int32_t* c_pos, int64_t c_stride, int32_t n_decode, float* out) {
+  AttnArgs a{};
+  a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
+  a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
+  if (!ctx->g.fp32) {
+    a.qtab = ctx->ws() + ctx->L.qtab; a.qtab_rows = ctx->L.ktab_rows;
+    if (n_new_cached > 0 && ctx->q_rows == n_new_cached) {
+      a.qbuf = ctx->ws() + ctx->L.qbuf;
+      a.qbuf_rows = ctx->cfg.max_decode;
+    }
+    a.mvt = ctx->ws() + ctx->L.mvt; a.rvt = ctx->ws() + ctx->L.rvt; a.r_pad = ctx->L.r_pad;
+    a.part_o = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_o);
+    a.part_ml = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_ml);
+  }
+  a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
+  a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
+  a.d_tok = d_tok; a.d_pos = d_pos; a.d_stride = d_stride; a.c_pos = c_pos; a.c_stride = c_stride;
+  a.out = out; a.err = err_word(ctx);
+  a.n_d = n_new_cached; a.n_c = n_decode; a.n_r = ctx->cfg.n_registers; a.S = ctx->len;
+  return a;
+}
+
+// Launch arguments of the subset logits (validated by the caller).
+VocabArgs logits_args(mdm_ctx* ctx, const float* h, int64_t h_batch_stride, int32_t n_decode, float* conf,
+                      int32_t* token, float* logits_or_null) {
+  VocabArgs a{};
+  a.w = ctx->buf.w_vocab; a.h = h; a.h_stride = h_batch_stride; a.n_c = n_decode;
+  a.hhi = reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hhi);
+  a.hlo = (ctx->cfg.precision == MDM_BF16 && ctx->cfg.accurate_conf)
+              ? reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hlo) : nullptr;
+  a.partials = reinterpret_cast<float*>(ctx->ws() + ctx->L.partials);
+  a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
+  a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
+  a.v_pad = ctx->L.v_pad;
+  return a;
+}
+
+}  // namespace
+
 mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t* d_pos, int64_t d_stride,
                               int32_t n_new_cached, const int32_t* c_pos, int64_t c_stride, int32_t n_decode,
                               float* out) {
@@ -345,26 +397,8 @@ mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t*
   if ((int64_t)ctx->len + n_decode > ctx->cfg.seq_len)
     return fail(ctx, MDM_E_CAPACITY, "cache length %d + n_decode %d exceeds seq_len %d", ctx->len, n_decode,
                 ctx->cfg.seq_len);
-  const int n_r = ctx->cfg.n_registers;
-  if (n_new_cached + n_decode + n_r == 0) return MDM_OK;
-  AttnArgs a{};
-  a.tq = ctx->buf.tq; a.tv = ctx->buf.tv;
-  a.ktab = ctx->ws() + ctx->L.ktab; a.ktab_rows = ctx->L.ktab_rows;
-  if (!ctx->g.fp32) {
-    a.qtab = ctx->ws() + ctx->L.qtab; a.qtab_rows = ctx->L.ktab_rows;
-    if (n_new_cached > 0 && ctx->q_rows == n_new_cached) {
-      a.qbuf = ctx->ws() + ctx->L.qbuf;
-      a.qbuf_rows = ctx->cfg.max_decode;
-    }
-    a.mvt = ctx->ws() + ctx->L.mvt; a.rvt = ctx->ws() + ctx->L.rvt; a.r_pad = ctx->L.r_pad;
-    a.part_o = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_o);
-    a.part_ml = reinterpret_cast<float*>(ctx->ws() + ctx->L.apart_ml);
-  }
-  a.kc = ctx->buf.k_cache; a.vc = ctx->buf.v_cache;
-  a.rope_cos = rope_cos(ctx); a.rope_sin = rope_sin(ctx);
-  a.d_tok = d_tok; a.d_pos = d_pos; a.d_stride = d_stride; a.c_pos = c_pos; a.c_stride = c_stride;
-  a.out = out; a.err = err_word(ctx);
-  a.n_d = n_new_cached; a.n_c = n_decode; a.n_r = n_r; a.S = ctx->len;
+  if (n_new_cached + n_decode + ctx->cfg.n_registers == 0) return MDM_OK;
+  const AttnArgs a = step_attn_args(ctx, d_tok, d_pos, d_stride, n_new_cached, c_pos, c_stride, n_decode, out);
   return hip_check(ctx, launch_attention(ctx->g, a, ctx->stream), "attention launch");
 }
 
@@ -380,16 +414,71 @@ mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_
   if (h_batch_stride < (int64_t)n_decode * hidden) return fail(ctx, MDM_E_ARG, "h_batch_stride too small");
   if (h_batch_stride % 4 || reinterpret_cast<uintptr_t>(h) % 16)
     return fail(ctx, MDM_E_ARG, "h must be 16-byte aligned with a stride that is a multiple of 4");
-  VocabArgs a{};
-  a.w = ctx->buf.w_vocab; a.h = h; a.h_stride = h_batch_stride; a.n_c = n_decode;
-  a.hhi = reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hhi);
-  a.hlo = (ctx->cfg.precision == MDM_BF16 && ctx->cfg.accurate_conf)
-              ? reinterpret_cast<uint16_t*>(ctx->ws() + ctx->L.hlo) : nullptr;
-  a.partials = reinterpret_cast<float*>(ctx->ws() + ctx->L.partials);
-  a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
-  a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
-  a.v_pad = ctx->L.v_pad;
+  const VocabArgs a = logits_args(ctx, h, h_batch_stride, n_decode, conf, token, logits_or_null);
   return hip_check(ctx, launch_vocab(ctx->g, a, ctx->stream), "vocab launch");
+}
+
+mdm_status mdm_order_step(mdm_ctx* ctx, int32_t n_new_cached, const int32_t* c_pos, int64_t c_stride,
+                          int32_t n_decode, int32_t commit, float* out, float* conf, int32_t* token,
+                          int32_t* seq_tokens, float* logits_or_null) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (ctx->g.fp32) return fail(ctx, MDM_E_UNSUPPORTED, "the fused order step needs the bf16 precision");
+  if (ctx->has_upper) return fail(ctx, MDM_E_UNSUPPORTED, "the fused order step runs one attention layer");
+  if (!out) return fail(ctx, MDM_E_ARG, "out is NULL");
+  if (reinterpret_cast<uintptr_t>(out) % 16) return fail(ctx, MDM_E_ARG, "out must be 16-byte aligned");
+  if (n_new_cached < 0 || n_decode < 0) return fail(ctx, MDM_E_ARG, "row counts must be >= 0");
+  if (n_new_cached > ctx->len)
+    return fail(ctx, MDM_E_ARG, "n_new_cached %d exceeds the cache length %d", n_new_cached, ctx->len);
+  if (n_new_cached > 0 && ctx->q_rows != n_new_cached)
+    return fail(ctx, MDM_E_ARG, "n_new_cached %d is not the row count of the preceding commit (%d)", n_new_cached,
+                ctx->q_rows);
+  if (n_decode > ctx->cfg.max_decode)
+    return fail(ctx, MDM_E_ARG, "n_decode %d exceeds max_decode %d", n_decode, ctx->cfg.max_decode);
+  if (n_decode > 0 && (!c_pos || !conf || !token)) return fail(ctx, MDM_E_ARG, "c_pos, conf and token must be non-NULL");
+  if (c_stride == 0) c_stride = n_decode;
+  if (c_stride < n_decode) return fail(ctx, MDM_E_ARG, "c_stride < n_decode");
+  if ((int64_t)ctx->len + n_decode > ctx->cfg.seq_len)
+    return fail(ctx, MDM_E_CAPACITY, "cache length %d + n_decode %d exceeds seq_len %d", ctx->len, n_decode,
+                ctx->cfg.seq_len);
+  const int n_r = ctx->cfg.n_registers;
+  if (n_new_cached + n_decode + n_r == 0) return MDM_OK;
+  AttnArgs a = step_attn_args(ctx, nullptr, nullptr, 0, n_new_cached, c_pos, c_stride, n_decode, out);
+  const int hidden = ctx->g.hidden;
+  VocabArgs v = logits_args(ctx, out + (int64_t)n_new_cached * hidden, (int64_t)(n_new_cached + n_decode + n_r) * hidden,
+                            n_decode, conf, token, logits_or_null);
+  if (n_decode > 0) {
+    a.pack_hi = v.hhi;
+    a.pack_lo = v.hlo;
+  }
+  mdm_status st = hip_check(ctx, launch_attention(ctx->g, a, ctx->stream), "attention launch");
+  if (st != MDM_OK || n_decode == 0) return st;
+  v.prepacked = 1;
+  v.cand_pos = c_pos; v.cand_stride = c_stride; v.seq_tokens = seq_tokens;
+  AppendArgs& cm = v.commit;
+  cm.err = err_word(ctx);
+  if (commit) {
+    // keys, queries and the (position, token) record in the merge; the values
+    // after it, transposed through LDS 32 rows at a time (one row's value
+    // alone touches a separate line per feature)
+    cm.tk = ctx->buf.tk; cm.tq = ctx->buf.tq; cm.kc = ctx->buf.k_cache;
+    cm.cache_pos = ctx->buf.cache_pos; cm.cache_tok = ctx->buf.cache_tok;
+    cm.rope_cos = rope_cos(ctx); cm.rope_sin = rope_sin(ctx);
+    cm.qout = ctx->ws() + ctx->L.qbuf; cm.q_rows = ctx->cfg.max_decode;
+    cm.slot0 = ctx->len;
+  }
+  st = hip_check(ctx, launch_vocab(ctx->g, v, ctx->stream), "vocab launch");
+  if (st == MDM_OK && commit) {
+    AppendArgs va{};
+    va.tv = ctx->buf.tv; va.vc = ctx->buf.v_cache;
+    va.tok = token; va.stride = n_decode; va.n_a = n_decode; va.slot0 = ctx->len;
+    va.err = err_word(ctx);
+    st = hip_check(ctx, launch_append(ctx->g, va, ctx->stream), "value commit launch");
+  }
+  if (st == MDM_OK && commit) {
+    ctx->len += n_decode;
+    ctx->q_rows = n_decode;
+  }
+  return st;
 }
 
 mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand_stride, const float* conf,

@@ -593,6 +593,26 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
 
 // The result of a wavefront: O = acc / l for its rows, or (key split) the
 // unscaled partial (O, reference, row sum) that k_attn_combine merges.
+// bf16 copies of four consecutive output features (from column col) of query
+// row `row` of sequence b for the logits, when it is a C row: hi = the value
+// rounded to bf16, lo = the remainder rounded to bf16.
+__device__ inline void pack_store4(const AttnArgs& a, const Geometry& g, int b, int row, int col, const floatx4& x) {
+  const int c = row - a.n_d;
+  if (!a.pack_hi || c < 0 || c >= a.n_c) return;
+  const int64_t off = ((int64_t)b * a.n_c + c) * g.hidden + col;
+  uint16_t hb[4], lb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hb[e] = f32_to_bf16(x[e]);
+    lb[e] = f32_to_bf16(x[e] - bf16_to_f32(hb[e]));
+  }
+  *reinterpret_cast<uint2*>(a.pack_hi + off) =
+      uint2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+  if (a.pack_lo)
+    *reinterpret_cast<uint2*>(a.pack_lo + off) =
+        uint2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+}
+
 template <int D>
 __device__ inline void write_result(const AttnArgs& a, const Geometry& g, const ChunkPlan& cp, const floatx16* acc,
                                     float m_ref, float l_run, int b, int row, int h, bool rvalid, bool active,
@@ -612,6 +632,7 @@ __device__ inline void write_result(const AttnArgs& a, const Geometry& g, const 
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) v[ii] = acc[db][4 * jj + ii] * inv;
           *reinterpret_cast<floatx4*>(o + 32 * db + 8 * jj + 4 * half) = v;
+          pack_store4(a, g, b, row, h * D + 32 * db + 8 * jj + 4 * half, v);
         }
     }
     return;
@@ -1055,6 +1076,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(Geometry g, At
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) x[ii] = sum[q][ii] * inv;
     o[q] = x;
+    pack_store4(a, g, b, row, h * D + part * QD + 4 * q, x);
   }
 }
 

@@ -17,9 +17,9 @@ struct Geometry {
 
 // Rows [0, n_a): token tok[b*stride + r] (or the mask token V when tok == NULL),
 // position pos[b*stride + r] (or r when pos == NULL).  Rows [n_a, n_a + n_reg):
-// register r - n_a (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) and,
-// when vc != NULL, transposed values to slots slot0 + r; records (pos, id) when
-// cache_pos != NULL.  When qout != NULL the same launch also writes the rows'
+// register r - n_a (id V+1+j, position seq_len+j).  Writes keys (RoPE'd) when
+// kc != NULL and transposed values when vc != NULL to slots slot0 + r; records
+// (pos, id) when cache_pos != NULL.  When qout != NULL the same launch also writes the rows'
 // RoPE'd queries for all H heads: qout[b][h][q_rows][d], row r at index r.
 struct AppendArgs {
   const void* tk;
@@ -89,6 +89,11 @@ struct AttnArgs {
   const void* tk;
   const void* tvt;
   int t_pad;
+  // Optional bf16 copies of the C rows' outputs for the logits, row m = b*n_c + c
+  // of [B*n_c][hidden]: pack_hi = the output rounded to bf16, pack_lo = the
+  // remainder rounded to bf16 (or NULL).  The same rounding as k_pack.
+  uint16_t* pack_hi;
+  uint16_t* pack_lo;
 };
 hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s);
 
@@ -108,6 +113,17 @@ struct VocabArgs {
   int32_t* token;           // [M]
   int m_pad;
   int emit;                 // nonzero: the screen writes the raw product to zpart [M][v_pad] and stops
+  int prepacked;            // nonzero: hhi (and hlo) already hold rows 0..M-1 (no k_pack); rows
+                            // M..m_pad-1 hold finite values that only reach their own logits
+  // Fused unmasking in a pre-generated order (k_merge): with cand_pos != NULL,
+  // row m = (b, c) is unmasked at position cand_pos[b*cand_stride + c]:
+  // seq_tokens[b][pos] = its token (when seq_tokens != NULL) and, when
+  // commit.kc != NULL, the row is committed to the cache at slot
+  // commit.slot0 + c with its queries at qout row c, as k_append does.
+  const int32_t* cand_pos;
+  int64_t cand_stride;
+  int32_t* seq_tokens;
+  AppendArgs commit;
 };
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
 

@@ -7,6 +7,11 @@ Per sampling step k (page 3, section 3.2):
     mdm_subset_logits_confidence(h of C_k)  logits, confidence and argmax for C_k only
     mdm_unmask_select(C_k)                  unmask (pre-generated order or confidence)
 
+With a pre-generated order (one bf16 layer) each step is instead one
+mdm_order_step, which gives the same results in fewer launches: the rows
+decoded at step k are unmasked and committed to the cache by step k itself
+(not after the last step), and are the D rows of step k + 1.
+
 With upper layers (layer l >= 2 projects layer l-1's outputs), every step
 runs mdm_layer_project + mdm_layer_attention per upper layer after the first
 attention, and the logits read the last layer's output.
@@ -77,7 +82,7 @@ class SparseStepRunner:
     """Device state of one workload: tables, caches, workspace, loop buffers."""
 
     def __init__(self, wl, device: str = "cuda", accurate_conf: Optional[bool] = None,
-                 precision: Optional[str] = None):
+                 precision: Optional[str] = None, fused: bool = True):
         cfg = wl.cfg
         self.wl, self.cfg = wl, cfg
         self.device = torch.device(device)
@@ -127,6 +132,11 @@ class SparseStepRunner:
         self.d_pos = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
         self.rem = [torch.zeros(B * max_decode, **i32) for _ in range(2)]
         self.layers = cfg.layers
+        # A pre-generated order on one bf16 layer runs each step as one fused
+        # mdm_order_step (the decoded rows enter the cache at the end of their
+        # own step instead of at the start of the next).
+        self.fused = (fused and self.precision == "bf16" and self.layers == 1
+                      and all(p.mode == L.MDM_SELECT_ORDER for p in self.plan))
         rows = max(p.n_d + p.n_c for p in self.plan)
         if self.layers > 1:
             rows = max(rows, cfg.prompt_len)          # the prefill's first-layer rows feed layer 2
@@ -200,9 +210,14 @@ class SparseStepRunner:
         st = self.plan[k]
         cfg = self.cfg
         ctx = self.ctx
+        c_ptr, c_stride = self._c_src(st)
+        if self.fused:
+            # the rows decoded here are committed here, except after the last step
+            L.mdm_order_step(ctx, st.n_d, c_ptr, c_stride, st.n_c, k + 1 < len(self.plan), self.outs[0],
+                             self.conf, self.token, self.seq_tokens, logits)
+            return
         if st.n_d:
             L.mdm_kv_append(ctx, self.d_tok[st.d_buf], self.d_pos[st.d_buf], st.n_d, st.n_d)
-        c_ptr, c_stride = self._c_src(st)
         L.mdm_step_attention(ctx, self.d_tok[st.d_buf], self.d_pos[st.d_buf], st.n_d, st.n_d,
                              c_ptr, c_stride, st.n_c, self.outs[0])
         if self.layers > 1:
@@ -236,12 +251,20 @@ class SparseStepRunner:
             self.step(k, lg)
             torch.cuda.synchronize(self.device)
             n_q = st.n_d + st.n_c + cfg.n_registers
+            token = self.token[:B * st.n_c].view(B, st.n_c).cpu().numpy().copy()
+            if self.fused:
+                # order mode unmasks every candidate, in candidate order
+                sel_pos = self.order[:, st.c_off:st.c_off + st.n_c].cpu().numpy().copy()
+                sel_tok = token.copy()
+            else:
+                sel_pos = self.d_pos[st.out_buf][:B * st.n_sel].view(B, st.n_sel).cpu().numpy().copy()
+                sel_tok = self.d_tok[st.out_buf][:B * st.n_sel].view(B, st.n_sel).cpu().numpy().copy()
             rec = dict(
                 k=k,
                 conf=self.conf[:B * st.n_c].view(B, st.n_c).cpu().numpy().copy(),
-                token=self.token[:B * st.n_c].view(B, st.n_c).cpu().numpy().copy(),
-                sel_pos=self.d_pos[st.out_buf][:B * st.n_sel].view(B, st.n_sel).cpu().numpy().copy(),
-                sel_tok=self.d_tok[st.out_buf][:B * st.n_sel].view(B, st.n_sel).cpu().numpy().copy(),
+                token=token,
+                sel_pos=sel_pos,
+                sel_tok=sel_tok,
             )
             if k in keep_o:
                 rec["o"] = self.out[:B * n_q * cfg.hidden].view(B, n_q, cfg.hidden).cpu().numpy().copy()

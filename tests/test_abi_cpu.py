@@ -93,6 +93,7 @@ def test_calls_on_null_context_fail_cleanly():
                      (L.mdm_step_attention, (None, None, 0, 0, None, 0, 0, None)),
                      (L.mdm_subset_logits_confidence, (None, 0, 1, None, None)),
                      (L.mdm_unmask_select, (None, 0, None, None, 1, 1, 0, None, None)),
+                     (L.mdm_order_step, (0, None, 0, 1, True, None, None, None)),
                      (L.mdm_sparse_step_reset, ()),
                      (L.mdm_device_status, ())]:
         with pytest.raises(L.MdmError) as e:

@@ -257,7 +257,7 @@ def test_forbidden_keys_nan_poison():
     from masked_discrete_diffusion_amd import _lib as L
     cfg = gpu_small_d128()
     _say("nan poison: gpu_small_d128")
-    wl, run = _runner(cfg)
+    wl, run = _runner(cfg, fused=False)
     run.prefill()
     for k in range(3):
         run.step(k)
@@ -328,7 +328,7 @@ def test_repeated_kernels_are_bitwise_identical(name, steps):
     from masked_discrete_diffusion_amd import _lib as L
     cfg = gpu_small_semi_ar() if name == "gpu_small_semi_ar" else get_config(name)
     _say(f"repeated kernels: {name} steps {steps}")
-    wl, run = _runner(cfg)
+    wl, run = _runner(cfg, fused=False)
     run.seq_tokens.copy_(run.seq0)
     run.prefill()
     for k in range(max(steps) + 1):
