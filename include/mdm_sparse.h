@@ -190,7 +190,7 @@ mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand
 
 /* One whole sampling step when the unmasking order is fixed beforehand (page 3,
  * section 3.2: image tokens are unmasked in a pre-generated order, so every
- * decoded position is unmasked), in three fewer launches than the separate
+ * decoded position is unmasked), in two fewer launches than the separate
  * calls.  The results are those of the sequence
  *   mdm_step_attention(ctx, D rows, n_new_cached, c_pos, c_stride, n_decode, out);
  *   mdm_subset_logits_confidence(ctx, C rows of out, ..., n_decode, conf, token, logits_or_null);
@@ -198,12 +198,11 @@ mdm_status mdm_unmask_select(mdm_ctx* ctx, const int32_t* cand_pos, int64_t cand
  *                     MDM_SELECT_ORDER, ..., seq_tokens);
  *   if (commit) mdm_kv_append(ctx, token, c_pos, ..., n_decode);
  * bit for bit: the attention also writes the bf16 split of the C rows'
- * outputs for the logits, and the merge of the logits writes each decided
- * token at its position (seq_tokens[b][pos], if non-NULL) and, with commit
- * non-zero, appends the row's key and queries to the cache (slot len + c for
- * candidate c; its value follows in one more launch), so that the n_decode
- * rows are the D rows (n_new_cached) of the next call.  Leave commit 0 on the
- * last step of a generation.
+ * outputs for the logits, the merge of the logits writes each decided token
+ * at its position (seq_tokens[b][pos], if non-NULL), and with commit non-zero
+ * the decided rows are appended (slot len + c for candidate c) with their
+ * queries kept, so that they are the D rows (n_new_cached) of the next call.
+ * Leave commit 0 on the last step of a generation.
  * n_new_cached: 0, or the row count of the preceding commit (this call's or
  * mdm_kv_append's) on this context, whose queries the context kept; their
  * token ids and positions are not needed.  out [B][n_q][H*d] fp32 (16-byte

@@ -453,26 +453,19 @@ mdm_status mdm_order_step(mdm_ctx* ctx, int32_t n_new_cached, const int32_t* c_p
   mdm_status st = hip_check(ctx, launch_attention(ctx->g, a, ctx->stream), "attention launch");
   if (st != MDM_OK || n_decode == 0) return st;
   v.prepacked = 1;
-  v.cand_pos = c_pos; v.cand_stride = c_stride; v.seq_tokens = seq_tokens;
-  AppendArgs& cm = v.commit;
-  cm.err = err_word(ctx);
-  if (commit) {
-    // keys, queries and the (position, token) record in the merge; the values
-    // after it, transposed through LDS 32 rows at a time (one row's value
-    // alone touches a separate line per feature)
-    cm.tk = ctx->buf.tk; cm.tq = ctx->buf.tq; cm.kc = ctx->buf.k_cache;
-    cm.cache_pos = ctx->buf.cache_pos; cm.cache_tok = ctx->buf.cache_tok;
-    cm.rope_cos = rope_cos(ctx); cm.rope_sin = rope_sin(ctx);
-    cm.qout = ctx->ws() + ctx->L.qbuf; cm.q_rows = ctx->cfg.max_decode;
-    cm.slot0 = ctx->len;
-  }
+  v.cand_pos = c_pos; v.cand_stride = c_stride; v.seq_tokens = seq_tokens; v.err = err_word(ctx);
   st = hip_check(ctx, launch_vocab(ctx->g, v, ctx->stream), "vocab launch");
   if (st == MDM_OK && commit) {
-    AppendArgs va{};
-    va.tv = ctx->buf.tv; va.vc = ctx->buf.v_cache;
-    va.tok = token; va.stride = n_decode; va.n_a = n_decode; va.slot0 = ctx->len;
-    va.err = err_word(ctx);
-    st = hip_check(ctx, launch_append(ctx->g, va, ctx->stream), "value commit launch");
+    // the decided rows enter the cache as mdm_kv_append(token, c_pos) would
+    // append them: one launch over 32-row blocks
+    AppendArgs ca{};
+    ca.tk = ctx->buf.tk; ca.tv = ctx->buf.tv; ca.kc = ctx->buf.k_cache; ca.vc = ctx->buf.v_cache;
+    ca.cache_pos = ctx->buf.cache_pos; ca.cache_tok = ctx->buf.cache_tok;
+    ca.rope_cos = rope_cos(ctx); ca.rope_sin = rope_sin(ctx);
+    ca.tok = token; ca.stride = n_decode; ca.pos = c_pos; ca.pos_stride = c_stride;
+    ca.n_a = n_decode; ca.slot0 = ctx->len; ca.err = err_word(ctx);
+    ca.tq = ctx->buf.tq; ca.qout = ctx->ws() + ctx->L.qbuf; ca.q_rows = ctx->cfg.max_decode;
+    st = hip_check(ctx, launch_append(ctx->g, ca, ctx->stream), "commit launch");
   }
   if (st == MDM_OK && commit) {
     ctx->len += n_decode;

@@ -32,7 +32,8 @@ struct AppendArgs {
   const float* rope_sin;
   const int32_t* tok;
   const int32_t* pos;
-  int64_t stride;
+  int64_t stride;           // of tok (and of pos when pos_stride is 0)
+  int64_t pos_stride;
   int n_a, n_reg, slot0;
   int* err;
   const void* tq;           // query table (with qout)
@@ -117,13 +118,11 @@ struct VocabArgs {
                             // M..m_pad-1 hold finite values that only reach their own logits
   // Fused unmasking in a pre-generated order (k_merge): with cand_pos != NULL,
   // row m = (b, c) is unmasked at position cand_pos[b*cand_stride + c]:
-  // seq_tokens[b][pos] = its token (when seq_tokens != NULL) and, when
-  // commit.kc != NULL, the row is committed to the cache at slot
-  // commit.slot0 + c with its queries at qout row c, as k_append does.
+  // seq_tokens[b][pos] = its token (when seq_tokens != NULL).
   const int32_t* cand_pos;
   int64_t cand_stride;
   int32_t* seq_tokens;
-  AppendArgs commit;
+  int* err;
 };
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
 

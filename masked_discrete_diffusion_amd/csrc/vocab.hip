@@ -15,7 +15,6 @@
 //            screened terms replaced by their exact ones.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "rope.hpp"
 
 namespace mdm {
 
@@ -666,75 +665,12 @@ __device__ inline void wave_lse(float& m, float& se) {
 
 // Unmasking in a pre-generated order, fused into the merge (page 3, section
 // 3.2: every decoded position is unmasked): the decided token of row
-// m = (b, c) is written at its candidate position in the dense sequence and,
-// with commit.kc set, the row enters the cache at slot commit.slot0 + c as
-// k_append writes a committed row: RoPE'd key per kv head, RoPE'd queries of
-// every head at qout row c, (position, token) record, and the transposed value
-// when commit.vc is set.  Every thread of the block takes 16-element units.
-__device__ inline void unmask_commit(const Geometry& g, const VocabArgs& a, int m, int tok) {
-  const AppendArgs& c = a.commit;
+// m = (b, c) is written at its candidate position in the dense sequence.
+__device__ inline void unmask_order(const Geometry& g, const VocabArgs& a, int m, int tok) {
   const int b = m / a.n_c, cc = m % a.n_c;
-  int pos = a.cand_pos[(int64_t)b * a.cand_stride + cc];
-  if (threadIdx.x == 0) {
-    if (pos < 0 || pos >= g.seq_len) flag_error(c.err, kErrPos);
-    else if (a.seq_tokens) a.seq_tokens[(int64_t)b * g.seq_len + pos] = tok;
-  }
-  if (!c.kc) return;
-  if (pos < 0 || pos >= g.max_pos) pos = 0;           // flagged above
-  if (tok < 0 || tok >= g.table_rows) {
-    if (threadIdx.x == 0) flag_error(c.err, kErrTok);
-    tok = 0;
-  }
-  const int slot = c.slot0 + cc;
-  if (threadIdx.x == 0 && c.cache_pos) {
-    c.cache_pos[(int64_t)b * g.slots + slot] = pos;
-    c.cache_tok[(int64_t)b * g.slots + slot] = tok;
-  }
-  constexpr int kU = 16;
-  const int D = g.D;
-  const int kunits = g.Hkv * D / kU;
-  const int qunits = c.qout ? g.H * D / kU : 0;
-  const int vunits = c.vc ? g.Hkv * D / kU : 0;
-  const uint16_t* tk = static_cast<const uint16_t*>(c.tk);
-  const uint16_t* tv = static_cast<const uint16_t*>(c.tv);
-  const uint16_t* tq = static_cast<const uint16_t*>(c.tq);
-  uint16_t* kc = static_cast<uint16_t*>(c.kc);
-  uint16_t* vc = static_cast<uint16_t*>(c.vc);
-  uint16_t* qo = static_cast<uint16_t*>(c.qout);
-  for (int u = threadIdx.x; u < kunits + qunits + vunits; u += blockDim.x) {
-    const int kind = u < kunits ? 0 : (u < kunits + qunits ? 1 : 2);          // key, query, value
-    const int f = (u - (kind == 0 ? 0 : (kind == 1 ? kunits : kunits + qunits))) * kU;
-    const int hd = f / D, j = f % D;                 // kv head (or query head), first element
-    if (kind == 2) {
-      // one slot of every 64-slot value tile row: 2-byte stores to separate
-      // lines, so the launcher prefers k_append for the values
-      const u16x8* src = reinterpret_cast<const u16x8*>(tv + ((int64_t)tok * g.Hkv + hd) * D + j);
-      const u16x8 v0 = src[0], v1 = src[1];
-      uint16_t* vhead = vc + ((int64_t)b * g.Hkv + hd) * D * g.slots;
-      uint16_t* dst = vhead + ((int64_t)(slot / kKeyTile) * D + j) * kKeyTile + slot % kKeyTile;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dst[(int64_t)e * kKeyTile] = v0[e];
-        dst[(int64_t)(8 + e) * kKeyTile] = v1[e];
-      }
-      continue;
-    }
-    float cs[kU / 2], sn[kU / 2];
-    const floatx4* cp = reinterpret_cast<const floatx4*>(c.rope_cos + (int64_t)pos * (D / 2) + j / 2);
-    const floatx4* sp = reinterpret_cast<const floatx4*>(c.rope_sin + (int64_t)pos * (D / 2) + j / 2);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const floatx4 c4 = cp[q], s4 = sp[q];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { cs[4 * q + e] = c4[e]; sn[4 * q + e] = s4[e]; }
-    }
-    if (kind == 0)
-      rope_store<uint16_t, kU>(tk + ((int64_t)tok * g.Hkv + hd) * D + j,
-                               kc + (((int64_t)b * g.Hkv + hd) * g.slots + slot) * D + j, cs, sn);
-    else
-      rope_store<uint16_t, kU>(tq + ((int64_t)tok * g.H + hd) * D + j,
-                               qo + (((int64_t)b * g.H + hd) * c.q_rows + cc) * D + j, cs, sn);
-  }
+  const int pos = a.cand_pos[(int64_t)b * a.cand_stride + cc];
+  if (pos < 0 || pos >= g.seq_len) flag_error(a.err, kErrPos);
+  else if (a.seq_tokens) a.seq_tokens[(int64_t)b * g.seq_len + pos] = tok;
 }
 
 // 4. decision and confidence (wave 0).  The exact logit replaces the screened
@@ -743,7 +679,7 @@ __device__ inline void unmask_commit(const Geometry& g, const VocabArgs& a, int 
 template <typename WT>
 __device__ inline void merge_decide(const Geometry& g, const VocabArgs& a, int m, int lane, const float* bestv,
                                     const int* besti, const float* s_m, const float* s_se,
-                                    const float (*s_dot)[kTopK], int& s_tok) {
+                                    const float (*s_dot)[kTopK]) {
   float bm = s_m[0], bse = s_se[0];
   for (int wv = 1; wv < 4; ++wv) lse_merge(bm, bse, s_m[wv], s_se[wv]);
   float ze[kTopK];
@@ -784,7 +720,7 @@ __device__ inline void merge_decide(const Geometry& g, const VocabArgs& a, int m
       if (tb == k) et = terms[1 + k];
     a.conf[m] = (float)(et / tot);
     a.token[m] = besti[tb];
-    s_tok = besti[tb];
+    if (a.cand_pos) unmask_order(g, a, m, besti[tb]);
   }
 }
 
@@ -793,7 +729,6 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
   __shared__ float s_m[4], s_se[4];
   __shared__ Cand s_c[4][kTopK];
   __shared__ float s_dot[4][kTopK];
-  __shared__ int s_tok;
   const int m = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
@@ -883,13 +818,7 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
 #pragma unroll
     for (int k = 0; k < kTopK; ++k) s_dot[wave][k] = dot[k];
   __syncthreads();
-  if (wave == 0) merge_decide<WT>(g, a, m, lane, bestv, besti, s_m, s_se, s_dot, s_tok);
-  if constexpr (sizeof(WT) == 2) {
-    if (a.cand_pos) {
-      __syncthreads();
-      unmask_commit(g, a, m, s_tok);
-    }
-  }
+  if (wave == 0) merge_decide<WT>(g, a, m, lane, bestv, besti, s_m, s_se, s_dot);
 }
 
 
