@@ -846,15 +846,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
     }
   }
 
-  uint32_t off[T::LPW];
-  dma_offsets<D>(wave, lane, off);
-  for (int i = 0; i < kAhead && i < n_my; ++i)
-    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
-
   // Q^T fragment (B operand): lane holds row l32, dims 16t + 8*half + 0..7, RoPE'd.
   // C and R rows read the query table (the mask token at the row's position,
   // the registers); D rows read the queries their append wrote, or, if the
-  // append did not write them, rotate their table row here.
+  // append did not write them, rotate their table row here.  Loaded before
+  // the first tiles are requested: the compiler's wait for the C rows'
+  // positions counts only its own loads, so issued after the tile loads it
+  // would also wait for those.
   bf16x8 qf[NKS];
   {
     const uint16_t* qrow = nullptr;
@@ -904,6 +902,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
       }
     }
   }
+
+  uint32_t off[T::LPW];
+  dma_offsets<D>(wave, lane, off);
+  for (int i = 0; i < kAhead && i < n_my; ++i)
+    tile_dma<D>(a, g, src, tile_ref(a, T0, T1, ord.at(i)), wave, lane, off, ks[i], vs[i]);
 
   // Key row of the K operand for this lane within a 32-key sub-tile: output
   // row r = 8jj + 4hh + ii maps to key 16(jj/2) + 8hh + 4(jj%2) + ii.
