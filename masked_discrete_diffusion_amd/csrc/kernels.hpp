@@ -51,7 +51,7 @@ hipError_t launch_value_tables(const Geometry& g, const void* tv, void* mvt, voi
 constexpr int kAttnMaxDecode = 2048;
 constexpr int kAttnSplitBlocks = 256;   // split only while fewer blocks than this
 constexpr int kAttnMaxSplit = 8;
-constexpr int kAttnMinSplitTiles = 8;   // key tiles per block at least (fewer: the combine pass costs more than the split saves)
+constexpr int kAttnMinSplitTiles = 6;   // key tiles per block at least (fewer: the combine pass costs more than the split saves)
 
 struct AttnArgs {
   const void* tq;
