@@ -96,3 +96,55 @@ def test_order_step_rejects_what_it_cannot_fuse():
         L.mdm_order_step(run32.ctx, 0, None, 0, 0, False, run32.out, None, None)
     assert e.value.status == L.MDM_E_UNSUPPORTED
     run32.close()
+
+
+def test_order_step_without_decode_rows_is_the_attention_alone():
+    """n_decode = 0: the fused call runs the attention only (no logits, no
+    commit), and its output is that of mdm_step_attention on the same state."""
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    cfg = gpu_small_d128()
+    _say("fused order step without decode rows: gpu_small_d128")
+    wl = make_workload(cfg)
+    run = SparseStepRunner(wl, device="cuda")
+    run.prefill()
+    st = run.plan[0]
+    c_ptr, c_stride = run._c_src(st)
+    L.mdm_order_step(run.ctx, 0, c_ptr, c_stride, st.n_c, True, run.out, run.conf, run.token, run.seq_tokens)
+    n_q = st.n_c + cfg.n_registers
+    rows = cfg.batch * n_q * cfg.hidden
+    length = L.mdm_cache_len(run.ctx)
+    run.out.fill_(float("nan"))
+    L.mdm_order_step(run.ctx, st.n_c, None, 0, 0, True, run.out, None, None)
+    torch.cuda.synchronize()
+    fused = run.out[:rows].clone()
+    assert L.mdm_cache_len(run.ctx) == length              # nothing committed
+    run.out.fill_(float("nan"))
+    # the same D rows through the separate call (their queries are the kept ones)
+    d_tok = run.token[:cfg.batch * st.n_c].view(cfg.batch, st.n_c).clone()
+    d_pos = run.order[:, st.c_off:st.c_off + st.n_c].contiguous()
+    L.mdm_step_attention(run.ctx, d_tok, d_pos, st.n_c, st.n_c, None, 0, 0, run.out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(fused).all()
+    assert torch.equal(fused, run.out[:rows])
+    L.mdm_device_status(run.ctx)
+    run.close()
+
+
+def test_fused_generation_repeats_bit_for_bit():
+    """Two fused generations on one context (reset in between) agree bit for
+    bit in every step's output, confidence and token and in the sequence."""
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    cfg = gpu_small_d128()
+    _say("fused determinism: gpu_small_d128")
+    wl = make_workload(cfg)
+    run = SparseStepRunner(wl, device="cuda")
+    steps = list(range(cfg.n_steps))
+    a, sa = run.generate_recorded(keep_o=steps)
+    b, sb = run.generate_recorded(keep_o=steps)
+    run.close()
+    assert np.array_equal(sa, sb)
+    for x, y in zip(a, b):
+        for key in ("o", "conf", "token"):
+            assert np.array_equal(x[key], y[key]), f"step {x['k']}: {key} differs"
