@@ -725,7 +725,7 @@ __device__ inline void merge_decide(const Geometry& g, const VocabArgs& a, int m
 }
 
 template <typename WT>
-__global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
+__global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M, int n_split) {
   __shared__ float s_m[4], s_se[4];
   __shared__ Cand s_c[4][kTopK];
   __shared__ float s_dot[4][kTopK];
@@ -739,12 +739,43 @@ __global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M) {
   Cand c[kTopK];
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
-  for (int tile = threadIdx.x; tile < n_vt; tile += blockDim.x) {
-    const floatx4 p0 = reinterpret_cast<const floatx4*>(part + tile * 8)[0];
-    const floatx4 p1 = reinterpret_cast<const floatx4*>(part + tile * 8)[1];
-    lse_merge(lm, lse, p0[0], p0[1]);
-    cand_insert(c, p0[2], __float_as_int(p0[3]));
-    cand_insert(c, p1[0], __float_as_int(p1[1]));
+  if (n_split > 1) {
+    // hidden was split over blocks and not reduced: sum this row's partial
+    // logits in split order (the screened logits), 16 columns per thread at a time
+    for (int c0 = 16 * threadIdx.x; c0 < g.V; c0 += 16 * blockDim.x) {
+      float vals[16];
+      int idx[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vals[e] = 0.f;
+      for (int sp = 0; sp < n_split; ++sp) {
+        const floatx4* z = reinterpret_cast<const floatx4*>(a.zpart + ((int64_t)sp * M + m) * a.v_pad + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 v = z[q];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) vals[4 * q + ii] += v[ii];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = c0 + e;
+        idx[e] = v;
+        if (a.logits && v < g.V) a.logits[(int64_t)m * g.V + v] = vals[e];
+        if (v >= g.V) vals[e] = kNegInf;
+      }
+      const Top2 t = summarize<16>(vals, idx);
+      lse_merge(lm, lse, t.m, t.se);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cand_insert(c, vals[e], idx[e]);
+    }
+  } else {
+    for (int tile = threadIdx.x; tile < n_vt; tile += blockDim.x) {
+      const floatx4 p0 = reinterpret_cast<const floatx4*>(part + tile * 8)[0];
+      const floatx4 p1 = reinterpret_cast<const floatx4*>(part + tile * 8)[1];
+      lse_merge(lm, lse, p0[0], p0[1]);
+      cand_insert(c, p0[2], __float_as_int(p0[3]));
+      cand_insert(c, p1[0], __float_as_int(p1[1]));
+    }
   }
   wave_lse(lm, lse);
   // wave top-K: K rounds of a (value desc, index asc) argmax; the owner pops
@@ -834,7 +865,7 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_screen_f32, grid, dim3(256), 0, s, g, a, M);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_merge<float>), merge_grid, dim3(256), 0, s, g, a, M);
+    hipLaunchKernelGGL((k_merge<float>), merge_grid, dim3(256), 0, s, g, a, M, 1);
     return hipGetLastError();
   }
   const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
@@ -863,7 +894,7 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     }
     ew = hipGetLastError();
     if (ew != hipSuccess) return ew;
-    hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
+    hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M, 1);
     return hipGetLastError();
   }
   int n_split = 1;
@@ -890,12 +921,16 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
 #undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (n_split > 1) {
+  // a two-way split is summed by the merge itself (two partial rows per
+  // merge row); wider splits of fewer rows go through the reduce launch,
+  // whose grid spreads the sums over the vocabulary tiles
+  const bool fold = n_split == 2;
+  if (n_split > 1 && !fold) {
     hipLaunchKernelGGL(k_screen_reduce, dim3(n_vt, (M + 31) / 32), dim3(256), 0, s, g, pa, M, n_split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M);
+  hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M, fold ? n_split : 1);
   return hipGetLastError();
 }
 
