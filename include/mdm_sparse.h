@@ -22,7 +22,9 @@
  *    buffers registered at init.  It allocates only the host-side context.
  *  - Every compute call is an asynchronous enqueue on the context's stream and
  *    returns after validating its arguments on the host; results are valid
- *    once that stream has been synchronised.  On any error nothing is enqueued.
+ *    once that stream has been synchronised.  On an argument, shape or
+ *    capacity error nothing is enqueued; a launch failure (MDM_E_HIP) inside a
+ *    call of several launches can leave its earlier launches enqueued.
  *  - "bf16" arrays hold bfloat16 bit patterns (uint16); "elem" means bf16 in
  *    MDM_BF16 precision and fp32 in MDM_FP32 precision.
  *  - A context is not thread-safe; use one context per stream.
