@@ -591,6 +591,55 @@ __device__ inline void tile_loop(const AttnArgs& a, const Geometry& g, const KvS
   }
 }
 
+// Quarter role (blocks of five chunks): wavefronts 4-7 share the fifth chunk,
+// wavefront 4 + q taking key half (q & 1) of the tiles of parity (q >> 1), so
+// that each SIMD carries 1.25 chunks instead of one SIMD carrying two.  Phases
+// as in tile_loop; the first half-tile computed sets the fixed reference.  The
+// four partial states are merged at the end of the kernel.
+template <int D, bool FAST>
+__device__ inline void tile_loop_quarter(const AttnArgs& a, const Geometry& g, const KvSrc& src, const TileOrder ord,
+                                         const uint32_t (&off)[AttnTile<D>::LPW],
+                                         uint16_t (*ks)[AttnTile<D>::K_ELEMS], uint16_t (*vs)[AttnTile<D>::V_ELEMS],
+                                         const bf16x8* qf, floatx16* acc, float& m_ref, float& l_run, int T0, int T1,
+                                         int n_comp, int w_end, bool active, int q, int wave, int lane, int krow,
+                                         int half, int l32, float sc, bool& over) {
+  const int tp = q >> 1, hf = q & 1;
+  if (FAST && n_comp > 0) {
+    bool have_ref = false;
+    for (int i = 0; i < n_comp; ++i) {
+      ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+      if ((i & 1) != tp) continue;
+      const int cur = i % kStages;
+      floatx16 sv = s_half<D>(ks[cur], qf, hf, krow, half);
+      if (!have_ref) {
+        m_ref = half_max<false>(sv, 32 * hf, kKeyTile, half, sc);
+        have_ref = true;
+      }
+      finish_half_fixed<D>(sv, vs[cur], hf, acc, m_ref, l_run, half, l32, sc);
+    }
+    over = !(l_run < 0x1p50f);
+  }
+  if (!FAST && n_comp > 0) {
+    for (int i = 0; i < n_comp; ++i) {
+      ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+      if ((i & 1) != tp) continue;
+      const int cur = i % kStages;
+      floatx16 sv = s_half<D>(ks[cur], qf, hf, krow, half);
+      finish_half<D, false>(sv, vs[cur], hf, kKeyTile, acc, m_ref, l_run, half, l32, sc);
+    }
+  }
+  for (int i = max(n_comp, 0); i < ord.n_full; ++i) ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+  for (int i = ord.n_full; i < ord.n; ++i) {
+    ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+    const int t = ord.at(i);
+    if (!active || t >= w_end || (i & 1) != tp) continue;
+    const int valid = tile_ref(a, T0, T1, t).valid;
+    const int cur = i % kStages;
+    floatx16 sv = s_half<D>(ks[cur], qf, hf, krow, half);
+    finish_half<D, true>(sv, vs[cur], hf, valid, acc, m_ref, l_run, half, l32, sc);
+  }
+}
+
 // The result of a wavefront: O = acc / l for its rows, or (key split) the
 // unscaled partial (O, reference, row sum) that k_attn_combine merges.
 // bf16 copies of four consecutive output features (from column col) of query
@@ -738,13 +787,67 @@ __device__ inline void tile_loop_pair(const AttnArgs& a, const Geometry& g, cons
 // are in flight.  Each wavefront waits only for its own loads of tile i
 // (vmcnt counts the younger tiles' loads it may leave outstanding), then the
 // barrier makes every wavefront's part of tile i visible.
-template <int D, bool PAIR>
+// Merge of the four quarter states of the fifth chunk (wavefronts 4-7) into
+// wavefront 4 through LDS (mrg: the free K ring), states added in wavefront
+// order; every quarter wavefront leaves with the group's overflow flag (the
+// four hold the same rows, so they recompute together or not at all).  Called
+// by every wavefront of the block (two barriers).
+template <int D>
+__device__ inline void quad_merge(float* mrg, floatx16* acc, float& m_ref, float& l_run, bool& over, bool quarter,
+                                  int wave, int lane) {
+  constexpr int NDB = D / 32, QW = kAttnWaves / 2, SZ = 16 * NDB + 3;
+  __syncthreads();
+  if (quarter) {
+    float* dst = mrg + (int64_t)(wave - QW) * SZ * kWave + lane;
+    if (wave > QW) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dst[(16 * db + e) * kWave] = acc[db][e];
+      dst[(16 * NDB) * kWave] = m_ref;
+      dst[(16 * NDB + 1) * kWave] = l_run;
+    }
+    dst[(16 * NDB + 2) * kWave] = over ? 1.f : 0.f;
+  }
+  __syncthreads();
+  if (quarter) {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) any |= mrg[((int64_t)j * SZ + 16 * NDB + 2) * kWave + lane] != 0.f;
+    over = any;
+    if (wave == QW) {
+      float m_new = m_ref;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) m_new = fmaxf(m_new, mrg[((int64_t)j * SZ + 16 * NDB) * kWave + lane]);
+      const float a0 = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] *= a0;
+      l_run *= a0;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const float* srcm = mrg + (int64_t)j * SZ * kWave + lane;
+        const float aj = __builtin_amdgcn_exp2f(srcm[(16 * NDB) * kWave] - m_new);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[db][e] += srcm[(16 * db + e) * kWave] * aj;
+        l_run += srcm[(16 * NDB + 1) * kWave] * aj;
+      }
+      m_ref = m_new;
+    }
+  }
+}
+
+template <int D, bool PAIR, bool QUAD>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnArgs a, ChunkPlan cp) {
   using T = AttnTile<D>;
   constexpr int NKS = D / 16;           // k-steps of the QK^T product
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
   __shared__ __align__(1024) uint16_t ks[kStages][T::K_ELEMS];
   __shared__ __align__(1024) uint16_t vs[kStages][T::V_ELEMS];
+  static_assert(!QUAD || 4 * (16 * NDB + 3) * kWave * sizeof(float) <= sizeof(ks), "quarter merge exceeds the K ring");
   __shared__ int kidx[kAttnMaxDecode];
 
   const int n_grid = gridDim.x;
@@ -769,7 +872,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   bool any_cr = false;
   for (int c = c0; c < c1; ++c) any_cr |= (c % cp.n_chunks) >= cp.chunks_d;
   const int parity = PAIR ? wave / (kAttnWaves / 2) : 0;
-  const int ch = c0 + (PAIR ? wave % (kAttnWaves / 2) : wave);
+  // QUAD (blocks of five chunks): wavefronts 4-7 share the fifth chunk
+  const bool quarter = QUAD && wave >= kAttnWaves / 2;
+  const int ch = c0 + (PAIR ? wave % (kAttnWaves / 2) : (quarter ? kAttnWaves / 2 : wave));
   const bool active = ch < c1;
   const int h = kvh * G + (active ? ch / cp.n_chunks : 0);
   int row_base = 0, row_end = 0;
@@ -928,12 +1033,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
   if constexpr (PAIR)
     tile_loop_pair<D, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active, parity,
                             wave, lane, krow, half, l32, sc, over);
-  else if (wave >= kAttnWaves / 2)
+  else if (quarter)
+    tile_loop_quarter<D, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
+                               wave - kAttnWaves / 2, wave, lane, krow, half, l32, sc, over);
+  else if (!QUAD && wave >= kAttnWaves / 2)
     tile_loop<D, true, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active, wave,
                              lane, krow, half, l32, sc, over);
   else
     tile_loop<D, false, true>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_comp, w_end, active,
                               wave, lane, krow, half, l32, sc, over);
+  // the quarter states merge now, so that the vote below needs no state kept
+  // across a second pass
+  float* const mrg = reinterpret_cast<float*>(&ks[0][0]);
+  const bool merged_away = quarter && wave > kAttnWaves / 2;    // state now in wavefront 4
+  if constexpr (QUAD) quad_merge<D>(mrg, acc, m_ref, l_run, over, quarter, wave, lane);
   // A score far above its row's first-tile maximum somewhere in the block:
   // stream the tiles again on the lazily rescaled path.
   // Only the wavefronts whose own rows failed the check recompute (the others
@@ -954,7 +1067,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
     } else {
       // the wavefronts that keep their result write it now, so that no
       // accumulator stays live across the second pass
-      if (!redo) {
+      if (!redo && !merged_away) {
         write_result<D>(a, g, cp, acc, m_ref, l_run, b, row, h, rvalid, active, logical, wave, half, l32);
         written = true;
       }
@@ -973,12 +1086,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
     if constexpr (PAIR)
       tile_loop_pair<D, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end, act_redo,
                                parity, wave, lane, krow, half, l32, sc, unused);
-    else if (wave >= kAttnWaves / 2)
+    else if (quarter)
+      tile_loop_quarter<D, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end,
+                                  act_redo, wave - kAttnWaves / 2, wave, lane, krow, half, l32, sc, unused);
+    else if (!QUAD && wave >= kAttnWaves / 2)
       tile_loop<D, true, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end, act_redo,
                                 wave, lane, krow, half, l32, sc, unused);
     else
       tile_loop<D, false, false>(a, g, src, ord, off, ks, vs, qf, acc, m_ref, l_run, T0, T1, n_redo, w_end,
                                  act_redo, wave, lane, krow, half, l32, sc, unused);
+    if constexpr (QUAD) quad_merge<D>(mrg, acc, m_ref, l_run, unused, quarter, wave, lane);
   }
 
   if constexpr (PAIR) {
@@ -1009,7 +1126,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_bf16(Geometry g, AttnA
     l_run = l_run * a0 + l1 * a1;
     m_ref = m_new;
   }
-  if (!written) write_result<D>(a, g, cp, acc, m_ref, l_run, b, row, h, rvalid, active, logical, wave, half, l32);
+  if (!written && !merged_away)
+    write_result<D>(a, g, cp, acc, m_ref, l_run, b, row, h, rvalid, active, logical, wave, half, l32);
 }
 
 // Merge of the key-split partials: one 256-thread block per chunk (blockIdx =
@@ -1234,12 +1352,17 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
     cp.ksplit = ks;
     cp.real_blocks = groups * ks;
     dim3 grid((cp.real_blocks + 7) / 8 * 8);
+    // blocks of five chunks: the fifth split over wavefronts 4-7 (QUAD)
+    const bool quad = !cp.pair && cp.per_block == kAttnWaves / 2 + 1;
     if (cp.pair) {
-      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
-      else hipLaunchKernelGGL((k_attn_bf16<64, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, true, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_bf16<64, true, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+    } else if (quad) {
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, false, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_bf16<64, false, true>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     } else {
-      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
-      else hipLaunchKernelGGL((k_attn_bf16<64, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      if (g.D == 128) hipLaunchKernelGGL((k_attn_bf16<128, false, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
+      else hipLaunchKernelGGL((k_attn_bf16<64, false, false>), grid, dim3(kAttnThreads), 0, s, g, a, cp);
     }
     if (ks > 1) {
       const dim3 cgrid(groups * kAttnWaves);

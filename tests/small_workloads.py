@@ -87,6 +87,17 @@ def gpu_wide_fixed(index=116, **kw):
     return Config(**base)
 
 
+# Blocks of five query chunks (the fifth split over four wavefronts): 3 x 32
+# heads, 100 rows decoded per step, so steps 2 and 3 have 100 + 100 + 64
+# query rows = 10 chunks per head in two groups of five.
+def gpu_five_chunks(index=118, **kw):
+    base = dict(name="gpu_five_chunks", index=index, batch=3, n_heads=32, n_kv_heads=32, head_dim=128,
+                vocab=300, prompt_len=16, gen_len=300, n_registers=64, n_steps=3,
+                schedule="fixed", per_step=100, order="random", precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
 # Text variants on the HIP path: infilling (four masked spans inside the
 # sequence) with semi-AR blocks decoded in a seeded random order.
 def gpu_text_infill(index=117, **kw):

@@ -106,6 +106,17 @@ def test_generation_matches_oracle(cfgfn):
     _check_generation(cfg, wl, run)
 
 
+def test_five_chunk_blocks_match_oracle():
+    """Steps with 10 query chunks per head run in blocks of five, the fifth
+    chunk split over wavefronts 4-7 by tile parity and key half and merged;
+    every row's output is compared with the oracle."""
+    from small_workloads import gpu_five_chunks
+    cfg = gpu_five_chunks()
+    _say(f"generation parity: {cfg.name}")
+    wl, run = _runner(cfg)
+    _check_generation(cfg, wl, run)
+
+
 def _check_generation(cfg, wl, run, ties=False):
     """ties=True (upper layers): a decision of the two sides may differ only
     where the oracle's own margin is within the tolerance (a top-1/top-2 logit
