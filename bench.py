@@ -484,7 +484,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(),
-                "kernel": "mdm_step_attention: k_attn_bf16<128, pair | lag> (+ k_attn_combine<128> on key-split steps)",
+                "kernel": "mdm_step_attention: k_attn_bf16<128, pair | lag | quad> (+ k_attn_combine<128> on key-split steps)",
                 "calls": n,
                 "launches_per_event_pair": ATT_REPEAT,
                 "avg_call_us": round(att_ms.mean() * 1e3, 2),
