@@ -137,3 +137,15 @@ def test_block_attention_validates_on_the_host():
             L.mdm_block_attention(L.MdmBlockAttnShape(**kw), q, fake, fake, fake, fake, fake, fake, ws, None)
         assert e.value.status == status, (kw, q, ws)
     assert L.mdm_block_attention_workspace_bytes(L.MdmBlockAttnShape(**dict(ok, n_heads=3))) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message before any
+    device work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
