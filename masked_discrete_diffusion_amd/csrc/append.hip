@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void k_rope_scatter(Geometry g, ProjArgs a) {
   const int b = m / a.n_q, r = m % a.n_q;
   const int unit = blockIdx.x * blockDim.x + threadIdx.x;
   const int D = g.D, hd = g.H * g.D, kd = g.Hkv * g.D;
-  if (unit * 8 >= hd + 2 * kd) return;
+  if (unit * 8 >= hd + kd) return;
   const int n0 = unit * 8;
   int pos;
   if (r < a.n_d) pos = a.d_pos[(int64_t)b * a.d_stride + r];
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void k_rope_scatter(Geometry g, ProjArgs a) {
   const floatx4 x1 = reinterpret_cast<const floatx4*>(zr)[1];
   const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   u16x8 y;
-  if (n0 < hd + kd) {
+  {
     const int j = (n0 < hd ? n0 : n0 - hd) % D;            // first dim (even): pairs j/2 .. j/2 + 3
     const float* cs = a.rope_cos + (int64_t)pos * (D / 2) + j / 2;
     const float* sn = a.rope_sin + (int64_t)pos * (D / 2) + j / 2;
@@ -229,22 +229,6 @@ __global__ __launch_bounds__(256) void k_rope_scatter(Geometry g, ProjArgs a) {
         ? static_cast<uint16_t*>(a.kc) + (((int64_t)b * g.Hkv + kvh) * g.slots + a.slot0 + r) * D + j
         : static_cast<uint16_t*>(a.tk) + (((int64_t)b * g.Hkv + kvh) * a.t_pad + (r - a.n_d)) * D + j;
     *reinterpret_cast<u16x8*>(dst) = y;
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = f32_to_bf16(x[e]);
-  const int kvh = (n0 - hd - kd) / D, j = (n0 - hd - kd) % D;
-  if (r < a.n_d) {
-    const int slot = a.slot0 + r;
-    uint16_t* dst = static_cast<uint16_t*>(a.vc) +
-                    ((((int64_t)b * g.Hkv + kvh) * (g.slots / kKeyTile) + slot / kKeyTile) * D + j) * kKeyTile +
-                    slot % kKeyTile;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e * kKeyTile] = y[e];
-  } else {
-    uint16_t* dst = static_cast<uint16_t*>(a.tvt) + (((int64_t)b * g.Hkv + kvh) * D + j) * a.t_pad + (r - a.n_d);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[(int64_t)e * a.t_pad] = y[e];
   }
 }
 
@@ -277,9 +261,59 @@ hipError_t launch_value_tables(const Geometry& g, const void* tv, void* mvt, voi
   return hipGetLastError();
 }
 
+// Upper layers, values: block = 32 consecutive query rows of one sequence x
+// 64 value features, staged in LDS so that the transposed stores (the cache's
+// 64-slot value tiles for D rows, tvt for C|R rows) write each feature's
+// consecutive rows together instead of one 2-byte store per line.
+constexpr int kVsRows = 32, kVsFeat = 64;
+
+__global__ __launch_bounds__(256) void k_value_scatter(Geometry g, ProjArgs a) {
+  __shared__ uint16_t vs[kVsRows][kVsFeat + 2];
+  const int f0 = blockIdx.x * kVsFeat;                    // first value feature (kv head * D + dim)
+  const int r0 = blockIdx.y * kVsRows;
+  const int b = blockIdx.z;
+  const int hd = g.H * g.D, kd = g.Hkv * g.D;
+  const int t = threadIdx.x;
+  {
+    const int lr = t / 8, u = t % 8;                      // row, 8-feature unit
+    const int r = r0 + lr;
+    if (r < a.n_q) {
+      const float* zr = a.z + (int64_t)(b * a.n_q + r) * a.n_pad + hd + kd + f0 + 8 * u;
+      const floatx4 x0 = reinterpret_cast<const floatx4*>(zr)[0];
+      const floatx4 x1 = reinterpret_cast<const floatx4*>(zr)[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vs[lr][8 * u + e] = f32_to_bf16(x0[e]);
+        vs[lr][8 * u + 4 + e] = f32_to_bf16(x1[e]);
+      }
+    }
+  }
+  __syncthreads();
+  const int rr = t % kVsRows;
+  const int r = r0 + rr;
+  if (r >= a.n_q) return;
+#pragma unroll
+  for (int i = 0; i < kVsFeat * kVsRows / 256; ++i) {
+    const int ff = t / kVsRows + i * (256 / kVsRows);     // feature within the block
+    const int f = f0 + ff;
+    const int kvh = f / g.D, j = f % g.D;
+    if (r < a.n_d) {
+      const int slot = a.slot0 + r;
+      static_cast<uint16_t*>(a.vc)[((((int64_t)b * g.Hkv + kvh) * (g.slots / kKeyTile) + slot / kKeyTile) * g.D + j) *
+                                       kKeyTile + slot % kKeyTile] = vs[rr][ff];
+    } else {
+      static_cast<uint16_t*>(a.tvt)[(((int64_t)b * g.Hkv + kvh) * g.D + j) * a.t_pad + (r - a.n_d)] = vs[rr][ff];
+    }
+  }
+}
+
 hipError_t launch_rope_scatter(const Geometry& g, const ProjArgs& a, int M, hipStream_t s) {
-  const int units = (g.H + 2 * g.Hkv) * g.D / 8;
+  const int units = (g.H + g.Hkv) * g.D / 8;                 // queries and keys
   hipLaunchKernelGGL(k_rope_scatter, dim3((units + 255) / 256, M), dim3(256), 0, s, g, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int kd = g.Hkv * g.D;
+  hipLaunchKernelGGL(k_value_scatter, dim3(kd / kVsFeat, (a.n_q + kVsRows - 1) / kVsRows, g.B), dim3(256), 0, s, g, a);
   return hipGetLastError();
 }
 
