@@ -77,7 +77,8 @@ typedef struct {
   int32_t precision;      /* mdm_precision                                            */
   int32_t accurate_conf;  /* bf16 only: nonzero splits h into bf16 hi + lo for the    */
                           /* vocab screening, so confidences are accurate enough to   */
-                          /* rank; zero screens with bf16(h) (argmax still exact)     */
+                          /* rank; zero screens with bf16(h) (the argmax is exact     */
+                          /* either way: see mdm_subset_logits_confidence)            */
   double rope_theta;      /* RoPE base (10000)                                        */
 } mdm_config;
 
@@ -115,9 +116,10 @@ size_t mdm_element_bytes(const mdm_config* cfg);
  * device error flag, builds in the workspace the rows every step reuses (bf16:
  * the RoPE'd keys and queries of the mask token at every position and of the
  * registers, and their values in the layout the attention tiles read), and
- * synchronises the stream once.  The tables tq/tk/tv are read here and by later
- * calls, so they must hold their final contents before init and not change
- * while the context lives.  `stream` is a hipStream_t (NULL = the default
+ * computes the largest row norm of w_vocab (for the decisions' error bound),
+ * and synchronises the stream once.  The tables tq/tk/tv and w_vocab are read
+ * here and by later calls, so they must hold their final contents before init
+ * and not change while the context lives.  `stream` is a hipStream_t (NULL = the default
  * stream).  On success *ctx owns a host allocation released by
  * mdm_sparse_step_destroy. */
 mdm_status mdm_sparse_step_init(mdm_ctx** ctx, const mdm_config* cfg, const mdm_buffers* buf,
@@ -163,10 +165,18 @@ mdm_status mdm_step_attention(mdm_ctx* ctx, const int32_t* d_tok, const int32_t*
 /* Logits for the decoded subset only, with confidence and argmax (page 1, key
  * design 1: only the positions being decoded need logits; page 3, section 3.2).
  * Row c of sequence b is h[b*h_batch_stride + c*H*d .. +H*d) (fp32).  For every
- * row: token = the lowest index of the largest logit, conf = the largest
- * softmax probability (temperature 1).  The bf16 path screens all logits with a
- * bf16 MFMA product, keeps the 4 best candidates per row and re-scores them
- * exactly in fp32 from the fp32 h; the fp32 path computes all logits in fp32.
+ * row: token = the lowest index of the largest logit z = h W^T, conf = the
+ * largest softmax probability (temperature 1).  All logits are first screened
+ * (bf16 path: a bf16 MFMA product of bf16(h), or of its hi + lo split with
+ * accurate_conf; fp32 path: fp32 products), keeping per 128-column tile the
+ * maximum, the sum of exponentials and the three best entries.  The 8 best
+ * entries are then re-scored exactly in fp32 from the fp32 h, and a bound on
+ * the screen's error (Cauchy-Schwarz on h minus its screened copy, times the
+ * largest vocabulary row norm, plus the accumulation error) proves that no
+ * other column reaches the best exact logit; where it cannot, the kernel
+ * re-scores every entry (or whole tile) that might, so the token is the argmax
+ * of the fp32 logits over the whole vocabulary.  conf uses the screened
+ * logits with the re-scored entries' terms exact.
  * conf, token: [B][n_decode].  logits_or_null: if non-NULL, receives the
  * screened logits [B][n_decode][V] (fp32). */
 mdm_status mdm_subset_logits_confidence(mdm_ctx* ctx, const float* h, int64_t h_batch_stride,
@@ -225,6 +235,26 @@ int32_t mdm_cache_len(const mdm_ctx* ctx);
 /* Synchronise the stream, read and clear the kernels' sticky range-check flag.
  * MDM_E_DEVICE if any kernel met an out-of-range token id or position. */
 mdm_status mdm_device_status(mdm_ctx* ctx);
+
+/* Per-row certificate of the logits decisions (page 1, key design 1: the
+ * decision is over the whole vocabulary).  With trace non-NULL (device, 16-byte
+ * aligned, caller-owned, at least B*max_decode rows of 8 floats), every later
+ * mdm_subset_logits_confidence / mdm_order_step writes for decided row m
+ * (= b*n_decode + c) trace[m*8 ..]: {z1, i1, z2, i2, D, eps_s, eps_e, flags}:
+ * z1 the exact fp32 logit of the decided token i1, z2/i2 the best exact logit
+ * among the other re-scored columns, D an upper bound on the screened logit of
+ * every column not re-scored, eps_s / eps_e the bounds on the screen's and the
+ * re-score's error (so D + eps_s < z1 - eps_e proves the argmax), flags bit 0:
+ * entries beyond the 8 candidates were re-scored, bit 1: whole tiles were,
+ * bit 2: z1 - z2 <= 2 eps_e (a tie at fp32 precision), bit 3: the argmax is
+ * proven.  i1, i2 and flags are int32 bit patterns.  NULL turns it off. */
+mdm_status mdm_set_decision_trace(mdm_ctx* ctx, float* trace);
+
+/* Synchronise the stream and read, then clear, the decision counters since the
+ * previous read: out[0] rows that re-scored entries beyond the 8 candidates,
+ * out[1] rows that re-scored whole tiles, out[2] rows whose two best exact
+ * logits were within twice the re-score error bound. */
+mdm_status mdm_decision_counts(mdm_ctx* ctx, int64_t* out);
 
 /* ---- upper layers --------------------------------------------------------
  * A model of L >= 2 attention layers without W_o, MLP or norms: layer l >= 2

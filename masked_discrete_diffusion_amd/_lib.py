@@ -98,6 +98,8 @@ _SIGS = {
     "mdm_sparse_step_reset": (_I32, [_P]),
     "mdm_cache_len": (_I32, [_P]),
     "mdm_device_status": (_I32, [_P]),
+    "mdm_set_decision_trace": (_I32, [_P, _P]),
+    "mdm_decision_counts": (_I32, [_P, ctypes.POINTER(_I64)]),
     "mdm_sparse_step_destroy": (None, [_P]),
     "mdm_last_error": (ctypes.c_char_p, [_P]),
     "mdm_status_string": (ctypes.c_char_p, [_I32]),
@@ -207,6 +209,18 @@ def mdm_cache_len(ctx) -> int:
 
 def mdm_device_status(ctx):
     _check(load().mdm_device_status(ctx), ctx)
+
+
+def mdm_set_decision_trace(ctx, trace):
+    _check(load().mdm_set_decision_trace(ctx, _ptr(trace)), ctx)
+
+
+def mdm_decision_counts(ctx):
+    """(rows re-scored beyond the candidates, rows that re-scored whole tiles,
+    rows whose two best exact logits are within twice the re-score bound)."""
+    out = (_I64 * 3)()
+    _check(load().mdm_decision_counts(ctx, out), ctx)
+    return tuple(int(x) for x in out)
 
 
 def mdm_sparse_step_destroy(ctx):

@@ -53,6 +53,7 @@ bool shape_supported(const mdm_config* c, std::string* why) {
   if (c->head_dim != 64 && c->head_dim != 128) { if (why) *why = "head_dim must be 64 or 128"; return false; }
   const int64_t hidden = (int64_t)c->n_heads * c->head_dim;
   if (hidden % 64) { if (why) *why = "n_heads * head_dim must be a multiple of 64"; return false; }
+  if (hidden > 8192) { if (why) *why = "n_heads * head_dim above 8192"; return false; }
   if ((int64_t)c->vocab + 1 + c->n_registers > INT32_MAX / 2) { if (why) *why = "vocab too large"; return false; }
   return true;
 }
@@ -93,7 +94,8 @@ Layout layout_of(const mdm_config* c) {
   const size_t hbytes = bf16 ? (size_t)L.m_pad * hidden * sizeof(uint16_t) : 0;
   L.hhi = off; off = align_up(off + hbytes, kAlign);
   L.hlo = off; off = align_up(off + ((bf16 && c->accurate_conf) ? hbytes : 0), kAlign);
-  L.partials = off; off = align_up(off + (size_t)L.m_pad * L.n_vt * 8 * sizeof(float), kAlign);
+  // per (row, vocabulary tile) partial records; tiles are at least 32 columns
+  L.partials = off; off = align_up(off + (size_t)L.m_pad * ((c->vocab + 31) / 32) * 8 * sizeof(float), kAlign);
   // split-hidden partial logits: at most 8 splits, capped at 32 MiB (splitting
   // is only chosen when few vocab tiles exist, i.e. for small vocabularies)
   const size_t zfull = 8 * (size_t)c->batch * c->max_decode * L.v_pad * sizeof(float);
@@ -145,6 +147,7 @@ struct mdm_ctx {
   Layout L;
   int len;
   int q_rows;     // rows of the latest append whose queries are in the workspace, or -1
+  float* trace = nullptr;   // per-row decision certificate (mdm_set_decision_trace), or NULL
   std::string err;
   // upper layers (mdm_attach_upper_layers)
   bool has_upper = false;
@@ -175,7 +178,11 @@ mdm_status hip_check(mdm_ctx* ctx, hipError_t e, const char* what) {
   return fail(ctx, MDM_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The first 256 bytes of the workspace: the error flag word, the decision
+// counters (3 x uint32 at byte 64) and max_v ||W_v||_2 (float at byte 128).
 int* err_word(mdm_ctx* c) { return reinterpret_cast<int*>(c->ws() + c->L.err); }
+unsigned* decision_stats(mdm_ctx* c) { return reinterpret_cast<unsigned*>(c->ws() + c->L.err + 64); }
+float* wmax_word(mdm_ctx* c) { return reinterpret_cast<float*>(c->ws() + c->L.err + 128); }
 const float* rope_cos(mdm_ctx* c) { return reinterpret_cast<const float*>(c->ws() + c->L.rope_cos); }
 const float* rope_sin(mdm_ctx* c) { return reinterpret_cast<const float*>(c->ws() + c->L.rope_sin); }
 
@@ -249,7 +256,8 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
   if (st == MDM_OK)
     st = hip_check(ctx, hipMemcpyAsync(ctx->ws() + L.rope_sin, sn.data(), sn.size() * sizeof(float),
                                        hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
-  if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 1, ctx->stream), "clear error flag");
+  if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 64, ctx->stream), "clear error flag");
+  if (st == MDM_OK) st = hip_check(ctx, launch_row_norm_max(g, buf->w_vocab, wmax_word(ctx), ctx->stream), "vocab row norms");
   // The packed logits rows start at zero: rows past a step's count are read
   // by the screen (their logits are never used) and must hold finite values.
   const size_t hwords = g.fp32 ? 0 : (size_t)L.m_pad * g.hidden / 2;
@@ -374,6 +382,9 @@ VocabArgs logits_args(mdm_ctx* ctx, const float* h, int64_t h_batch_stride, int3
   a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
   a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
   a.v_pad = ctx->L.v_pad;
+  a.wmax = wmax_word(ctx);
+  a.stats = decision_stats(ctx);
+  a.trace = ctx->trace;
   return a;
 }
 
@@ -629,6 +640,28 @@ mdm_status mdm_layer_attention(mdm_ctx* ctx, int32_t layer, int32_t n_new_cached
 }
 
 int32_t mdm_cache_len(const mdm_ctx* ctx) { return ctx ? ctx->len : -1; }
+
+mdm_status mdm_set_decision_trace(mdm_ctx* ctx, float* trace) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (reinterpret_cast<uintptr_t>(trace) % 16) return fail(ctx, MDM_E_ARG, "trace must be 16-byte aligned");
+  ctx->trace = trace;
+  return MDM_OK;
+}
+
+mdm_status mdm_decision_counts(mdm_ctx* ctx, int64_t* out) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (!out) return fail(ctx, MDM_E_ARG, "out is NULL");
+  unsigned c[3] = {0, 0, 0};
+  mdm_status st = hip_check(ctx, hipMemcpyAsync(c, decision_stats(ctx), sizeof c, hipMemcpyDeviceToHost, ctx->stream),
+                            "read decision counters");
+  if (st == MDM_OK) st = hip_check(ctx, hipStreamSynchronize(ctx->stream), "synchronize");
+  if (st == MDM_OK)
+    st = hip_check(ctx, launch_fill_i32(reinterpret_cast<int32_t*>(decision_stats(ctx)), 0, 3, ctx->stream),
+                   "clear decision counters");
+  if (st != MDM_OK) return st;
+  for (int i = 0; i < 3; ++i) out[i] = c[i];
+  return MDM_OK;
+}
 
 mdm_status mdm_device_status(mdm_ctx* ctx) {
   if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");

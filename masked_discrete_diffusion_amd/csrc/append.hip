@@ -116,7 +116,10 @@ __global__ __launch_bounds__(256) void k_append(Geometry g, AppendArgs a) {
       pos = g.seq_len + j;
     }
     if (id < 0 || id >= g.table_rows) { flag_error(a.err, kErrTok); id = 0; }
-    if (pos < 0 || pos >= g.max_pos) { flag_error(a.err, kErrPos); pos = 0; }
+    // sequence rows sit at 0..seq_len-1; only the register rows may use the
+    // positions after the sequence
+    const int pos_end = r < a.n_a ? g.seq_len : g.max_pos;
+    if (pos < 0 || pos >= pos_end) { flag_error(a.err, kErrPos); pos = 0; }
   }
 
   const T* tv = static_cast<const T*>(a.tv);

@@ -16,7 +16,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kKeyTile = 64;       // keys per LDS stage in attention; cache slots are a multiple
 constexpr int kVocabTile = 128;    // vocab columns per screening tile (one partial per tile)
-constexpr int kTopK = 4;           // candidates re-scored exactly per row
+constexpr int kCand = 8;           // candidates re-scored exactly per row
 
 // Error bits of the device flag word.
 constexpr int kErrTok = 1;

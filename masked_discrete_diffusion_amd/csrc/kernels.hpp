@@ -105,7 +105,7 @@ struct VocabArgs {
   int n_c;                  // rows per sequence
   uint16_t* hhi;            // [m_pad][hidden] bf16 workspace (bf16 mode)
   uint16_t* hlo;            // [m_pad][hidden] bf16 workspace (accurate mode), or NULL
-  float* partials;          // [m_pad][n_vt][8]
+  float* partials;          // [m_pad][ceil(V / tile_w)][8], tile_w >= 32
   float* zpart;             // split partial logits [n_split][M][v_pad] (bf16 path)
   int64_t zpart_bytes;
   int v_pad;                // V rounded up to the vocab tile
@@ -123,8 +123,20 @@ struct VocabArgs {
   int64_t cand_stride;
   int32_t* seq_tokens;
   int* err;
+  // Decision certificate: wmax = max_v ||W_v||_2 (rounded up, built at init);
+  // trace (optional) [M][8] = {z_best, i_best, z_runner_up, i_runner_up, D, eps_s,
+  // eps_e, flags} per row (int fields as bit patterns); stats (optional) counts
+  // rows that re-scored beyond the candidates, rows that re-scored whole tiles
+  // and rows whose two best exact logits lie within 2 eps_e.
+  const float* wmax;
+  float* trace;
+  unsigned* stats;
+  int n_split;              // set by the launcher: hidden splits summed before the epilogue
+  int tile_w;               // set by the launcher: vocabulary columns per partial record
 };
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
+// max_v ||W_v||_2 of the vocabulary head, rounded up, into *out (which must hold 0)
+hipError_t launch_row_norm_max(const Geometry& g, const void* w, float* out, hipStream_t s);
 
 // Upper layers: y = h_prev W^T for every query row (h_prev fp32, split into
 // bf16 hi + lo; W bf16 [N][hidden] with N = (H + 2 H_kv) d, rows q | k | v),

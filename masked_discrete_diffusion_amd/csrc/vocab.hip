@@ -5,14 +5,17 @@
 //            in a dense [m_pad][hidden] operand, zero rows past M.
 // 2. screen: z^T = W h^T on bf16 MFMA (32x32x16), one 128-column vocab tile by
 //            32/64/128 rows per block; the epilogue keeps per (row, tile) the maximum,
-//            the sum of exp(z - max) and the two best (value, index) pairs, and
+//            the sum of exp(z - max) and the three best (value, index) pairs, and
 //            never writes the logits (unless asked to, for validation).
 //            fp32 mode: the same tile and epilogue with fp32 VALU products.
-// 3. merge:  per row, combine the tiles (max, sum of exp), take the kTopK best
-//            candidates, recompute their logits exactly in fp32 from the fp32 h,
-//            decide the argmax among them (lowest index on ties) and the
-//            confidence exp(z_best - M) / sum exp(z - M), with the candidates'
-//            screened terms replaced by their exact ones.
+// 3. decide: per row, combine the tiles (max, sum of exp), re-score the kCand
+//            best entries exactly in fp32 from the fp32 h, prove from the
+//            screen's error bound that no other column can beat the best of
+//            them (re-scoring more where the bound cannot), decide the argmax
+//            (lowest index on ties) and the confidence exp(z_best - M) / sum
+//            exp(z - M), with the re-scored entries' terms exact.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,51 +27,62 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kKChunk = 64;        // hidden elements per LDS stage
 constexpr int kScreenTargetBlocks = 256;   // split hidden until about this many blocks
 
-struct Top2 {
+// Per (row, vocabulary tile) summary of screened logits: the maximum, the sum
+// of exp(z - max) and the three best (value, index) pairs in rank order
+// (larger value first, lower index on equal values).  Every other column of
+// the tile ranks after the third, so its screened value is at most v3.
+struct Top3 {
   float m;      // running maximum
   float se;     // sum of exp(z - m)
-  float v1, v2;
-  int i1, i2;
+  float v1, v2, v3;
+  int i1, i2, i3;
 };
 
-__device__ inline void top2_push(Top2& t, float v, int i) {
+__device__ inline void top3_push(Top3& t, float v, int i) {
   if (ranks_before(v, i, t.v1, t.i1)) {
-    t.v2 = t.v1; t.i2 = t.i1; t.v1 = v; t.i1 = i;
+    t.v3 = t.v2; t.i3 = t.i2; t.v2 = t.v1; t.i2 = t.i1; t.v1 = v; t.i1 = i;
   } else if (ranks_before(v, i, t.v2, t.i2)) {
-    t.v2 = v; t.i2 = i;
+    t.v3 = t.v2; t.i3 = t.i2; t.v2 = v; t.i2 = i;
+  } else if (ranks_before(v, i, t.v3, t.i3)) {
+    t.v3 = v; t.i3 = i;
   }
 }
 
-__device__ inline Top2 top2_merge(const Top2& a, const Top2& b) {
-  Top2 r;
+__device__ inline Top3 top3_merge(const Top3& a, const Top3& b) {
+  Top3 r;
   r.m = fmaxf(a.m, b.m);
   r.se = (a.m == kNegInf ? 0.f : a.se * expf(a.m - r.m)) + (b.m == kNegInf ? 0.f : b.se * expf(b.m - r.m));
-  r.v1 = a.v1; r.i1 = a.i1; r.v2 = a.v2; r.i2 = a.i2;
-  top2_push(r, b.v1, b.i1);
-  top2_push(r, b.v2, b.i2);
+  r.v1 = a.v1; r.i1 = a.i1; r.v2 = a.v2; r.i2 = a.i2; r.v3 = a.v3; r.i3 = a.i3;
+  top3_push(r, b.v1, b.i1);
+  top3_push(r, b.v2, b.i2);
+  top3_push(r, b.v3, b.i3);
   return r;
 }
 
-__device__ inline Top2 top2_shfl_xor(const Top2& t, int mask) {
-  Top2 o;
+__device__ inline Top3 top3_shfl_xor(const Top3& t, int mask) {
+  Top3 o;
   o.m = __shfl_xor(t.m, mask);
   o.se = __shfl_xor(t.se, mask);
   o.v1 = __shfl_xor(t.v1, mask);
   o.v2 = __shfl_xor(t.v2, mask);
+  o.v3 = __shfl_xor(t.v3, mask);
   o.i1 = __shfl_xor(t.i1, mask);
   o.i2 = __shfl_xor(t.i2, mask);
+  o.i3 = __shfl_xor(t.i3, mask);
   return o;
 }
 
-// Fold a lane's logits into (max, sumexp, top2): values[n] with indices idx[n].
+// Fold a lane's logits into (max, sumexp, top-3): values[n] with indices idx[n].
 template <int N>
-__device__ inline Top2 summarize(const float* vals, const int* idx) {
-  Top2 t;
-  t.m = kNegInf; t.se = 0.f; t.v1 = kNegInf; t.v2 = kNegInf; t.i1 = 0x7fffffff; t.i2 = 0x7fffffff;
+__device__ inline Top3 summarize(const float* vals, const int* idx) {
+  Top3 t;
+  t.m = kNegInf; t.se = 0.f;
+  t.v1 = t.v2 = t.v3 = kNegInf;
+  t.i1 = t.i2 = t.i3 = 0x7fffffff;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     t.m = fmaxf(t.m, vals[e]);
-    top2_push(t, vals[e], idx[e]);
+    top3_push(t, vals[e], idx[e]);
   }
   if (t.m != kNegInf) {
 #pragma unroll
@@ -77,9 +91,10 @@ __device__ inline Top2 summarize(const float* vals, const int* idx) {
   return t;
 }
 
-__device__ inline void store_partial(float* p, const Top2& t) {
+// One 32-byte partial record: {m, se, v1, i1} {v2, i2, v3, i3}.
+__device__ inline void store_partial(float* p, const Top3& t) {
   floatx4 a = {t.m, t.se, t.v1, __int_as_float(t.i1)};
-  floatx4 c = {t.v2, __int_as_float(t.i2), 0.f, 0.f};
+  floatx4 c = {t.v2, __int_as_float(t.i2), t.v3, __int_as_float(t.i3)};
   reinterpret_cast<floatx4*>(p)[0] = a;
   reinterpret_cast<floatx4*>(p)[1] = c;
 }
@@ -147,7 +162,7 @@ struct ScreenStage {
   static constexpr int FIT = 160 * 1024 / (ELEMS * 2);
   static constexpr int NST = FIT >= 5 ? 5 : FIT;                   // ring depth
   static_assert(NST >= 2, "a stage must fit twice");
-  static_assert(NST * ELEMS * 2 >= 4 * 32 * RB * (int)sizeof(float) * 6, "the reduction buffer reuses the ring");
+  static_assert(NST * ELEMS * 2 >= 4 * 32 * RB * (int)sizeof(Top3), "the reduction buffer reuses the ring");
 };
 
 // Physical unit of logical unit u in LDS row r.
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
   constexpr int RBW = S::RBW;
   constexpr int AHEAD = S::NST - 1;
   __shared__ __align__(1024) uint16_t ring[S::NST][S::ELEMS];
-  Top2 (*red)[MT] = reinterpret_cast<Top2 (*)[MT]>(&ring[0][0]);   // after the stages are consumed
+  Top3 (*red)[MT] = reinterpret_cast<Top3 (*)[MT]>(&ring[0][0]);   // after the stages are consumed
 
   const int vt = blockIdx.x;
   const int mt = blockIdx.y;
@@ -299,16 +314,16 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
       vals[e] = v < g.V ? acc[rb][e] : kNegInf;
       if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[rb][e];
     }
-    Top2 t = summarize<16>(vals, idx);
-    t = top2_merge(t, top2_shfl_xor(t, 32));
+    Top3 t = summarize<16>(vals, idx);
+    t = top3_merge(t, top3_shfl_xor(t, 32));
     if (half == 0) red[wv][32 * (rb0 + rb) + l32] = t;
   }
   __syncthreads();
   if (threadIdx.x < MT) {
     const int r = threadIdx.x;
-    Top2 t = red[0][r];
+    Top3 t = red[0][r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) t = top2_merge(t, red[w][r]);
+    for (int w = 1; w < 4; ++w) t = top3_merge(t, red[w][r]);
     const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
     if (m0 + r < a.m_pad) store_partial(a.partials + ((int64_t)(m0 + r) * n_vt + vt) * 8, t);
   }
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     const int r = m0 + 32 * (rb0 + rb) + l32;
-    Top2 tt;
+    Top3 tt;
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb) {
       float vals[16];
@@ -487,10 +502,10 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
         vals[e] = v < g.V ? acc[vb][rb][e] : kNegInf;
         if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[vb][rb][e];
       }
-      const Top2 t = summarize<16>(vals, idx);
-      tt = vb == 0 ? t : top2_merge(tt, t);
+      const Top3 t = summarize<16>(vals, idx);
+      tt = vb == 0 ? t : top3_merge(tt, t);
     }
-    tt = top2_merge(tt, top2_shfl_xor(tt, 32));
+    tt = top3_merge(tt, top3_shfl_xor(tt, 32));
     if (half == 0 && vt < n_vt && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, tt);
   }
 }
@@ -523,9 +538,9 @@ __global__ __launch_bounds__(256) void k_screen_reduce(Geometry g, VocabArgs a, 
     if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = vals[e];
     if (v >= g.V) vals[e] = kNegInf;
   }
-  Top2 t = summarize<16>(vals, idx);
+  Top3 t = summarize<16>(vals, idx);
 #pragma unroll
-  for (int mask = 1; mask < 8; mask <<= 1) t = top2_merge(t, top2_shfl_xor(t, mask));
+  for (int mask = 1; mask < 8; mask <<= 1) t = top3_merge(t, top3_shfl_xor(t, mask));
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
   if (threadIdx.x % 8 == 0 && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, t);
 }
@@ -591,19 +606,38 @@ __global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int
       vals[q] = v < g.V ? acc[i][q] : kNegInf;
       if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = acc[i][q];
     }
-    Top2 tt = summarize<4>(vals, idx);
+    Top3 tt = summarize<4>(vals, idx);
 #pragma unroll
-    for (int mask = 1; mask < 32; mask <<= 1) tt = top2_merge(tt, top2_shfl_xor(tt, mask));
+    for (int mask = 1; mask < 32; mask <<= 1) tt = top3_merge(tt, top3_shfl_xor(tt, mask));
     if (tv == 0 && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, tt);
   }
 }
 
-// ----------------------------------------------------- merge and re-score --
-// One block (4 wavefronts) per row: the threads fold the tiles' (max, sum of
-// exp, top-2) partials, the block keeps the kTopK best candidates, and all
-// threads re-score the candidates together exactly in fp32 from the fp32 h
-// (each thread a slice of hidden for every candidate, then a fixed-order
-// reduction).
+// ---------------------------------------------------- decide (merge) --
+// One wavefront per row (four rows per block).  The decision is the argmax of
+// the exact fp32 logits z = h W^T over the whole vocabulary, which the screen
+// only approximates; the kernel makes that exact as follows.
+//
+// 1. Fold the tiles' (max, sum of exp) and take the kCand best of the tiles'
+//    top-3 entries (and the next one, v_next).
+// 2. Re-score the kCand candidates exactly in fp32 from the fp32 h (each lane
+//    a fixed slice of hidden, fixed-order wavefront sum).  z* = best exact.
+// 3. Every column that was not re-scored has a screened value of at most
+//    D = max(v_next, v3 of each tile whose three entries were all candidates).
+//    A screened value differs from the exact logit by at most
+//      eps_s = (||h - h_s||_2 + gamma(n_s) ||h_s||_2) * max_v ||W_v||_2
+//    (h_s = the screen's rounded copy of h, n_s its accumulation depth;
+//    Cauchy-Schwarz), and a re-scored one by eps_e = gamma(n_e) ||h|| max||W_v||.
+//    If D + eps_s < z* - eps_e no other column can win.  Otherwise (rare) every
+//    tile entry whose screened value reaches tau = z* - eps_e - eps_s is
+//    re-scored too, and every column of a tile whose third entry reaches tau
+//    (its unseen columns may), after which nothing outside the re-scored set
+//    can reach z*.
+// 4. conf = exp(z* - M) / sum exp(z - M) over the screened terms, with the
+//    re-scored candidates' terms replaced by their exact ones (in double).
+// Optional per-row certificate (trace) and per-context counters record the
+// rows that needed step 3's extra re-scoring and the rows whose two best exact
+// logits lie within 2 eps_e of each other (a tie at fp32 precision).
 struct Cand {
   float v;
   int i;
@@ -629,14 +663,17 @@ struct W8<float> {
   }
 };
 
+// Insert (v, i) into the sorted list c (rank order), dropping the last; selects only.
 __device__ inline void cand_insert(Cand* c, float v, int i) {
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    if (ranks_before(v, i, c[k].v, c[k].i)) {
-      const Cand t = c[k];
-      c[k].v = v; c[k].i = i;
-      v = t.v; i = t.i;
-    }
+  for (int k = 0; k < kCand; ++k) {
+    const bool sw = ranks_before(v, i, c[k].v, c[k].i);
+    const float tv = c[k].v;
+    const int ti = c[k].i;
+    c[k].v = sw ? v : tv;
+    c[k].i = sw ? i : ti;
+    v = sw ? tv : v;
+    i = sw ? ti : i;
   }
 }
 
@@ -663,8 +700,17 @@ __device__ inline void wave_lse(float& m, float& se) {
 #undef MDM_LSE_STEP
 }
 
-// Unmasking in a pre-generated order, fused into the merge (page 3, section
-// 3.2: every decoded position is unmasked): the decided token of row
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const int o = __shfl_xor(__float_as_int(x), 1 << s);
+    x = fmaxf(x, __int_as_float(o));
+  }
+  return x;
+}
+
+// Unmasking in a pre-generated order, fused into the decision (page 3,
+// section 3.2: every decoded position is unmasked): the decided token of row
 // m = (b, c) is written at its candidate position in the dense sequence.
 __device__ inline void unmask_order(const Geometry& g, const VocabArgs& a, int m, int tok) {
   const int b = m / a.n_c, cc = m % a.n_c;
@@ -673,185 +719,480 @@ __device__ inline void unmask_order(const Geometry& g, const VocabArgs& a, int m
   else if (a.seq_tokens) a.seq_tokens[(int64_t)b * g.seq_len + pos] = tok;
 }
 
-// 4. decision and confidence (wave 0).  The exact logit replaces the screened
-//    term of each candidate in the sum of exp; the double exps are taken one
-//    per lane and summed by lane 0 in a fixed order.
+// gamma(n) = n u / (1 - n u), u = 2^-24: the bound on the relative error of a
+// sum of n fp32 roundings
+__device__ inline float gamma_f32(float n) {
+  const float nu = n * 5.9604645e-8f;
+  return nu / (1.f - nu);
+}
+
+// Raw 8 elements of a row (16 bytes of bf16 or 32 of fp32) and their values.
 template <typename WT>
-__device__ inline void merge_decide(const Geometry& g, const VocabArgs& a, int m, int lane, const float* bestv,
-                                    const int* besti, const float* s_m, const float* s_se,
-                                    const float (*s_dot)[kTopK]) {
-  float bm = s_m[0], bse = s_se[0];
-  for (int wv = 1; wv < 4; ++wv) lse_merge(bm, bse, s_m[wv], s_se[wv]);
-  float ze[kTopK];
-#pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    const bool ok = besti[k] >= 0 && besti[k] < g.V;
-    ze[k] = ok ? ((s_dot[0][k] + s_dot[1][k]) + (s_dot[2][k] + s_dot[3][k])) : kNegInf;
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u16x8 r;
+  __device__ inline void load(const uint16_t* p) { r = *reinterpret_cast<const u16x8*>(p); }
+  __device__ inline float at(int e) const { return bf16_to_f32(r[e]); }
+};
+template <>
+struct Raw8<float> {
+  floatx4 a, b;
+  __device__ inline void load(const float* p) {
+    a = reinterpret_cast<const floatx4*>(p)[0];
+    b = reinterpret_cast<const floatx4*>(p)[1];
   }
-  int tb = 0;
+  __device__ inline float at(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Lane l's slice of a hidden row: elements [8l + 512j, +8) for j < NIT; the
+// addresses are clamped into the row (every load is issued unconditionally)
+// and elements past the row are zero.
+template <int NIT>
+__device__ inline void load_h_slice(const float* row, int lane, int hidden, float (&x)[NIT][8]) {
+  Raw8<float> raw[NIT];
 #pragma unroll
-  for (int k = 1; k < kTopK; ++k)
-    if (ranks_before(ze[k], besti[k], ze[tb], besti[tb])) tb = k;
-  double mx = bm;
+  for (int j = 0; j < NIT; ++j) raw[j].load(row + min(8 * lane + 512 * j, hidden - 8));
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k)
-    if (ze[k] != kNegInf) mx = fmax(mx, (double)ze[k]);
-  // lane 0: the screened sum; lane 1+k: exact term k; lane 1+kTopK+k: screened term k
-  double arg = (double)bm - mx;
+  for (int j = 0; j < NIT; ++j) {
+    const bool ok = 8 * lane + 512 * j < hidden;
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    if (lane == 1 + k) arg = (double)ze[k] - mx;
-    if (lane == 1 + kTopK + k) arg = (double)bestv[k] - mx;
-  }
-  const double ex = exp(arg);
-  double terms[2 * kTopK + 1];
-#pragma unroll
-  for (int q = 0; q <= 2 * kTopK; ++q) terms[q] = __shfl(ex, q);
-  if (lane == 0) {
-    double tot = (double)bse * terms[0];
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-      if (ze[k] == kNegInf) continue;
-      tot += terms[1 + k] - terms[1 + kTopK + k];
-    }
-    double et = terms[1];
-#pragma unroll
-    for (int k = 1; k < kTopK; ++k)
-      if (tb == k) et = terms[1 + k];
-    a.conf[m] = (float)(et / tot);
-    a.token[m] = besti[tb];
-    if (a.cand_pos) unmask_order(g, a, m, besti[tb]);
+    for (int e = 0; e < 8; ++e) x[j][e] = ok ? raw[j].at(e) : 0.f;
   }
 }
 
-template <typename WT>
-__global__ __launch_bounds__(256) void k_merge(Geometry g, VocabArgs a, int M, int n_split) {
-  __shared__ float s_m[4], s_se[4];
-  __shared__ Cand s_c[4][kTopK];
-  __shared__ float s_dot[4][kTopK];
+// Exact fp32 logit of vocabulary column `col` from the wavefront's slices of h:
+// lane l takes elements [8l + 512j, +8) in order, the lanes' sums are added in
+// a fixed tree (the same order as the candidates' re-score).
+template <typename WT, int NIT>
+__device__ inline float wave_dot(const float (&hr)[NIT][8], const WT* w, int col, int lane, int hidden) {
+  const WT* row = w + (int64_t)col * hidden;
+  Raw8<WT> raw[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) raw[j].load(row + min(8 * lane + 512 * j, hidden - 8));
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NIT; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(hr[j][e], raw[j].at(e), acc);
+  return group_sum<6>(acc);
+}
+
+template <typename WT, int NIT, bool kLo>
+__global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) {
+  constexpr bool kF32 = sizeof(WT) == 4;
+  constexpr int NB = (NIT + 3) / 4;         // 8-element pieces of h per thread (block layout)
+  __shared__ float s_lse[4][2];
+  __shared__ Cand s_c[4][kCand + 1];
+  __shared__ float s_red[4][kCand + 2];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   const int m = blockIdx.x;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
+  const int tw = a.tile_w;                  // vocabulary columns per partial record
+  const int n_vt = (g.V + tw - 1) / tw;
   const float* part = a.partials + (int64_t)m * n_vt * 8;
-
-  // 1. fold the tiles: (max, sum of exp) and each lane's kTopK best
-  float lm = kNegInf, lse = 0.f;
-  Cand c[kTopK];
-#pragma unroll
-  for (int k = 0; k < kTopK; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
-  if (n_split > 1) {
-    // hidden was split over blocks and not reduced: sum this row's partial
-    // logits in split order (the screened logits), 16 columns per thread at a time
-    for (int c0 = 16 * threadIdx.x; c0 < g.V; c0 += 16 * blockDim.x) {
-      float vals[16];
-      int idx[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) vals[e] = 0.f;
-      for (int sp = 0; sp < n_split; ++sp) {
-        const floatx4* z = reinterpret_cast<const floatx4*>(a.zpart + ((int64_t)sp * M + m) * a.v_pad + c0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4 v = z[q];
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) vals[4 * q + ii] += v[ii];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = c0 + e;
-        idx[e] = v;
-        if (a.logits && v < g.V) a.logits[(int64_t)m * g.V + v] = vals[e];
-        if (v >= g.V) vals[e] = kNegInf;
-      }
-      const Top2 t = summarize<16>(vals, idx);
-      lse_merge(lm, lse, t.m, t.se);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) cand_insert(c, vals[e], idx[e]);
-    }
-  } else {
-    for (int tile = threadIdx.x; tile < n_vt; tile += blockDim.x) {
-      const floatx4 p0 = reinterpret_cast<const floatx4*>(part + tile * 8)[0];
-      const floatx4 p1 = reinterpret_cast<const floatx4*>(part + tile * 8)[1];
-      lse_merge(lm, lse, p0[0], p0[1]);
-      cand_insert(c, p0[2], __float_as_int(p0[3]));
-      cand_insert(c, p1[0], __float_as_int(p1[1]));
-    }
-  }
-  wave_lse(lm, lse);
-  // wave top-K: K rounds of a (value desc, index asc) argmax; the owner pops
-#pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    float bv = c[0].v;
-    int bi = c[0].i;
-    group_argmax<6>(bv, bi);
-    if (lane == 0) s_c[wave][k] = Cand{bv, bi};
-    if (bi == c[0].i && bi != 0x7fffffff) {
-#pragma unroll
-      for (int q = 0; q < kTopK - 1; ++q) c[q] = c[q + 1];
-      c[kTopK - 1].v = kNegInf;
-      c[kTopK - 1].i = 0x7fffffff;
-    }
-  }
-  if (lane == 0) { s_m[wave] = lm; s_se[wave] = lse; }
-  __syncthreads();
-
-  // 2. block top-K, taken by every wave from the 4 x kTopK wave candidates in
-  //    lanes 0..15 (indices are distinct: each vocab column lives in one tile)
-  float bestv[kTopK];
-  int besti[kTopK];
-  {
-    float cv = kNegInf;
-    int ci = 0x7fffffff;
-    if (lane < 4 * kTopK) { cv = s_c[lane / kTopK][lane % kTopK].v; ci = s_c[lane / kTopK][lane % kTopK].i; }
-#pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-      float bv = cv;
-      int bi = ci;
-      group_argmax<4>(bv, bi);
-      bestv[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
-      besti[k] = __builtin_amdgcn_readfirstlane(bi);
-      if (ci == besti[k] && ci != 0x7fffffff) { cv = kNegInf; ci = 0x7fffffff; }
-    }
-  }
-
-  // 3. exact fp32 logits of the candidates: thread t takes hidden elements
-  //    [8t + 2048j, +8) for all kTopK candidates, so the h row is read once;
-  //    then a fixed-order sum (lanes, then waves)
+  const WT* w = static_cast<const WT*>(a.w);
   const int b = m / a.n_c, cc = m % a.n_c;
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
-  const WT* w = static_cast<const WT*>(a.w);
-  const WT* wr[kTopK];
+
+  // thread t's piece j of h: elements [8t + 2048 j, +8) (block layout); loaded
+  // first, its latency overlaps the fold; addresses clamped, zero past the row
+  float hb[NB][8];
+  {
+    Raw8<float> raw[NB];
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) {
-    const bool ok = besti[k] >= 0 && besti[k] < g.V;
-    wr[k] = w + (int64_t)(ok ? besti[k] : 0) * g.hidden;
-  }
-  float dot[kTopK];
+    for (int j = 0; j < NB; ++j) raw[j].load(hrow + min(8 * tid + 2048 * j, g.hidden - 8));
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) dot[k] = 0.f;
-#pragma unroll 2
-  for (int e0 = 8 * threadIdx.x; e0 < g.hidden; e0 += 8 * 256) {
-    const floatx4 h0 = reinterpret_cast<const floatx4*>(hrow + e0)[0];
-    const floatx4 h1 = reinterpret_cast<const floatx4*>(hrow + e0)[1];
+    for (int j = 0; j < NB; ++j) {
+      const bool ok = 8 * tid + 2048 * j < g.hidden;
 #pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-      float wv[8];
-      W8<WT>::load(wr[k] + e0, wv);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dot[k] = fmaf(h0[e], wv[e], dot[k]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dot[k] = fmaf(h1[e], wv[4 + e], dot[k]);
+      for (int e = 0; e < 8; ++e) hb[j][e] = ok ? raw[j].at(e) : 0.f;
     }
   }
+
+  // 1. fold the tiles: (max, sum of exp) and the kCand + 1 best entries
+  __shared__ Cand s_best[kCand + 1];
+  __shared__ float s_m, s_se;
+  if (n_vt <= kWave) {
+    // one tile per lane of wavefront 0: its three entries are already in rank order
+    if (wave == 0) {
+      const int t = min(lane, n_vt - 1);
+      const floatx4 p0 = reinterpret_cast<const floatx4*>(part + t * 8)[0];
+      const floatx4 p1 = reinterpret_cast<const floatx4*>(part + t * 8)[1];
+      const bool own = lane < n_vt;
+      float lm = own ? p0[0] : kNegInf, lse = own ? p0[1] : 0.f;
+      Cand h3[3] = {{own ? p0[2] : kNegInf, own ? __float_as_int(p0[3]) : 0x7fffffff},
+                    {own ? p1[0] : kNegInf, own ? __float_as_int(p1[1]) : 0x7fffffff},
+                    {own ? p1[2] : kNegInf, own ? __float_as_int(p1[3]) : 0x7fffffff}};
+      wave_lse(lm, lse);
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) dot[k] = group_sum<6>(dot[k]);
-  if (lane == 0)
+      for (int k = 0; k <= kCand; ++k) {
+        float bv = h3[0].v;
+        int bi = h3[0].i;
+        group_argmax<6>(bv, bi);
+        if (lane == 0) s_best[k] = Cand{bv, bi};
+        const bool pop = bi == h3[0].i && bi != 0x7fffffff;
+        h3[0].v = pop ? h3[1].v : h3[0].v; h3[0].i = pop ? h3[1].i : h3[0].i;
+        h3[1].v = pop ? h3[2].v : h3[1].v; h3[1].i = pop ? h3[2].i : h3[1].i;
+        h3[2].v = pop ? kNegInf : h3[2].v; h3[2].i = pop ? 0x7fffffff : h3[2].i;
+      }
+      if (lane == 0) { s_m = lm; s_se = lse; }
+    }
+  } else {
+    // several tiles per thread (large vocabularies): sorted insertion, then a
+    // block merge of the wavefronts' top-(kCand + 1)
+    float lm = kNegInf, lse = 0.f;
+    Cand c[kCand];
 #pragma unroll
-    for (int k = 0; k < kTopK; ++k) s_dot[wave][k] = dot[k];
+    for (int k = 0; k < kCand; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
+    auto fold4 = [&](int t0) {
+      floatx4 p0[4], p1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = min(t0 + u * 256 + tid, n_vt - 1);
+        p0[u] = reinterpret_cast<const floatx4*>(part + t * 8)[0];
+        p1[u] = reinterpret_cast<const floatx4*>(part + t * 8)[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + u * 256 + tid < n_vt) {
+          lse_merge(lm, lse, p0[u][0], p0[u][1]);
+          cand_insert(c, p0[u][2], __float_as_int(p0[u][3]));
+          cand_insert(c, p1[u][0], __float_as_int(p1[u][1]));
+          cand_insert(c, p1[u][2], __float_as_int(p1[u][3]));
+        }
+      }
+    };
+    fold4(0);                               // straight-line for up to 1024 tiles
+    for (int t0 = 1024; t0 < n_vt; t0 += 1024) fold4(t0);
+    wave_lse(lm, lse);
+#pragma unroll
+    for (int k = 0; k <= kCand; ++k) {
+      float bv = c[0].v;
+      int bi = c[0].i;
+      group_argmax<6>(bv, bi);
+      if (lane == 0) s_c[wave][k] = Cand{bv, bi};
+      const bool pop = bi == c[0].i && bi != 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < kCand - 1; ++q) {
+        c[q].v = pop ? c[q + 1].v : c[q].v;
+        c[q].i = pop ? c[q + 1].i : c[q].i;
+      }
+      c[kCand - 1].v = pop ? kNegInf : c[kCand - 1].v;
+      c[kCand - 1].i = pop ? 0x7fffffff : c[kCand - 1].i;
+    }
+    if (lane == 0) { s_lse[wave][0] = lm; s_lse[wave][1] = lse; }
+    __syncthreads();
+    if (wave == 0) {
+      // block top-(kCand + 1) from the 4 x (kCand + 1) wavefront entries
+      // (indices are distinct: each column lives in one tile)
+      float cv = kNegInf;
+      int ci = 0x7fffffff;
+      if (lane < 4 * (kCand + 1)) { cv = s_c[lane / (kCand + 1)][lane % (kCand + 1)].v; ci = s_c[lane / (kCand + 1)][lane % (kCand + 1)].i; }
+#pragma unroll
+      for (int k = 0; k <= kCand; ++k) {
+        float bv = cv;
+        int bi = ci;
+        group_argmax<6>(bv, bi);
+        if (lane == 0) s_best[k] = Cand{bv, bi};
+        const bool pop = ci == bi && ci != 0x7fffffff;
+        cv = pop ? kNegInf : cv;
+        ci = pop ? 0x7fffffff : ci;
+      }
+      if (lane == 0) {
+        float m0 = s_lse[0][0], se0 = s_lse[0][1];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) lse_merge(m0, se0, s_lse[q][0], s_lse[q][1]);
+        s_m = m0; s_se = se0;
+      }
+    }
+  }
   __syncthreads();
-  if (wave == 0) merge_decide<WT>(g, a, m, lane, bestv, besti, s_m, s_se, s_dot);
+  float bestv[kCand + 1];
+  int besti[kCand + 1];
+#pragma unroll
+  for (int k = 0; k <= kCand; ++k) { bestv[k] = s_best[k].v; besti[k] = s_best[k].i; }
+  const float lm = s_m, lse = s_se;
+
+  // 2. exact fp32 logits of the candidates: every thread loads its pieces of
+  //    the kCand rows at once, then a fixed-order sum (lanes, then wavefronts)
+  float dot[kCand], hh = 0.f, dd = 0.f;
+  {
+    Raw8<WT> raw[NB][kCand];
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+      const WT* crow = w + (int64_t)((besti[k] >= 0 && besti[k] < g.V) ? besti[k] : 0) * g.hidden;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) raw[j][k].load(crow + min(8 * tid + 2048 * j, g.hidden - 8));
+    }
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) dot[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = hb[j][e];
+        hh = fmaf(x, x, hh);
+        if constexpr (!kF32) {
+          const float hi = bf16_to_f32(f32_to_bf16(x));
+          float r = x - hi;                  // exact (x and hi share the leading bits)
+          if constexpr (kLo) r -= bf16_to_f32(f32_to_bf16(r));
+          dd = fmaf(r, r, dd);
+        }
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) dot[k] = fmaf(x, raw[j][k].at(e), dot[k]);
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) dot[k] = group_sum<6>(dot[k]);
+  hh = group_sum<6>(hh);
+  dd = group_sum<6>(dd);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) s_red[wave][k] = dot[k];
+    s_red[wave][kCand] = hh;
+    s_red[wave][kCand + 1] = dd;
+  }
+  __syncthreads();
+  // every wavefront forms the same exact logits and bounds (uniform values)
+  float ze[kCand];
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) {
+    const float z = (s_red[0][k] + s_red[1][k]) + (s_red[2][k] + s_red[3][k]);
+    ze[k] = (besti[k] >= 0 && besti[k] < g.V) ? z : kNegInf;
+  }
+  hh = (s_red[0][kCand] + s_red[1][kCand]) + (s_red[2][kCand] + s_red[3][kCand]);
+  dd = (s_red[0][kCand + 1] + s_red[1][kCand + 1]) + (s_red[2][kCand + 1] + s_red[3][kCand + 1]);
+  // error bounds (rounded up by a small factor for the fp32 evaluation of the norms)
+  const float wmax = *a.wmax;
+  const float hn = sqrtf(hh) * 1.0001f;
+  // accumulation depth of a screened logit: sequential fp32 FMAs (fp32 screen);
+  // for the MFMA screen every 32x32x16 step is counted as 17 roundings of up
+  // to 2u each (products of bf16 values are exact in fp32; the order and
+  // rounding inside an MFMA are not relied on), plus the split sums
+  const float n_s = kF32 ? (float)g.hidden + 8.f
+                         : 2.f * ((float)(g.hidden / 16) * 17.f * (kLo ? 2.f : 1.f) + 8.f + (float)a.n_split);
+  const float eps_s = (sqrtf(dd) * 1.0001f + gamma_f32(n_s) * hn * 1.01f) * wmax;
+  // the re-scores: candidates and single entries take at most max(8 NB, 8 NIT)
+  // sequential FMAs per thread and 8 tree levels; whole tiles hidden / 2 FMAs
+  // per thread and one addition
+  const float eps_e = gamma_f32((float)max(8 * NB, 8 * NIT) + 8.f) * hn * wmax;
+  const float eps_f = gamma_f32((float)(g.hidden / 2) + 1.f) * hn * wmax;
+
+  int tb = 0;
+#pragma unroll
+  for (int k = 1; k < kCand; ++k)
+    if (ranks_before(ze[k], besti[k], ze[tb], besti[tb])) tb = k;
+  float zbest = ze[0];
+  int ibest = besti[0];
+#pragma unroll
+  for (int k = 1; k < kCand; ++k)
+    if (tb == k) { zbest = ze[k]; ibest = besti[k]; }
+
+  // 3. the bound on every column left out, and the re-scoring it may call for
+  float dmax = bestv[kCand];
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) {
+    int same = 0;
+#pragma unroll
+    for (int q = 0; q < kCand; ++q) same += (besti[q] / tw == besti[k] / tw) ? 1 : 0;
+    // a tile with all three entries among the candidates: its other columns rank after its third
+    bool last = true;
+#pragma unroll
+    for (int q = k + 1; q < kCand; ++q) last = last && (besti[q] / tw != besti[k] / tw);
+    if (same == 3 && last && besti[k] != 0x7fffffff) dmax = fmaxf(dmax, bestv[k]);
+  }
+  const bool rescan = dmax != kNegInf && dmax + eps_s >= zbest - eps_e;   // uniform over the block
+  if (!rescan && wave != 0) return;         // the rest is wavefront 0's unless the block re-scores
+  int flags = 0;
+  float zrun = kNegInf;              // runner-up exact logit among everything re-scored
+  int irun = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < kCand; ++k)
+    if (k != tb && ranks_before(ze[k], besti[k], zrun, irun)) { zrun = ze[k]; irun = besti[k]; }
+  // conf sum relative to the screened maximum lm: exact minus screened terms of
+  // the re-scored entries (double, one term per lane, fixed-order sum)
+  double extra = 0.0;
+  {
+    float zk = kNegInf, sk = 0.f;           // lane k < kCand takes candidate k
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+      zk = lane == k ? ze[k] : zk;
+      sk = lane == k ? bestv[k] : sk;
+    }
+    const double term = zk == kNegInf ? 0.0 : exp((double)zk - (double)lm) - exp((double)sk - (double)lm);
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) extra += __shfl(term, k);
+  }
+
+  if (rescan) {
+    // Rare.  Every wavefront scans the tiles in order (the same values in each);
+    // wavefront 0 re-scores the single entries at or above tau one by one
+    // (wavefront dots, lane l taking elements [8l + 512j, +8)); a tile whose
+    // third entry reaches tau is re-scored whole by the block, two threads per
+    // column (elements [0, hidden/2) and [hidden/2, hidden), added in that order).
+    __shared__ Cand s_ft[4][2];
+    flags |= 1;
+    float hr[NIT][8];
+    load_h_slice<NIT>(hrow, lane, g.hidden, hr);
+    const float tau = zbest - eps_e - eps_s;
+    float dafter = kNegInf;
+    for (int t0 = 0; t0 < n_vt; t0 += kWave) {
+      const int t = t0 + lane;
+      float v[3] = {kNegInf, kNegInf, kNegInf};
+      int ix[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
+      if (t < n_vt) {
+        const floatx4 p0 = reinterpret_cast<const floatx4*>(part + t * 8)[0];
+        const floatx4 p1 = reinterpret_cast<const floatx4*>(part + t * 8)[1];
+        v[0] = p0[2]; ix[0] = __float_as_int(p0[3]);
+        v[1] = p1[0]; ix[1] = __float_as_int(p1[1]);
+        v[2] = p1[2]; ix[2] = __float_as_int(p1[3]);
+      }
+      const bool full = t < n_vt && v[2] >= tau;
+      if (!full) dafter = fmaxf(dafter, v[2]);          // the tile's unseen columns
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        bool is_cand = false;
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) is_cand = is_cand || (besti[k] == ix[q]);
+        const bool want = v[q] >= tau && !is_cand && ix[q] >= 0 && ix[q] < g.V;
+        if (!want && !is_cand) dafter = fmaxf(dafter, v[q]);
+        uint64_t mask = wave == 0 ? __ballot(want) : 0ull;
+        while (mask) {
+          const int src = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const int col = __shfl(ix[q], src);
+          const float scr = __shfl(v[q], src);
+          const float z = wave_dot<WT, NIT>(hr, w, col, lane, g.hidden);
+          extra += exp((double)z - (double)lm) - exp((double)scr - (double)lm);
+          if (ranks_before(z, col, zbest, ibest)) {
+            zrun = zbest; irun = ibest; zbest = z; ibest = col;
+          } else if (ranks_before(z, col, zrun, irun)) {
+            zrun = z; irun = col;
+          }
+        }
+      }
+      uint64_t fmask = __ballot(full);      // the same in every wavefront
+      while (fmask) {
+        flags |= 2;
+        const int tile = t0 + __builtin_ctzll(fmask);
+        fmask &= fmask - 1;
+        // block re-score of the tile's columns (their screened terms stay in
+        // the conf sum: only the decision uses them)
+        const int col = tile * tw + (tid >> 1), hf = tid & 1;
+        bool ok = (tid >> 1) < tw && col < g.V;
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) ok = ok && besti[k] != col;
+        float acc = 0.f;
+        if ((tid >> 1) < tw) {
+          const int half_len = g.hidden / 2;
+          const float* hp = hrow + hf * half_len;
+          const WT* wp = w + (int64_t)min(col, g.V - 1) * g.hidden + hf * half_len;
+          for (int e0 = 0; e0 < half_len; e0 += 8) {
+            Raw8<float> hx;
+            Raw8<WT> wx;
+            hx.load(hp + e0);
+            wx.load(wp + e0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(hx.at(e), wx.at(e), acc);
+          }
+        }
+        const float other = __shfl_xor(acc, 1);
+        float z = hf == 0 ? acc + other : other + acc;
+        float bv = ok ? z : kNegInf;
+        int bi = ok ? col : 0x7fffffff;
+        // the block's two best columns of the tile
+        float b1 = bv;
+        int i1 = bi;
+        group_argmax<6>(b1, i1);
+        const bool pop = bi == i1;
+        float b2 = pop ? kNegInf : bv;
+        int i2 = pop ? 0x7fffffff : bi;
+        group_argmax<6>(b2, i2);
+        if (lane == 0) { s_ft[wave][0] = Cand{b1, i1}; s_ft[wave][1] = Cand{b2, i2}; }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const float zc = s_ft[q][r].v;
+              const int cc2 = s_ft[q][r].i;
+              if (cc2 == 0x7fffffff) continue;
+              if (ranks_before(zc, cc2, zbest, ibest)) {
+                zrun = zbest; irun = ibest; zbest = zc; ibest = cc2;
+              } else if (ranks_before(zc, cc2, zrun, irun)) {
+                zrun = zc; irun = cc2;
+              }
+            }
+        }
+        __syncthreads();
+      }
+    }
+    if (wave != 0) return;
+    dmax = wave_max(dafter);
+  }
+  const float eps_r = (flags & 2) ? fmaxf(eps_e, eps_f) : eps_e;
+  if (zrun != kNegInf && zbest - zrun <= 2.f * eps_r) flags |= 4;
+  if (dmax == kNegInf || dmax + eps_s < zbest - eps_e) flags |= 8;
+
+  // 4. confidence = exp(z* - lm) / (sum of exp(z - lm)): screened terms with
+  //    the re-scored entries' terms replaced by their exact ones
+  if (lane == 0) {
+    const double tot = (lm == kNegInf ? 0.0 : (double)lse) + extra;
+    a.conf[m] = (float)(exp((double)zbest - (double)lm) / tot);
+    a.token[m] = ibest;
+    if (a.cand_pos) unmask_order(g, a, m, ibest);
+    if (a.trace) {
+      floatx4 t0 = {zbest, __int_as_float(ibest), zrun, __int_as_float(irun)};
+      floatx4 t1 = {dmax, eps_s, eps_e, __int_as_float(flags)};
+      reinterpret_cast<floatx4*>(a.trace + (int64_t)m * 8)[0] = t0;
+      reinterpret_cast<floatx4*>(a.trace + (int64_t)m * 8)[1] = t1;
+    }
+    if (a.stats) {
+      if (flags & 1) atomicAdd(&a.stats[0], 1u);
+      if (flags & 2) atomicAdd(&a.stats[1], 1u);
+      if (flags & 4) atomicAdd(&a.stats[2], 1u);
+    }
+  }
 }
 
+template <typename WT, bool kLo>
+hipError_t launch_decide_lo(const Geometry& g, const VocabArgs& a, int M, hipStream_t s) {
+  const dim3 grid(M), block(256);
+  const int nit = (g.hidden + 511) / 512;
+  if (nit <= 1) hipLaunchKernelGGL((k_decide<WT, 1, kLo>), grid, block, 0, s, g, a, M);
+  else if (nit <= 2) hipLaunchKernelGGL((k_decide<WT, 2, kLo>), grid, block, 0, s, g, a, M);
+  else if (nit <= 4) hipLaunchKernelGGL((k_decide<WT, 4, kLo>), grid, block, 0, s, g, a, M);
+  else if (nit <= 8) hipLaunchKernelGGL((k_decide<WT, 8, kLo>), grid, block, 0, s, g, a, M);
+  else hipLaunchKernelGGL((k_decide<WT, 16, kLo>), grid, block, 0, s, g, a, M);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t launch_decide(const Geometry& g, const VocabArgs& a, int M, hipStream_t s) {
+  if constexpr (!std::is_same<WT, float>::value)
+    if (a.hlo) return launch_decide_lo<WT, true>(g, a, M, s);
+  return launch_decide_lo<WT, false>(g, a, M, s);
+}
+
+// max_v ||W_v||_2 (rounded up) into *out: one wavefront per vocabulary row
+template <typename WT>
+__global__ __launch_bounds__(256) void k_row_norm_max(Geometry g, const WT* w, float* out) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (row >= g.V) return;
+  float acc = 0.f;
+  for (int e0 = 8 * lane; e0 < g.hidden; e0 += 512) {
+    float wv[8];
+    W8<WT>::load(w + (int64_t)row * g.hidden + e0, wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(wv[e], wv[e], acc);
+  }
+  acc = group_sum<6>(acc);
+  // the fp32 sum of squares is within gamma(hidden/64 + 6) of exact: round up
+  const float nrm = sqrtf(acc * (1.f + gamma_f32((float)(g.hidden / 64 + 8)))) * 1.00001f;
+  if (lane == 0) atomicMax(reinterpret_cast<unsigned*>(out), __float_as_uint(nrm));
+}
 
 }  // namespace
 
@@ -859,14 +1200,15 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   const int M = g.B * a.n_c;
   if (M <= 0) return hipSuccess;
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
-  const dim3 merge_grid(M);
   if (g.fp32) {
     dim3 grid(n_vt, (M + 31) / 32);
     hipLaunchKernelGGL(k_screen_f32, grid, dim3(256), 0, s, g, a, M);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_merge<float>), merge_grid, dim3(256), 0, s, g, a, M, 1);
-    return hipGetLastError();
+    VocabArgs da = a;
+    da.n_split = 1;
+    da.tile_w = kVocabTile;
+    return launch_decide<float>(g, da, M, s);
   }
   const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   const int mt_rows = 32 * rb;
@@ -894,8 +1236,9 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     }
     ew = hipGetLastError();
     if (ew != hipSuccess) return ew;
-    hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M, 1);
-    return hipGetLastError();
+    pa.n_split = 1;
+    pa.tile_w = kVocabTile;
+    return launch_decide<uint16_t>(g, pa, M, s);
   }
   int n_split = 1;
   const int chunks = g.hidden / kKChunk;
@@ -921,16 +1264,22 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
 #undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // a two-way split is summed by the merge itself (two partial rows per
-  // merge row); wider splits of fewer rows go through the reduce launch,
+  // split partial logits are summed in split order by the reduce launch,
   // whose grid spreads the sums over the vocabulary tiles
-  const bool fold = n_split == 2;
-  if (n_split > 1 && !fold) {
+  if (n_split > 1) {
     hipLaunchKernelGGL(k_screen_reduce, dim3(n_vt, (M + 31) / 32), dim3(256), 0, s, g, pa, M, n_split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_merge<uint16_t>), merge_grid, dim3(256), 0, s, g, pa, M, fold ? n_split : 1);
+  pa.n_split = n_split;
+  pa.tile_w = kVocabTile;
+  return launch_decide<uint16_t>(g, pa, M, s);
+}
+
+hipError_t launch_row_norm_max(const Geometry& g, const void* w, float* out, hipStream_t s) {
+  const dim3 grid((g.V + 3) / 4), block(256);
+  if (g.fp32) hipLaunchKernelGGL((k_row_norm_max<float>), grid, block, 0, s, g, static_cast<const float*>(w), out);
+  else hipLaunchKernelGGL((k_row_norm_max<uint16_t>), grid, block, 0, s, g, static_cast<const uint16_t*>(w), out);
   return hipGetLastError();
 }
 

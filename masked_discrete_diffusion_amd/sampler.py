@@ -235,10 +235,19 @@ class SparseStepRunner:
         for k in range(len(self.plan) if n_steps is None else n_steps):
             self.step(k)
 
-    def generate_recorded(self, n_steps: Optional[int] = None, keep_o=(), keep_logits=()):
-        """Eager generation that copies each step's decisions back to the host."""
+    def generate_recorded(self, n_steps: Optional[int] = None, keep_o=(), keep_logits=(), trace: bool = False):
+        """Eager generation that copies each step's decisions back to the host.
+        With trace, every step also records the decisions' certificate rows
+        (mdm_set_decision_trace); the decision counters of the generation are
+        left in self.decision_counts."""
         cfg = self.cfg
         B = cfg.batch
+        tbuf = None
+        if trace:
+            max_decode = max(p.n_c for p in self.plan)
+            tbuf = torch.zeros(B * max_decode * 8, dtype=torch.float32, device=self.device)
+            L.mdm_set_decision_trace(self.ctx, tbuf)
+        L.mdm_decision_counts(self.ctx)                 # clear
         self.seq_tokens.copy_(self.seq0)
         self.prefill()
         recs = []
@@ -270,8 +279,13 @@ class SparseStepRunner:
                 rec["o"] = self.out[:B * n_q * cfg.hidden].view(B, n_q, cfg.hidden).cpu().numpy().copy()
             if lg is not None:
                 rec["logits"] = lg.view(B, st.n_c, cfg.vocab).cpu().numpy()
+            if tbuf is not None:
+                rec["trace"] = tbuf[:B * st.n_c * 8].view(B, st.n_c, 8).cpu().numpy().copy()
             recs.append(rec)
+        if tbuf is not None:
+            L.mdm_set_decision_trace(self.ctx, None)
         L.mdm_device_status(self.ctx)
+        self.decision_counts = L.mdm_decision_counts(self.ctx)
         return recs, self.seq_tokens.cpu().numpy().copy()
 
     def capture_graph(self, n_steps: Optional[int] = None) -> torch.cuda.CUDAGraph:

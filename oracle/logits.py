@@ -44,3 +44,15 @@ def decide(z: np.ndarray):
     top2 = -np.sort(-z, axis=-1)[..., :2]
     margin = top2[..., 0] - top2[..., 1] if z.shape[-1] > 1 else np.full(z.shape[:-1], np.inf)
     return token.astype(np.int64), round_f32(conf64), conf64, margin
+
+
+def top_two(z: np.ndarray):
+    """Per row the two best (index, value) pairs of the float64 logits, in rank
+    order: larger value first, lower index on equal values.  Returns idx [n, 2]
+    (int64) and val [n, 2] (float64).  Used as the reference for the per-decision
+    certificate (how far the decision is from a tie, and how close a measured
+    logit is to the exact one)."""
+    z = np.asarray(z, dtype=np.float64)
+    # a stable sort of -z keeps equal values in index order
+    order = np.argsort(-z, axis=-1, kind="stable")[..., :2]
+    return order.astype(np.int64), np.take_along_axis(z, order, axis=-1)

@@ -38,10 +38,21 @@ import numpy as np
 
 from . import rope
 from .attention import attend
-from .logits import decide, subset_logits
+from .logits import decide, subset_logits, top_two
 from .masks import step_mask
 from .numerics import round_bf16, round_storage, table_values
 from .select import select_all, select_by_confidence
+
+
+def split_layer2(w_rows: np.ndarray, hq: int, hk: int):
+    """Layer-2 projection matrices from the stored weight rows.
+
+    The rows of W_2 [(H + 2 H_kv) d][hidden] are the query heads, then the key
+    heads, then the value heads; output feature j of a row is the dot product
+    of the layer-1 output h1 with row j.  Returned as (Wq, Wk, Wv) laid out
+    [hidden][features], so that q = h1 @ Wq.
+    """
+    return w_rows[:hq].T, w_rows[hq:hq + hk].T, w_rows[hq + hk:hq + 2 * hk].T
 
 
 @dataclass
@@ -71,9 +82,8 @@ class Model:
         if layer2 is None and getattr(wl, "layer_w", None):
             if len(wl.layer_w) != 1:
                 raise ValueError("the oracle models at most two layers")
-            w2 = table_values(wl.layer_w[0])                  # [q | k | v rows][hidden]
-            hq, hk = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
-            layer2 = (w2[:hq].T, w2[hq:hq + hk].T, w2[hq + hk:].T)
+            layer2 = split_layer2(table_values(wl.layer_w[0]), cfg.n_heads * cfg.head_dim,
+                                  cfg.n_kv_heads * cfg.head_dim)
         return cls(n_heads=cfg.n_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
                    vocab=cfg.vocab, n_registers=cfg.n_registers, seq_len=cfg.seq_len,
                    tq=wl.tq, tk=wl.tk, tv=wl.tv, w=table_values(wl.w_vocab),
@@ -204,6 +214,8 @@ class StepRecord:
     conf32: list
     conf64: list
     margin: list
+    top2_idx: list            # per sequence: [n_C, 2] the two best vocabulary indices (float64 logits)
+    top2_val: list            # per sequence: [n_C, 2] their logits
     selected: list            # per sequence: indices into c_pos that are unmasked
     conf_gap: list            # per sequence: conf32 gap at the top-n cut (semi-AR), else nan
     o: Optional[list] = None          # per sequence [n_q, hidden] (kept steps only)
@@ -255,8 +267,9 @@ def run_workload(wl, batches=None, n_steps: Optional[int] = None, keep_steps=(),
         h = np.concatenate([o.h for o in outs])
         z = subset_logits(h, model.w)
         token, conf32, conf64, margin = decide(z)
+        t2_idx, t2_val = top_two(z)
         rec = StepRecord(k=k, d_pos=[d[1] for d in d_state], c_pos=c_list, token=[], conf32=[],
-                         conf64=[], margin=[], selected=[], conf_gap=[])
+                         conf64=[], margin=[], top2_idx=[], top2_val=[], selected=[], conf_gap=[])
         off = 0
         step_unmask = []
         for i, b in enumerate(batches):
@@ -273,6 +286,8 @@ def run_workload(wl, batches=None, n_steps: Optional[int] = None, keep_steps=(),
             rec.conf32.append(c32)
             rec.conf64.append(conf64[off:off + n_c])
             rec.margin.append(margin[off:off + n_c])
+            rec.top2_idx.append(t2_idx[off:off + n_c])
+            rec.top2_val.append(t2_val[off:off + n_c])
             rec.selected.append(sel)
             rec.conf_gap.append(gap)
             u_pos, u_tok = c_list[i][sel], tk[sel]

@@ -15,6 +15,12 @@ HIP path plays no part.  For each workload it stores, in
   o_steps   steps whose attention output rows were sampled
   o_rows    [len(o_steps)][n_rows] sampled query-row indices (sequence 0)
   o_vals    [len(o_steps)][n_rows][hidden] attention output (float32)
+  top2_idx  [B][sum n_C][2] the two best vocabulary indices of every decision
+  top2_val  [B][sum n_C][2] their exact (float64) logits
+  h_rows    [len(o_steps)][3] decoded-row indices (within the step's C rows of
+            sequence 0) whose h is stored
+  h_vals    [len(o_steps)][3][hidden] those rows' h (float64): the tests form
+            the exact logits h W^T and the bf16 screen's h_bf16 W^T from them
 """
 
 from __future__ import annotations
@@ -55,7 +61,9 @@ def expected(cfg):
     conf = [np.concatenate([r.conf32[b] for r in res.records]) for b in range(B)]
     margin = [np.concatenate([r.margin[b] for r in res.records]) for b in range(B)]
     gaps = np.array([[r.conf_gap[b] for b in range(B)] for r in res.records], dtype=np.float64)
-    o_rows, o_vals = [], []
+    t2i = [np.concatenate([r.top2_idx[b] for r in res.records]) for b in range(B)]
+    t2v = [np.concatenate([r.top2_val[b] for r in res.records]) for b in range(B)]
+    o_rows, o_vals, h_rows, h_vals = [], [], [], []
     for k in steps:
         r = res.records[k]
         n_d, n_c = r.d_pos[0].size, r.c_pos[0].size
@@ -63,10 +71,15 @@ def expected(cfg):
         rows = (rows + [rows[-1]] * 6)[:6]
         o_rows.append(rows)
         o_vals.append(r.o[0][rows].astype(np.float32))
+        hr = [0, n_c // 2, n_c - 1]
+        h_rows.append(hr)
+        h_vals.append(r.o[0][[n_d + i for i in hr]])
     out = dict(tokens=res.tokens.astype(np.int32), sel_pos=np.stack(sel_pos).astype(np.int32),
                dec_tok=np.stack(dec_tok).astype(np.int32), conf=np.stack(conf).astype(np.float32),
                margin=np.stack(margin), conf_gap=gaps, o_steps=np.array(steps, dtype=np.int32),
-               o_rows=np.array(o_rows, dtype=np.int32), o_vals=np.stack(o_vals))
+               o_rows=np.array(o_rows, dtype=np.int32), o_vals=np.stack(o_vals),
+               top2_idx=np.stack(t2i).astype(np.int32), top2_val=np.stack(t2v),
+               h_rows=np.array(h_rows, dtype=np.int32), h_vals=np.stack(h_vals))
     return out, dt
 
 

@@ -147,3 +147,14 @@ def gpu_two_layer_semi_ar(index=119, **kw):
     base = dict(name="gpu_two_layer_semi_ar", layers=2, n_heads=4, n_kv_heads=2, vocab=1200)
     base.update(kw)
     return gpu_small_semi_ar(index=index, **base)
+
+
+# The bf16 screen's row tilings and hidden splits on one 8192-column
+# vocabulary: a cosine schedule over 600 positions in 8 steps decodes
+# 12..117 rows per sequence, 36..351 rows per step over 3 sequences.
+def gpu_screen_regimes(index=120, **kw):
+    base = dict(name="gpu_screen_regimes", index=index, batch=3, n_heads=2, n_kv_heads=2, head_dim=128,
+                vocab=8192, prompt_len=20, gen_len=600, n_registers=16, n_steps=8,
+                schedule="cosine", order="random", precision="bf16")
+    base.update(kw)
+    return Config(**base)

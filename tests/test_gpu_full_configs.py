@@ -2,12 +2,28 @@
 compared with the oracle's stored results (tests/golden/expected_<name>.npz,
 written by tests/golden/make_expected.py, which calls only the oracle).
 
-Bars: every decoded token, every unmasked position and the unmask order are
-bit-exact; confidences and the sampled attention-output rows are within
-2e-2 relative + 1e-2 absolute (bf16 path) or 1e-5 (fp32 path), and the
-attention rows also within a tight relative bound.  The oracle's smallest
-top-1/top-2 logit margin and (semi-AR) confidence gap at the cut are printed
-as the certificate that the decisions are not numerical ties.
+Bars:
+* every decoded token, every unmasked position and the unmask order are
+  bit-exact;
+* confidences and the sampled attention-output rows are within 2e-2 relative
+  + 1e-2 absolute (bf16 path) or 1e-5 (fp32 path), and the attention rows also
+  within a tight relative bound;
+* screened logits of sampled decoded rows, over the whole vocabulary, within
+  the same bars against the oracle's logits of the same rows: the exact h W^T
+  where the screen multiplies h split into bf16 hi + lo (and in fp32), else the
+  product the bf16 screen approximates, bf16(h) W^T, with one bf16 ulp of room
+  for an element of h within the attention output's error bound of a rounding
+  boundary (|W_vi| times that ulp per element);
+* decision certificate, per decided row: the kernel's own proof flag (no
+  column outside the exactly re-scored set can reach the decided logit) is
+  set; and the oracle's top-1/top-2 margin exceeds twice the error of the
+  GPU's exact top-1 minus top-2 logit difference (the decision is not a
+  numerical tie; the two logits' own errors, which share the error of h, are
+  printed too).  The smallest margin / (2 |d(z1 - z2)|) ratio is printed per
+  workload, with
+  the number of rows whose two best exact logits lie within twice the
+  re-score's worst-case error bound (a bound, far above the measured error,
+  so those rows are reported rather than failed).
 """
 
 import os
@@ -16,12 +32,39 @@ import numpy as np
 import pytest
 
 from mdm_inputs import CONFIGS, make_workload
+from oracle.logits import subset_logits
+from oracle.numerics import round_bf16, table_values
 
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
 TIGHT = {"bf16": 2e-4, "fp32": 1e-5}
+PROVEN = 8          # trace flag: the argmax over the whole vocabulary is proven
+TIE = 4             # trace flag: the two best exact logits within 2 eps_e
+
+
+def bf16_flip_room(h, eps):
+    """One bf16 ulp where h lies within eps of a bf16 rounding boundary, else 0."""
+    b = round_bf16(h)
+    mag = np.where(b != 0, np.abs(b), np.finfo(np.float32).tiny)
+    ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+    return np.where((ulp / 2 - np.abs(h - b)) <= eps, ulp, 0.0)
+
+
+def chunked_logits(h, w_bits, chunk=8192):
+    """oracle.logits.subset_logits over vocabulary chunks (bounds the float64 copy of W)."""
+    out = np.empty((h.shape[0], w_bits.shape[0]))
+    for v0 in range(0, w_bits.shape[0], chunk):
+        out[:, v0:v0 + chunk] = subset_logits(h, table_values(w_bits[v0:v0 + chunk]))
+    return out
+
+
+def abs_w_dot(room, w_bits, chunk=8192):
+    out = np.empty((room.shape[0], w_bits.shape[0]))
+    for v0 in range(0, w_bits.shape[0], chunk):
+        out[:, v0:v0 + chunk] = room @ np.abs(table_values(w_bits[v0:v0 + chunk])).T
+    return out
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=[c.name for c in CONFIGS])
@@ -32,7 +75,9 @@ def test_full_config_matches_oracle(cfg):
     wl = make_workload(cfg)
     run = SparseStepRunner(wl, device="cuda")
     o_steps = [int(k) for k in exp["o_steps"]]
-    recs, seq = run.generate_recorded(keep_o=o_steps)
+    recs, seq = run.generate_recorded(keep_o=o_steps, keep_logits=o_steps, trace=True)
+    counts = run.decision_counts
+    accurate = bool(run.mc.accurate_conf)
     run.close()
     rtol, atol = TOL[cfg.precision]
 
@@ -44,6 +89,8 @@ def test_full_config_matches_oracle(cfg):
     assert np.array_equal(seq, exp["tokens"]), "final sequences differ"
     err = np.abs(conf.astype(np.float64) - exp["conf"].astype(np.float64))
     assert np.all(err <= atol + rtol * np.abs(exp["conf"])), f"confidence error {err.max():.3g}"
+
+    # attention outputs of the sampled rows
     worst_rel = 0.0
     for i, k in enumerate(o_steps):
         rows = exp["o_rows"][i]
@@ -53,8 +100,49 @@ def test_full_config_matches_oracle(cfg):
         assert np.all(e <= atol + rtol * np.abs(ref)), f"attention output at step {k}: {e.max():.3g}"
         worst_rel = max(worst_rel, float(e.max() / np.abs(ref).max()))
     assert worst_rel <= TIGHT[cfg.precision], f"attention output relative error {worst_rel:.3g}"
+
+    # screened logits of sampled decoded rows over the whole vocabulary
+    worst_z = 0.0
+    for i, k in enumerate(o_steps):
+        h = exp["h_vals"][i]
+        got = recs[k]["logits"][0][exp["h_rows"][i]].astype(np.float64)
+        if cfg.precision == "fp32" or accurate:
+            ref, z_atol = chunked_logits(h, wl.w_vocab), atol
+        else:
+            ref = chunked_logits(round_bf16(h), wl.w_vocab)
+            eps = TIGHT[cfg.precision] * float(np.abs(recs[k]["o"][0]).max())
+            z_atol = atol + abs_w_dot(bf16_flip_room(h, eps), wl.w_vocab)
+        e = np.abs(got - ref)
+        bad = ~(e <= z_atol + rtol * np.abs(ref))
+        assert not bad.any(), f"logits at step {k}: {int(bad.sum())} of {bad.size} outside, max {e.max():.3g}"
+        worst_z = max(worst_z, float(e.max()))
+
+    # per-decision certificate
+    trace = np.concatenate([r["trace"] for r in recs], axis=1)            # [B][sum n_C][8]
+    ints = trace.view(np.int32)
+    flags = ints[..., 7]
+    assert np.array_equal(ints[..., 1], dec_tok), "trace tokens differ from the decided tokens"
+    assert np.all(flags & PROVEN), f"{int(np.sum(~flags & PROVEN))} decisions without a proof"
+    n_tie = int(np.sum((flags & TIE) != 0))       # within the re-score's worst-case bound: reported only
+    t_idx, t_val = exp["top2_idx"], exp["top2_val"]
+    assert np.array_equal(t_idx[..., 0], exp["dec_tok"])
+    z1g, z2g = trace[..., 0].astype(np.float64), trace[..., 2].astype(np.float64)
+    dz1 = np.abs(z1g - t_val[..., 0])
+    same2 = ints[..., 3] == t_idx[..., 1]
+    dz2 = np.where(same2, np.abs(z2g - t_val[..., 1]), 0.0)
+    margin = t_val[..., 0] - t_val[..., 1]
+    # what decides the argmax is the error of the difference of the two logits
+    # (their errors share the error of h); where the GPU's runner-up is another
+    # column, bound it by the two logits' errors
+    dm = np.where(same2, np.abs((z1g - z2g) - margin), dz1 + np.max(dz2) + np.max(dz1))
+    ratio = margin / (2.0 * np.maximum(dm, 1e-30))
+    n_bad = int(np.sum(ratio <= 1.0))
     gaps = exp["conf_gap"]
     gap = float(np.nanmin(gaps)) if np.isfinite(gaps).any() else float("nan")
-    print(f"  {cfg.name}: {dec_tok.size} decisions identical; min oracle margin "
-          f"{exp['margin'].min():.3g}, min conf gap {gap:.3g}, max conf err {err.max():.3g}, "
-          f"max O rel err {worst_rel:.3g}", flush=True)
+    print(f"  {cfg.name}: {dec_tok.size} decisions identical; min margin {margin.min():.3g}, "
+          f"max |dz| {max(dz1.max(), dz2.max()):.3g}, max |d(z1-z2)| {dm.max():.3g}, "
+          f"min margin/(2|d(z1-z2)|) {ratio.min():.3g} "
+          f"({n_bad} at or below 1), runner-up index agrees on {int(same2.sum())}/{same2.size}; "
+          f"re-scored beyond the candidates {counts[0]}, whole tiles {counts[1]}, within 2 eps_e {n_tie}; "
+          f"min conf gap {gap:.3g}, "
+          f"max conf err {err.max():.3g}, max O rel err {worst_rel:.3g}, max logit err {worst_z:.3g}", flush=True)

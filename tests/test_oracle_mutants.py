@@ -113,3 +113,56 @@ def test_mutant_new_rows_not_committed_before_attention(monkeypatch):
                         if nn else orig(nc, nn, nd, nr))
     with pytest.raises(AssertionError):
         T_inv.test_incremental_equals_dense_block_mask(1, "bf16", T_inv.tiny_bf16)
+
+
+# ---- second layer: each planted mistake must break the brute-force pin ------
+import test_oracle_two_layer as T_two
+from oracle.numerics import round_storage
+
+
+def _qkv_layer2_variant(rotate_q=True, round_v=True):
+    def qkv_layer2(self, h1, pos):
+        wq, wk, wv = self.layer2
+        n = h1.shape[0]
+        d, h, hk = self.head_dim, self.n_heads, self.n_kv_heads
+        q = (h1 @ wq).reshape(n, h, d)
+        k = (h1 @ wk).reshape(n, hk, d)
+        v = (h1 @ wv).reshape(n, hk, d)
+        q = self._rot(q, pos) if rotate_q else round_storage(q, self.precision)
+        v = round_storage(v, self.precision) if round_v else v
+        return q, self._rot(k, pos), v
+    return qkv_layer2
+
+
+def test_mutant_layer2_queries_unrotated(monkeypatch):
+    monkeypatch.setattr(step_mod.Model, "qkv_layer2", _qkv_layer2_variant(rotate_q=False))
+    with pytest.raises(AssertionError):
+        T_two.test_two_layer_step_matches_bruteforce()
+
+
+def test_mutant_layer2_values_unrounded(monkeypatch):
+    monkeypatch.setattr(step_mod.Model, "qkv_layer2", _qkv_layer2_variant(round_v=False))
+    with pytest.raises(AssertionError):
+        T_two.test_two_layer_step_matches_bruteforce()
+
+
+def test_mutant_layer2_key_value_blocks_swapped(monkeypatch):
+    orig = step_mod.split_layer2
+
+    def split(w, hq, hk):
+        q, k, v = orig(w, hq, hk)
+        return q, v, k
+    monkeypatch.setattr(step_mod, "split_layer2", split)
+    with pytest.raises(AssertionError):
+        T_two.test_two_layer_step_matches_bruteforce()
+
+
+def test_mutant_layer2_query_block_transposed(monkeypatch):
+    orig = step_mod.split_layer2
+
+    def split(w, hq, hk):
+        q, k, v = orig(w, hq, hk)
+        return q.T, k, v                      # square block: the shapes still fit
+    monkeypatch.setattr(step_mod, "split_layer2", split)
+    with pytest.raises(AssertionError):
+        T_two.test_two_layer_step_matches_bruteforce()

@@ -60,3 +60,25 @@ def test_generator_bf16_encoding_matches_torch():
     want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(bits, want)
     assert np.array_equal(bf16_bits_to_f32(bits).astype(np.float64), table_values(bits))
+
+
+def test_top_two_matches_a_scan_with_ties():
+    """The two best (index, value) pairs per row, pinned by a plain scan that
+    keeps the first index of equal values; rows with ties included."""
+    from oracle.logits import top_two
+    rng = np.random.default_rng(5)
+    z = rng.integers(-4, 5, size=(300, 17)).astype(np.float64)      # many equal values
+    z[:5] = 2.0                                                     # all equal
+    idx, val = top_two(z)
+    for r in range(z.shape[0]):
+        row = list(z[r])
+        b1 = 0
+        for j in range(len(row)):
+            if row[j] > row[b1]:
+                b1 = j
+        b2 = 1 if b1 == 0 else 0
+        for j in range(len(row)):
+            if j != b1 and row[j] > row[b2]:
+                b2 = j
+        assert (idx[r, 0], idx[r, 1]) == (b1, b2)
+        assert (val[r, 0], val[r, 1]) == (row[b1], row[b2])
