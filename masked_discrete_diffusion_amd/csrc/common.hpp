@@ -22,21 +22,21 @@ constexpr int kCand = 8;           // candidates re-scored exactly per row
 constexpr int kErrTok = 1;
 constexpr int kErrPos = 2;
 
-__device__ inline void flag_error(int* err, int bit) {
+__device__ __attribute__((always_inline)) inline void flag_error(int* err, int bit) {
   if (err) atomicOr(err, bit);
 }
 
 // bf16 bit pattern -> float (exact).
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __attribute__((always_inline)) inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // float -> bf16 bit pattern, round to nearest even (hardware conversion on gfx950).
-__device__ inline uint16_t f32_to_bf16(float f) {
+__device__ __attribute__((always_inline)) inline uint16_t f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
 
 // Two floats -> packed bf16 pair (first in the low half), round to nearest even.
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
+__device__ __attribute__((always_inline)) inline uint32_t pack_bf16x2(float a, float b) {
   const floatx2 f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
@@ -47,7 +47,7 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // truncate; a carry into the exponent is the correct result.  Inputs are
 // finite and in the normal range of bf16 (O(1) activations); the truncated
 // double is then exactly representable in fp32 and in bf16.
-__device__ inline uint16_t f64_to_bf16(double x) {
+__device__ __attribute__((always_inline)) inline uint16_t f64_to_bf16(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
   const uint64_t lsb = (u >> 45) & 1ull;
   u += ((1ull << 44) - 1ull) + lsb;
@@ -59,7 +59,7 @@ __device__ inline uint16_t f64_to_bf16(double x) {
 // RoPE of one interleaved pair (x0, x1) by the angle whose fp32 cos/sin are c, s.
 // Evaluated in double: x (bf16 or fp32) times c or s (fp32) is exact in double,
 // so each component rounds once; contraction into fma cannot change it.
-__device__ inline void rope_pair(float x0, float x1, float c, float s, double& r0, double& r1) {
+__device__ __attribute__((always_inline)) inline void rope_pair(float x0, float x1, float c, float s, double& r0, double& r1) {
   const double dx0 = x0, dx1 = x1, dc = c, ds = s;
   r0 = dx0 * dc - dx1 * ds;
   r1 = dx0 * ds + dx1 * dc;
@@ -67,7 +67,7 @@ __device__ inline void rope_pair(float x0, float x1, float c, float s, double& r
 
 // Strict "a ranks before b" for (value, index) candidates: larger value first,
 // lower index on equal values.
-__device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
+__device__ __attribute__((always_inline)) inline bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
@@ -84,7 +84,7 @@ struct U2 {
   uint32_t a, b;
 };
 template <int S>
-__device__ inline U2 wave_pair(uint32_t x) {
+__device__ __attribute__((always_inline)) inline U2 wave_pair(uint32_t x) {
   static_assert(S >= 0 && S <= 5, "step");
   if constexpr (S == 0) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false)};
   else if constexpr (S == 1) return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false)};
@@ -101,7 +101,7 @@ __device__ inline U2 wave_pair(uint32_t x) {
 
 // Sum over aligned groups of 2^N lanes (N <= 6): steps 0..N-1.
 template <int N>
-__device__ inline float group_sum(float x) {
+__device__ __attribute__((always_inline)) inline float group_sum(float x) {
   if constexpr (N > 0) {
     x = group_sum<N - 1>(x);
     const U2 p = wave_pair<N - 1>(__float_as_uint(x));
@@ -112,7 +112,7 @@ __device__ inline float group_sum(float x) {
 
 // (value desc, index asc) best pair over aligned groups of 2^N lanes.
 template <int N>
-__device__ inline void group_argmax(float& v, int& i) {
+__device__ __attribute__((always_inline)) inline void group_argmax(float& v, int& i) {
   if constexpr (N > 0) {
     group_argmax<N - 1>(v, i);
     const U2 pv = wave_pair<N - 1>(__float_as_uint(v));
@@ -139,29 +139,29 @@ __device__ inline void group_argmax(float& v, int& i) {
 // own vmcnt waits for its loads only become stricter (the counter retires in
 // issue order).  M0 holds the LDS base; nothing else in these kernels uses M0,
 // and one wait state separates its write from the load.
-__device__ inline void dma16_at(const void* base, uint32_t off, uint32_t lds) {
+__device__ __attribute__((always_inline)) inline void dma16_at(const void* base, uint32_t off, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory");
 }
 // LDS byte address of a pointer into shared memory.
-__device__ inline uint32_t lds_addr(const void* p) {
+__device__ __attribute__((always_inline)) inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)p;
 }
-__device__ inline void dma16(const void* base, uint32_t off, void* lds_block) { dma16_at(base, off, lds_addr(lds_block)); }
+__device__ __attribute__((always_inline)) inline void dma16(const void* base, uint32_t off, void* lds_block) { dma16_at(base, off, lds_addr(lds_block)); }
 
 // Wait until at most N of this wavefront's vector-memory operations are in
 // flight, and its LDS operations are done.  vmcnt retires in issue order, so
 // with N = (loads this wave issued after tile i) it waits exactly for tile i.
 template <int N>
-__device__ inline void ring_wait() {
+__device__ __attribute__((always_inline)) inline void ring_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt immediate out of range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier without the release fence of __syncthreads (that fence
 // would wait for every LDS-DMA load in flight); waits are explicit, above.
-__device__ inline void ring_barrier() {
+__device__ __attribute__((always_inline)) inline void ring_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

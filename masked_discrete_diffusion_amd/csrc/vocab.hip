@@ -26,6 +26,8 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kKChunk = 64;        // hidden elements per LDS stage
 constexpr int kScreenTargetBlocks = 256;   // split hidden until about this many blocks
+constexpr int kSplitMaxRows = 1 << 20;     // split hidden only for steps of at most this many rows
+constexpr bool kFoldSplitsInDecide = false; // split sums: in the decision kernel, else a reduce launch
 
 // Per (row, vocabulary tile) summary of screened logits: the maximum, the sum
 // of exp(z - max) and the three best (value, index) pairs in rank order
@@ -38,7 +40,7 @@ struct Top3 {
   int i1, i2, i3;
 };
 
-__device__ inline void top3_push(Top3& t, float v, int i) {
+__device__ __attribute__((always_inline)) inline Top3 top3_push(Top3 t, float v, int i) {
   if (ranks_before(v, i, t.v1, t.i1)) {
     t.v3 = t.v2; t.i3 = t.i2; t.v2 = t.v1; t.i2 = t.i1; t.v1 = v; t.i1 = i;
   } else if (ranks_before(v, i, t.v2, t.i2)) {
@@ -46,20 +48,28 @@ __device__ inline void top3_push(Top3& t, float v, int i) {
   } else if (ranks_before(v, i, t.v3, t.i3)) {
     t.v3 = v; t.i3 = i;
   }
+  return t;
 }
 
-__device__ inline Top3 top3_merge(const Top3& a, const Top3& b) {
+// (max, sum of exp) of two partial sums
+__device__ __attribute__((always_inline)) inline void lse_merge(float& m, float& se, float om, float ose) {
+  const float nm = fmaxf(m, om);
+  se = (m == kNegInf ? 0.f : se * expf(m - nm)) + (om == kNegInf ? 0.f : ose * expf(om - nm));
+  m = nm;
+}
+
+__device__ __attribute__((always_inline)) inline Top3 top3_merge(Top3 a, Top3 b) {
   Top3 r;
   r.m = fmaxf(a.m, b.m);
   r.se = (a.m == kNegInf ? 0.f : a.se * expf(a.m - r.m)) + (b.m == kNegInf ? 0.f : b.se * expf(b.m - r.m));
   r.v1 = a.v1; r.i1 = a.i1; r.v2 = a.v2; r.i2 = a.i2; r.v3 = a.v3; r.i3 = a.i3;
-  top3_push(r, b.v1, b.i1);
-  top3_push(r, b.v2, b.i2);
-  top3_push(r, b.v3, b.i3);
+  r = top3_push(r, b.v1, b.i1);
+  r = top3_push(r, b.v2, b.i2);
+  r = top3_push(r, b.v3, b.i3);
   return r;
 }
 
-__device__ inline Top3 top3_shfl_xor(const Top3& t, int mask) {
+__device__ __attribute__((always_inline)) inline Top3 top3_shfl_xor(Top3 t, int mask) {
   Top3 o;
   o.m = __shfl_xor(t.m, mask);
   o.se = __shfl_xor(t.se, mask);
@@ -74,7 +84,7 @@ __device__ inline Top3 top3_shfl_xor(const Top3& t, int mask) {
 
 // Fold a lane's logits into (max, sumexp, top-3): values[n] with indices idx[n].
 template <int N>
-__device__ inline Top3 summarize(const float* vals, const int* idx) {
+__device__ __attribute__((always_inline)) inline Top3 summarize(const float* vals, const int* idx) {
   Top3 t;
   t.m = kNegInf; t.se = 0.f;
   t.v1 = t.v2 = t.v3 = kNegInf;
@@ -82,7 +92,7 @@ __device__ inline Top3 summarize(const float* vals, const int* idx) {
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     t.m = fmaxf(t.m, vals[e]);
-    top3_push(t, vals[e], idx[e]);
+    t = top3_push(t, vals[e], idx[e]);
   }
   if (t.m != kNegInf) {
 #pragma unroll
@@ -92,7 +102,7 @@ __device__ inline Top3 summarize(const float* vals, const int* idx) {
 }
 
 // One 32-byte partial record: {m, se, v1, i1} {v2, i2, v3, i3}.
-__device__ inline void store_partial(float* p, const Top3& t) {
+__device__ __attribute__((always_inline)) inline void store_partial(float* p, Top3 t) {
   floatx4 a = {t.m, t.se, t.v1, __int_as_float(t.i1)};
   floatx4 c = {t.v2, __int_as_float(t.i2), t.v3, __int_as_float(t.i3)};
   reinterpret_cast<floatx4*>(p)[0] = a;
@@ -140,9 +150,9 @@ __global__ __launch_bounds__(256) void k_pack(Geometry g, VocabArgs a, int M) {
 // banks.  Every wavefront issues the same number of 1 KiB DMA blocks, so the
 // ring waits are constants.
 // With n_split > 1 the hidden dimension is split over blockIdx.z: every split
-// writes its partial logits and k_screen_reduce sums them in split order and
-// runs the epilogue (a separate launch: an in-kernel last-block reduction
-// needs device-scope fences, which write back and invalidate a whole L2).
+// writes its partial logits and the decision kernel sums them in split order
+// (an in-kernel last-block reduction would need device-scope fences, which
+// write back and invalidate a whole L2).
 template <int RB, int NG, bool kLo>
 struct ScreenStage {
   static constexpr int NW = 4 * NG;                                // wavefronts per block
@@ -166,14 +176,14 @@ struct ScreenStage {
 };
 
 // Physical unit of logical unit u in LDS row r.
-__device__ inline int swz(int r, int u) { return u ^ ((r >> 1) & 7); }
+__device__ __attribute__((always_inline)) inline int swz(int r, int u) { return u ^ ((r >> 1) & 7); }
 
 // Per-lane byte offsets of this wavefront's DMA units, relative to the
 // stage's W base (W row v0) or h base (row m0), and the kind of each slot
 // (0 W, 1 h hi, 2 h lo).  Lane l of block blk fills physical unit q = 64 blk
 // + l (row q / 8, position q % 8) with the logical unit stored there.
 template <class S>
-__device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int v0, uint32_t* off, int* kind) {
+__device__ __attribute__((always_inline)) inline void screen_offsets(int wave, int lane, int hidden, int V, int v0, uint32_t* off, int* kind) {
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
     const int blk = wave * S::LPW + i;
@@ -193,7 +203,7 @@ __device__ inline void screen_offsets(int wave, int lane, int hidden, int V, int
 }
 
 template <class S>
-__device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const uint16_t* lb, int wave,
+__device__ __attribute__((always_inline)) inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const uint16_t* lb, int wave,
                                   const uint32_t* off, const int* kind, uint32_t stage_lds) {
 #pragma unroll
   for (int i = 0; i < S::LPW; ++i) {
@@ -204,7 +214,7 @@ __device__ inline void screen_dma(const uint16_t* wb, const uint16_t* hb, const 
 }
 
 template <int LPW, int AHEAD>
-__device__ inline void screen_wait(int younger) {
+__device__ __attribute__((always_inline)) inline void screen_wait(int younger) {
   static_assert(AHEAD <= 4, "waits are spelled out for up to four stages ahead");
   if (younger >= 3 && AHEAD >= 4) ring_wait<3 * LPW>();
   else if (younger >= 2 && AHEAD >= 3) ring_wait<2 * LPW>();
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
         }
       }
     }
-    return;                                   // k_screen_reduce folds the splits (or the caller reads z)
+    return;                                   // the decision kernel folds the splits (or the caller reads z)
   }
 
   __syncthreads();                            // every wavefront is done with the ring
@@ -358,7 +368,7 @@ struct WideStage {
   static_assert(NST >= 3, "the ring must hold three stages");
 };
 
-__device__ inline int swz4(int r, int u) { return u ^ ((r >> 2) & 3); }
+__device__ __attribute__((always_inline)) inline int swz4(int r, int u) { return u ^ ((r >> 2) & 3); }
 
 template <int RB, bool kLo>
 __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, int M, int n_split) {
@@ -510,39 +520,75 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
   }
 }
 
+// Insert (v, i) into the rank-ordered top-3 with selects only (no branches:
+// the lanes of the reduce push different values).
+__device__ __attribute__((always_inline)) inline Top3 top3_push_sel(Top3 t, float v, int i) {
+  const bool b1 = ranks_before(v, i, t.v1, t.i1);
+  const bool b2 = ranks_before(v, i, t.v2, t.i2);
+  const bool b3 = ranks_before(v, i, t.v3, t.i3);
+  const float n3 = b2 ? t.v2 : (b3 ? v : t.v3);
+  const int j3 = b2 ? t.i2 : (b3 ? i : t.i3);
+  const float n2 = b1 ? t.v1 : (b2 ? v : t.v2);
+  const int j2 = b1 ? t.i1 : (b2 ? i : t.i2);
+  t.v1 = b1 ? v : t.v1;
+  t.i1 = b1 ? i : t.i1;
+  t.v2 = n2; t.i2 = j2;
+  t.v3 = n3; t.i3 = j3;
+  return t;
+}
+
 // Fold the hidden-split partial logits of one 128-vocab tile for 32 rows:
-// thread t: row t/8, vocab columns 16(t%8) .. +16; splits summed in order.
+// thread t: row t/8, vocab columns 16(t%8) .. +16; splits summed in order,
+// every split's loads issued before the sums (up to 4 splits).
 __global__ __launch_bounds__(256) void k_screen_reduce(Geometry g, VocabArgs a, int M, int n_split) {
   const int vt = blockIdx.x;
   const int r = blockIdx.y * 32 + threadIdx.x / 8;
+  const int rr = min(r, M - 1);
   const int c0 = vt * kVocabTile + 16 * (threadIdx.x % 8);
+  floatx4 zp[4][4];
+#pragma unroll
+  for (int sp = 0; sp < 4; ++sp) {
+    const floatx4* z = reinterpret_cast<const floatx4*>(a.zpart + ((int64_t)min(sp, n_split - 1) * M + rr) * a.v_pad + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) zp[sp][q] = z[q];
+  }
   float vals[16];
   int idx[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) vals[e] = 0.f;
-  if (r < M) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const floatx4* z = reinterpret_cast<const floatx4*>(a.zpart + ((int64_t)sp * M + r) * a.v_pad + c0);
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 v = z[q];
+    for (int ii = 0; ii < 4; ++ii) {
+      float z = zp[0][q][ii];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) vals[4 * q + ii] += v[ii];
-      }
+      for (int sp = 1; sp < 4; ++sp) z = sp < n_split ? z + zp[sp][q][ii] : z;
+      const int v = c0 + 4 * q + ii;
+      idx[4 * q + ii] = v;
+      if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = z;
+      vals[4 * q + ii] = v < g.V ? z : kNegInf;
     }
-  }
+  Top3 t;
+  t.m = kNegInf; t.se = 0.f;
+  t.v1 = t.v2 = t.v3 = kNegInf;
+  t.i1 = t.i2 = t.i3 = 0x7fffffff;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int v = c0 + e;
-    idx[e] = v;
-    if (a.logits && r < M && v < g.V) a.logits[(int64_t)r * g.V + v] = vals[e];
-    if (v >= g.V) vals[e] = kNegInf;
+    t.m = fmaxf(t.m, vals[e]);
+    t = top3_push_sel(t, vals[e], idx[e]);
   }
-  Top3 t = summarize<16>(vals, idx);
+  if (t.m != kNegInf) {
 #pragma unroll
-  for (int mask = 1; mask < 8; mask <<= 1) t = top3_merge(t, top3_shfl_xor(t, mask));
+    for (int e = 0; e < 16; ++e) t.se += expf(vals[e] - t.m);
+  }
+#pragma unroll
+  for (int mask = 1; mask < 8; mask <<= 1) {
+    const Top3 o = top3_shfl_xor(t, mask);
+    lse_merge(t.m, t.se, o.m, o.se);
+    t = top3_push_sel(t, o.v1, o.i1);
+    t = top3_push_sel(t, o.v2, o.i2);
+    t = top3_push_sel(t, o.v3, o.i3);
+  }
   const int n_vt = (g.V + kVocabTile - 1) / kVocabTile;
-  if (threadIdx.x % 8 == 0 && r < a.m_pad) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, t);
+  if (threadIdx.x % 8 == 0 && r < M) store_partial(a.partials + ((int64_t)r * n_vt + vt) * 8, t);
 }
 
 // ------------------------------------------------------------ screen, fp32 --
@@ -647,7 +693,7 @@ template <typename WT>
 struct W8;
 template <>
 struct W8<uint16_t> {
-  static __device__ inline void load(const uint16_t* p, float* out) {
+  static __device__ __attribute__((always_inline)) inline void load(const uint16_t* p, float* out) {
     const u16x8 r = *reinterpret_cast<const u16x8*>(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = bf16_to_f32(r[e]);
@@ -655,7 +701,7 @@ struct W8<uint16_t> {
 };
 template <>
 struct W8<float> {
-  static __device__ inline void load(const float* p, float* out) {
+  static __device__ __attribute__((always_inline)) inline void load(const float* p, float* out) {
     const floatx4 a = reinterpret_cast<const floatx4*>(p)[0];
     const floatx4 b = reinterpret_cast<const floatx4*>(p)[1];
 #pragma unroll
@@ -663,29 +709,29 @@ struct W8<float> {
   }
 };
 
-// Insert (v, i) into the sorted list c (rank order), dropping the last; selects only.
-__device__ inline void cand_insert(Cand* c, float v, int i) {
+// A rank-ordered candidate list, passed and returned by value (an array
+// behind a pointer or reference would be kept in memory).
+struct CandList {
+  Cand c[kCand];
+};
+
+// Insert (v, i) into the sorted list (rank order), dropping the last; selects only.
+__device__ __attribute__((always_inline)) inline CandList cand_insert(CandList l, float v, int i) {
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
-    const bool sw = ranks_before(v, i, c[k].v, c[k].i);
-    const float tv = c[k].v;
-    const int ti = c[k].i;
-    c[k].v = sw ? v : tv;
-    c[k].i = sw ? i : ti;
+    const bool sw = ranks_before(v, i, l.c[k].v, l.c[k].i);
+    const float tv = l.c[k].v;
+    const int ti = l.c[k].i;
+    l.c[k].v = sw ? v : tv;
+    l.c[k].i = sw ? i : ti;
     v = sw ? tv : v;
     i = sw ? ti : i;
   }
-}
-
-// (max, sum of exp) of two partial sums
-__device__ inline void lse_merge(float& m, float& se, float om, float ose) {
-  const float nm = fmaxf(m, om);
-  se = (m == kNegInf ? 0.f : se * expf(m - nm)) + (om == kNegInf ? 0.f : ose * expf(om - nm));
-  m = nm;
+  return l;
 }
 
 // (max, sum of exp) over the whole wavefront
-__device__ inline void wave_lse(float& m, float& se) {
+__device__ __attribute__((always_inline)) inline void wave_lse(float& m, float& se) {
   static_assert(kWave == 64, "wave");
 #define MDM_LSE_STEP(S)                                                   \
   {                                                                       \
@@ -700,7 +746,7 @@ __device__ inline void wave_lse(float& m, float& se) {
 #undef MDM_LSE_STEP
 }
 
-__device__ inline float wave_max(float x) {
+__device__ __attribute__((always_inline)) inline float wave_max(float x) {
 #pragma unroll
   for (int s = 0; s < 6; ++s) {
     const int o = __shfl_xor(__float_as_int(x), 1 << s);
@@ -712,7 +758,7 @@ __device__ inline float wave_max(float x) {
 // Unmasking in a pre-generated order, fused into the decision (page 3,
 // section 3.2: every decoded position is unmasked): the decided token of row
 // m = (b, c) is written at its candidate position in the dense sequence.
-__device__ inline void unmask_order(const Geometry& g, const VocabArgs& a, int m, int tok) {
+__device__ __attribute__((always_inline)) inline void unmask_order(const Geometry& g, const VocabArgs& a, int m, int tok) {
   const int b = m / a.n_c, cc = m % a.n_c;
   const int pos = a.cand_pos[(int64_t)b * a.cand_stride + cc];
   if (pos < 0 || pos >= g.seq_len) flag_error(a.err, kErrPos);
@@ -721,43 +767,50 @@ __device__ inline void unmask_order(const Geometry& g, const VocabArgs& a, int m
 
 // gamma(n) = n u / (1 - n u), u = 2^-24: the bound on the relative error of a
 // sum of n fp32 roundings
-__device__ inline float gamma_f32(float n) {
+__device__ __attribute__((always_inline)) inline float gamma_f32(float n) {
   const float nu = n * 5.9604645e-8f;
   return nu / (1.f - nu);
 }
 
-// Raw 8 elements of a row (16 bytes of bf16 or 32 of fp32) and their values.
+// Raw 8 elements of a row (16 bytes of bf16 or 32 of fp32) and their values;
+// loaded and read through free functions taking and returning values.
 template <typename WT>
 struct Raw8;
 template <>
 struct Raw8<uint16_t> {
   u16x8 r;
-  __device__ inline void load(const uint16_t* p) { r = *reinterpret_cast<const u16x8*>(p); }
-  __device__ inline float at(int e) const { return bf16_to_f32(r[e]); }
 };
 template <>
 struct Raw8<float> {
   floatx4 a, b;
-  __device__ inline void load(const float* p) {
-    a = reinterpret_cast<const floatx4*>(p)[0];
-    b = reinterpret_cast<const floatx4*>(p)[1];
-  }
-  __device__ inline float at(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
+__device__ __attribute__((always_inline)) inline Raw8<uint16_t> raw8_load(const uint16_t* p) {
+  Raw8<uint16_t> x;
+  x.r = *reinterpret_cast<const u16x8*>(p);
+  return x;
+}
+__device__ __attribute__((always_inline)) inline Raw8<float> raw8_load(const float* p) {
+  Raw8<float> x;
+  x.a = reinterpret_cast<const floatx4*>(p)[0];
+  x.b = reinterpret_cast<const floatx4*>(p)[1];
+  return x;
+}
+__device__ __attribute__((always_inline)) inline float raw8_at(Raw8<uint16_t> x, int e) { return bf16_to_f32(x.r[e]); }
+__device__ __attribute__((always_inline)) inline float raw8_at(Raw8<float> x, int e) { return e < 4 ? x.a[e] : x.b[e - 4]; }
 
 // Lane l's slice of a hidden row: elements [8l + 512j, +8) for j < NIT; the
 // addresses are clamped into the row (every load is issued unconditionally)
 // and elements past the row are zero.
 template <int NIT>
-__device__ inline void load_h_slice(const float* row, int lane, int hidden, float (&x)[NIT][8]) {
+__device__ __attribute__((always_inline)) inline void load_h_slice(const float* row, int lane, int hidden, float (&x)[NIT][8]) {
   Raw8<float> raw[NIT];
 #pragma unroll
-  for (int j = 0; j < NIT; ++j) raw[j].load(row + min(8 * lane + 512 * j, hidden - 8));
+  for (int j = 0; j < NIT; ++j) raw[j] = raw8_load(row + min(8 * lane + 512 * j, hidden - 8));
 #pragma unroll
   for (int j = 0; j < NIT; ++j) {
     const bool ok = 8 * lane + 512 * j < hidden;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[j][e] = ok ? raw[j].at(e) : 0.f;
+    for (int e = 0; e < 8; ++e) x[j][e] = ok ? raw8_at(raw[j], e) : 0.f;
   }
 }
 
@@ -765,16 +818,16 @@ __device__ inline void load_h_slice(const float* row, int lane, int hidden, floa
 // lane l takes elements [8l + 512j, +8) in order, the lanes' sums are added in
 // a fixed tree (the same order as the candidates' re-score).
 template <typename WT, int NIT>
-__device__ inline float wave_dot(const float (&hr)[NIT][8], const WT* w, int col, int lane, int hidden) {
+__device__ __attribute__((always_inline)) inline float wave_dot(const float (&hr)[NIT][8], const WT* w, int col, int lane, int hidden) {
   const WT* row = w + (int64_t)col * hidden;
   Raw8<WT> raw[NIT];
 #pragma unroll
-  for (int j = 0; j < NIT; ++j) raw[j].load(row + min(8 * lane + 512 * j, hidden - 8));
+  for (int j = 0; j < NIT; ++j) raw[j] = raw8_load(row + min(8 * lane + 512 * j, hidden - 8));
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < NIT; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(hr[j][e], raw[j].at(e), acc);
+    for (int e = 0; e < 8; ++e) acc = fmaf(hr[j][e], raw8_at(raw[j], e), acc);
   return group_sum<6>(acc);
 }
 
@@ -794,6 +847,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   const WT* w = static_cast<const WT*>(a.w);
   const int b = m / a.n_c, cc = m % a.n_c;
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
+  const float wmax = *a.wmax;               // loaded early: used after the re-score
 
   // thread t's piece j of h: elements [8t + 2048 j, +8) (block layout); loaded
   // first, its latency overlaps the fold; addresses clamped, zero past the row
@@ -801,19 +855,20 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   {
     Raw8<float> raw[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) raw[j].load(hrow + min(8 * tid + 2048 * j, g.hidden - 8));
+    for (int j = 0; j < NB; ++j) raw[j] = raw8_load(hrow + min(8 * tid + 2048 * j, g.hidden - 8));
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const bool ok = 8 * tid + 2048 * j < g.hidden;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hb[j][e] = ok ? raw[j].at(e) : 0.f;
+      for (int e = 0; e < 8; ++e) hb[j][e] = ok ? raw8_at(raw[j], e) : 0.f;
     }
   }
 
   // 1. fold the tiles: (max, sum of exp) and the kCand + 1 best entries
   __shared__ Cand s_best[kCand + 1];
   __shared__ float s_m, s_se;
-  if (n_vt <= kWave) {
+  const bool fold = a.n_split > 1 && a.zpart != nullptr;   // split partial logits, not tile records
+  if (n_vt <= kWave && !fold) {
     // one tile per lane of wavefront 0: its three entries are already in rank order
     if (wave == 0) {
       const int t = min(lane, n_vt - 1);
@@ -839,13 +894,56 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
       if (lane == 0) { s_m = lm; s_se = lse; }
     }
   } else {
-    // several tiles per thread (large vocabularies): sorted insertion, then a
-    // block merge of the wavefronts' top-(kCand + 1)
+    // several tiles per thread (large vocabularies), or the hidden dimension
+    // split over screen blocks: sorted insertion, then a block merge of the
+    // wavefronts' top-(kCand + 1)
     float lm = kNegInf, lse = 0.f;
-    Cand c[kCand];
+    CandList cl;
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) { c[k].v = kNegInf; c[k].i = 0x7fffffff; }
-    auto fold4 = [&](int t0) {
+    for (int k = 0; k < kCand; ++k) { cl.c[k].v = kNegInf; cl.c[k].i = 0x7fffffff; }
+    if (fold) {
+      // the screen's per-split partial logits of this row are summed here in
+      // split order (up to 4 splits): thread t takes 32 consecutive columns
+      // per pass, every split's loads issued before any sum; the four threads
+      // of a 128-column tile then merge their (max, sum of exp, top-3)
+      for (int c0 = 32 * tid; c0 < g.V; c0 += 32 * 256) {
+        floatx4 zp[4][8];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+          const floatx4* zr = reinterpret_cast<const floatx4*>(
+              a.zpart + ((int64_t)min(sp, a.n_split - 1) * M + m) * a.v_pad + c0);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zp[sp][q] = zr[q];
+        }
+        float vals[32];
+        int idx[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float z = zp[0][q][e];
+#pragma unroll
+            for (int sp = 1; sp < 4; ++sp) z = sp < a.n_split ? z + zp[sp][q][e] : z;
+            const int col = c0 + 4 * q + e;
+            idx[4 * q + e] = col;
+            vals[4 * q + e] = col < g.V ? z : kNegInf;
+            if (a.logits && col < g.V) a.logits[(int64_t)m * g.V + col] = z;
+          }
+        Top3 t = summarize<32>(vals, idx);
+        t = top3_merge(t, top3_shfl_xor(t, 1));
+        t = top3_merge(t, top3_shfl_xor(t, 2));
+        if ((tid & 3) == 0) {
+          // the tile's record, for the rare re-scoring pass below
+          if (c0 < g.V) store_partial(a.partials + ((int64_t)m * n_vt + c0 / tw) * 8, t);
+          lse_merge(lm, lse, t.m, t.se);
+          cl = cand_insert(cl, t.v1, t.i1);
+          cl = cand_insert(cl, t.v2, t.i2);
+          cl = cand_insert(cl, t.v3, t.i3);
+        }
+      }
+    } else {
+    // four tiles per thread and pass, every load issued before any is used
+    for (int t0 = 0; t0 < n_vt; t0 += 1024) {
       floatx4 p0[4], p1[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -857,29 +955,28 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
       for (int u = 0; u < 4; ++u) {
         if (t0 + u * 256 + tid < n_vt) {
           lse_merge(lm, lse, p0[u][0], p0[u][1]);
-          cand_insert(c, p0[u][2], __float_as_int(p0[u][3]));
-          cand_insert(c, p1[u][0], __float_as_int(p1[u][1]));
-          cand_insert(c, p1[u][2], __float_as_int(p1[u][3]));
+          cl = cand_insert(cl, p0[u][2], __float_as_int(p0[u][3]));
+          cl = cand_insert(cl, p1[u][0], __float_as_int(p1[u][1]));
+          cl = cand_insert(cl, p1[u][2], __float_as_int(p1[u][3]));
         }
       }
-    };
-    fold4(0);                               // straight-line for up to 1024 tiles
-    for (int t0 = 1024; t0 < n_vt; t0 += 1024) fold4(t0);
+    }
+    }
     wave_lse(lm, lse);
 #pragma unroll
     for (int k = 0; k <= kCand; ++k) {
-      float bv = c[0].v;
-      int bi = c[0].i;
+      float bv = cl.c[0].v;
+      int bi = cl.c[0].i;
       group_argmax<6>(bv, bi);
       if (lane == 0) s_c[wave][k] = Cand{bv, bi};
-      const bool pop = bi == c[0].i && bi != 0x7fffffff;
+      const bool pop = bi == cl.c[0].i && bi != 0x7fffffff;
 #pragma unroll
       for (int q = 0; q < kCand - 1; ++q) {
-        c[q].v = pop ? c[q + 1].v : c[q].v;
-        c[q].i = pop ? c[q + 1].i : c[q].i;
+        cl.c[q].v = pop ? cl.c[q + 1].v : cl.c[q].v;
+        cl.c[q].i = pop ? cl.c[q + 1].i : cl.c[q].i;
       }
-      c[kCand - 1].v = pop ? kNegInf : c[kCand - 1].v;
-      c[kCand - 1].i = pop ? 0x7fffffff : c[kCand - 1].i;
+      cl.c[kCand - 1].v = pop ? kNegInf : cl.c[kCand - 1].v;
+      cl.c[kCand - 1].i = pop ? 0x7fffffff : cl.c[kCand - 1].i;
     }
     if (lane == 0) { s_lse[wave][0] = lm; s_lse[wave][1] = lse; }
     __syncthreads();
@@ -923,7 +1020,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
     for (int k = 0; k < kCand; ++k) {
       const WT* crow = w + (int64_t)((besti[k] >= 0 && besti[k] < g.V) ? besti[k] : 0) * g.hidden;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) raw[j][k].load(crow + min(8 * tid + 2048 * j, g.hidden - 8));
+      for (int j = 0; j < NB; ++j) raw[j][k] = raw8_load(crow + min(8 * tid + 2048 * j, g.hidden - 8));
     }
 #pragma unroll
     for (int k = 0; k < kCand; ++k) dot[k] = 0.f;
@@ -940,7 +1037,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
           dd = fmaf(r, r, dd);
         }
 #pragma unroll
-        for (int k = 0; k < kCand; ++k) dot[k] = fmaf(x, raw[j][k].at(e), dot[k]);
+        for (int k = 0; k < kCand; ++k) dot[k] = fmaf(x, raw8_at(raw[j][k], e), dot[k]);
       }
   }
 #pragma unroll
@@ -953,8 +1050,15 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
     s_red[wave][kCand] = hh;
     s_red[wave][kCand + 1] = dd;
   }
+  __shared__ int s_rescan;
   __syncthreads();
-  // every wavefront forms the same exact logits and bounds (uniform values)
+  if (wave != 0) {
+    // wavefronts 1-3 are needed again only for the rare block re-scan, which
+    // wavefront 0 announces after the barrier below
+    __syncthreads();
+    if (!s_rescan) return;
+  }
+  // the exact logits and bounds (the same values in every wavefront that gets here)
   float ze[kCand];
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
@@ -964,7 +1068,6 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   hh = (s_red[0][kCand] + s_red[1][kCand]) + (s_red[2][kCand] + s_red[3][kCand]);
   dd = (s_red[0][kCand + 1] + s_red[1][kCand + 1]) + (s_red[2][kCand + 1] + s_red[3][kCand + 1]);
   // error bounds (rounded up by a small factor for the fp32 evaluation of the norms)
-  const float wmax = *a.wmax;
   const float hn = sqrtf(hh) * 1.0001f;
   // accumulation depth of a screened logit: sequential fp32 FMAs (fp32 screen);
   // for the MFMA screen every 32x32x16 step is counted as 17 roundings of up
@@ -979,15 +1082,12 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   const float eps_e = gamma_f32((float)max(8 * NB, 8 * NIT) + 8.f) * hn * wmax;
   const float eps_f = gamma_f32((float)(g.hidden / 2) + 1.f) * hn * wmax;
 
-  int tb = 0;
-#pragma unroll
-  for (int k = 1; k < kCand; ++k)
-    if (ranks_before(ze[k], besti[k], ze[tb], besti[tb])) tb = k;
+  int tb = 0;                        // tracked by value: no indexing by tb
   float zbest = ze[0];
   int ibest = besti[0];
 #pragma unroll
   for (int k = 1; k < kCand; ++k)
-    if (tb == k) { zbest = ze[k]; ibest = besti[k]; }
+    if (ranks_before(ze[k], besti[k], zbest, ibest)) { tb = k; zbest = ze[k]; ibest = besti[k]; }
 
   // 3. the bound on every column left out, and the re-scoring it may call for
   float dmax = bestv[kCand];
@@ -1003,7 +1103,10 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
     if (same == 3 && last && besti[k] != 0x7fffffff) dmax = fmaxf(dmax, bestv[k]);
   }
   const bool rescan = dmax != kNegInf && dmax + eps_s >= zbest - eps_e;   // uniform over the block
-  if (!rescan && wave != 0) return;         // the rest is wavefront 0's unless the block re-scores
+  if (wave == 0) {
+    if (lane == 0) s_rescan = rescan ? 1 : 0;
+    __syncthreads();                        // pairs with the barrier wavefronts 1-3 wait at
+  }
   int flags = 0;
   float zrun = kNegInf;              // runner-up exact logit among everything re-scored
   int irun = 0x7fffffff;
@@ -1091,10 +1194,10 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
           for (int e0 = 0; e0 < half_len; e0 += 8) {
             Raw8<float> hx;
             Raw8<WT> wx;
-            hx.load(hp + e0);
-            wx.load(wp + e0);
+            hx = raw8_load(hp + e0);
+            wx = raw8_load(wp + e0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(hx.at(e), wx.at(e), acc);
+            for (int e = 0; e < 8; ++e) acc = fmaf(raw8_at(hx, e), raw8_at(wx, e), acc);
           }
         }
         const float other = __shfl_xor(acc, 1);
@@ -1242,7 +1345,8 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   }
   int n_split = 1;
   const int chunks = g.hidden / kKChunk;
-  while (n_split < 8 && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks && chunks % (n_split * 2) == 0 &&
+  while (n_split < 4 && M <= kSplitMaxRows && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks &&
+         chunks % (n_split * 2) == 0 &&
          (int64_t)n_split * 2 * M * pa.v_pad * 4 <= a.zpart_bytes)
     n_split *= 2;
   hipError_t e;
@@ -1264,12 +1368,17 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
 #undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // split partial logits are summed in split order by the reduce launch,
-  // whose grid spreads the sums over the vocabulary tiles
-  if (n_split > 1) {
+  // split partial logits are summed in split order, by the reduce launch
+  // (whose grid spreads the sums over the vocabulary tiles) or by the
+  // decision kernel itself
+  if (n_split > 1 && !kFoldSplitsInDecide) {
     hipLaunchKernelGGL(k_screen_reduce, dim3(n_vt, (M + 31) / 32), dim3(256), 0, s, g, pa, M, n_split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    pa.n_split = n_split;              // the accumulation depth of the screened values
+    pa.zpart = nullptr;                // the decision reads the reduced tile records
+    pa.tile_w = kVocabTile;
+    return launch_decide<uint16_t>(g, pa, M, s);
   }
   pa.n_split = n_split;
   pa.tile_w = kVocabTile;
