@@ -353,6 +353,22 @@ mdm_status mdm_block_attention(const mdm_block_attn_shape* shape, const uint16_t
                                const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
                                float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mdm_block_attention without a workspace argument.  The per-tile block-id
+ * ranges go to a library-owned static device array of 16384 int32 (64 KiB)
+ * per GPU, which each GPU holds until the process ends; the launch needs
+ * 2 * batch * ceil(n_rows / 64) of them (MDM_E_UNSUPPORTED beyond, checked
+ * before anything is enqueued).  The array's device address is looked up once
+ * per device, on the first call with that device current.  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array; each call writes
+ * the ranges it reads before reading them, so nothing needs clearing, but
+ * calls that overlap on one GPU (e.g. on two streams) race.  Other arguments,
+ * layouts and errors as in mdm_block_attention. */
+mdm_status mdm_block_attention_static(const mdm_block_attn_shape* shape, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                                      float* out, void* stream);
+
 /* Release the host context (device buffers stay the caller's). */
 void mdm_sparse_step_destroy(mdm_ctx* ctx);
 

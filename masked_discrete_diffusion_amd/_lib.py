@@ -110,6 +110,7 @@ _SIGS = {
     "mdm_block_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MdmBlockAttnShape)]),
     "mdm_block_attention": (_I32, [ctypes.POINTER(MdmBlockAttnShape), _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]),
+    "mdm_block_attention_static": (_I32, [ctypes.POINTER(MdmBlockAttnShape), _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -240,6 +241,11 @@ def mdm_block_attention(shape: MdmBlockAttnShape, q, k, v, blocks, n_clean_block
     _check(load().mdm_block_attention(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(blocks),
                                       _ptr(n_clean_blocks), _ptr(out), _ptr(workspace), workspace_bytes,
                                       _ptr(stream)))
+
+
+def mdm_block_attention_static(shape: MdmBlockAttnShape, q, k, v, blocks, n_clean_blocks, out, stream=None):
+    _check(load().mdm_block_attention_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(blocks),
+                                             _ptr(n_clean_blocks), _ptr(out), _ptr(stream)))
 
 
 def mdm_upper_workspace_bytes(cfg: MdmConfig) -> int:

@@ -694,9 +694,11 @@ size_t mdm_block_attention_workspace_bytes(const mdm_block_attn_shape* shape) {
   return block_shape_ok(shape) ? block_ws_bytes(shape) : 0;
 }
 
-mdm_status mdm_block_attention(const mdm_block_attn_shape* s, const uint16_t* q, const uint16_t* k,
-                               const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
-                               float* out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Shape and pointer checks shared by both block-attention entry points.
+mdm_status block_attention_check(const mdm_block_attn_shape* s, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                                 const float* out) {
   if (!block_shape_ok(s))
     return fail(nullptr, MDM_E_ARG, "block attention: sizes must be positive and n_heads a multiple of n_kv_heads");
   if (s->head_dim != kBlockAttnHeadDim)
@@ -704,10 +706,20 @@ mdm_status mdm_block_attention(const mdm_block_attn_shape* s, const uint16_t* q,
   if (s->n_rows > kBlockAttnMaxTiles * kKeyTile)
     return fail(nullptr, MDM_E_UNSUPPORTED, "block attention: %d rows (at most %d)", s->n_rows,
                 kBlockAttnMaxTiles * kKeyTile);
-  if (!q || !k || !v || !blocks || !n_clean_blocks || !out || !workspace)
+  if (!q || !k || !v || !blocks || !n_clean_blocks || !out)
     return fail(nullptr, MDM_E_ARG, "block attention: a required pointer is NULL");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16)
     return fail(nullptr, MDM_E_ARG, "block attention: q, k, v and out must be 16-byte aligned");
+  return MDM_OK;
+}
+}  // namespace
+
+mdm_status mdm_block_attention(const mdm_block_attn_shape* s, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mdm_status st = block_attention_check(s, q, k, v, blocks, n_clean_blocks, out);
+  if (st != MDM_OK) return st;
+  if (!workspace) return fail(nullptr, MDM_E_ARG, "block attention: a required pointer is NULL");
   if ((uintptr_t)workspace % 4) return fail(nullptr, MDM_E_ARG, "block attention: workspace must be 4-byte aligned");
   if (workspace_bytes < block_ws_bytes(s))
     return fail(nullptr, MDM_E_SHAPE, "block attention: workspace has %zu bytes, needs %zu", workspace_bytes,
@@ -715,6 +727,27 @@ mdm_status mdm_block_attention(const mdm_block_attn_shape* s, const uint16_t* q,
   BlockAttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.blk = blocks; a.n_clean = n_clean_blocks; a.out = out;
   a.ranges = static_cast<int32_t*>(workspace);
+  a.B = s->batch; a.n = s->n_rows; a.H = s->n_heads; a.Hkv = s->n_kv_heads;
+  return hip_check(nullptr, launch_block_attention(a, static_cast<hipStream_t>(stream)), "block attention launch");
+}
+
+mdm_status mdm_block_attention_static(const mdm_block_attn_shape* s, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const int32_t* blocks, const int32_t* n_clean_blocks,
+                                      float* out, void* stream) {
+  mdm_status st = block_attention_check(s, q, k, v, blocks, n_clean_blocks, out);
+  if (st != MDM_OK) return st;
+  int32_t* ranges = nullptr;
+  size_t cap = 0;
+  st = hip_check(nullptr, block_attention_static_scratch(&ranges, &cap), "block attention: static range array");
+  if (st != MDM_OK) return st;
+  const size_t need = block_ws_bytes(s) / sizeof(int32_t);
+  if (need > cap)
+    return fail(nullptr, MDM_E_UNSUPPORTED,
+                "block attention (static): batch * ceil(n_rows / 64) = %zu tile ranges, at most %zu", need / 2,
+                cap / 2);
+  BlockAttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.blk = blocks; a.n_clean = n_clean_blocks; a.out = out;
+  a.ranges = ranges;
   a.B = s->batch; a.n = s->n_rows; a.H = s->n_heads; a.Hkv = s->n_kv_heads;
   return hip_check(nullptr, launch_block_attention(a, static_cast<hipStream_t>(stream)), "block attention launch");
 }

@@ -31,9 +31,17 @@
 // keys at 4 neighbouring 4-dim groups hand every lane 4 consecutive keys of
 // one dim, which is what the MFMA operand wants.
 #include <climits>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
+
+// Per-tile block-id ranges of mdm_block_attention_static, for callers that
+// cannot allocate: 16384 int32 (64 KiB), which every GPU the library runs on
+// holds until the process ends.  Host code never passes this name to a kernel
+// (in host code it is a host-side stand-in); it uses the device address that
+// block_attention_static_scratch() looks up.
+static __device__ __align__(256) int32_t scratch[mdm::kStaticRangeInts];
 
 namespace mdm {
 
@@ -610,6 +618,29 @@ hipError_t launch_block_attention(BlockAttnArgs a, hipStream_t s) {
   a.real_blocks = a.B * a.Hkv * a.nbk;
   hipLaunchKernelGGL(k_block_attn, dim3(a.real_blocks), dim3(kBaThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress the first time a device is current here, then kept per
+// device (each GPU holds its own copy of the array at its own address).
+hipError_t block_attention_static_scratch(int32_t** ptr, size_t* n_ints) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<int32_t*>(p);
+  }
+  *ptr = addr[dev];
+  *n_ints = kStaticRangeInts;
+  return hipSuccess;
 }
 
 }  // namespace mdm

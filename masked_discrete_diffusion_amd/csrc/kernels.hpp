@@ -204,4 +204,9 @@ struct BlockAttnArgs {
 };
 hipError_t launch_block_attention(BlockAttnArgs a, hipStream_t s);
 
+// The library-owned range array of the allocation-free block attention:
+// kStaticRangeInts int32 per GPU; *ptr = its device address on the current device.
+constexpr int kStaticRangeInts = 16384;
+hipError_t block_attention_static_scratch(int32_t** ptr, size_t* n_ints);
+
 }  // namespace mdm
