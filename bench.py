@@ -30,6 +30,13 @@ Training-form attention (the block-mask forward of the same method):
         bf16 MFMA peak, timed with HIP events over K launches, and the CPU
         oracle on a bounded sample.
 
+Speed-up switches (page 1, ablation Table 6: cache prompt / cache res /
+truncate res, and the plain bidirectional dense MDM):
+    python bench.py --ablation [--ablation-steps K]
+        one JSON line per setting: tokens unmasked/s of whole generations of
+        the workload under that setting (HIP-graph replays, as above) and its
+        speed-up over the setting with every switch off.
+
 Profiling helpers (used to produce profiles/):
     python bench.py --profile-steps N         N eager generations, nothing else
     python bench.py --copy-calibration        one plain 1 GiB device copy
@@ -345,6 +352,58 @@ def block_attention_cpu_baseline(inp, budget_s):
                       f"({cfg.n_rows} rows each) in {dt:.1f} s, float64 NumPy"}
 
 
+def ablation_bench(args):
+    """Every setting of the speed-up switches on the workload, each timed as
+    whole generations replayed from a HIP graph."""
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    from masked_discrete_diffusion_amd.ablation import ALL_SWITCHES, AblationRunner, switch_work
+    from mdm_inputs import get_config, make_workload
+
+    cfg = get_config(args.workload)
+    wl = make_workload(cfg)
+    print(f"[bench] {cfg.name}: switch settings, workload ready", file=sys.stderr, flush=True)
+    base = None
+    for sw in ALL_SWITCHES:
+        run = AblationRunner(wl, sw, device="cuda:0")
+        run.generate()
+        torch.cuda.synchronize()
+        L.mdm_device_status(run.ctx)
+        graph = run.capture_graph()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.ablation_steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        L.mdm_device_status(run.ctx)
+        value = cfg.batch * cfg.gen_len * args.ablation_steps / elapsed
+        if base is None:
+            base = value
+        res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+               "steps": args.ablation_steps, "warmup": args.warmup,
+               "ms_per_step": round(elapsed / args.ablation_steps * 1e3, 4), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.precision == "bf16" else "fp32",
+               "data": "synthetic",
+               "config": {"workload": f"{cfg.name}/{sw.name}", "batch": cfg.batch, "prompt_tokens": cfg.prompt_len,
+                          "image_tokens": cfg.gen_len, "sampling_steps": cfg.n_steps,
+                          "registers": run.n_registers, "cache_prompt": sw.cache_prompt,
+                          "cache_res": sw.cache_res, "truncate": sw.truncate,
+                          "bidirectional": sw.bidirectional, "parallelism": "none"},
+               "speedup_vs_all_off": round(value / base, 3)}
+        att, head = switch_work(cfg, run.counts, sw)
+        gen_s = elapsed / args.ablation_steps
+        res["algorithmic_tflop_per_generation"] = {"attention": round(att / 1e12, 3), "head": round(head / 1e12, 3)}
+        res["mfma_frac"] = round((att + head) / gen_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        print(json.dumps(res), flush=True)
+        del graph
+        run.close()
+        del run
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +422,9 @@ def main():
                     help="run one plain device copy of 1 GiB (counter calibration) and exit")
     ap.add_argument("--block-attention", action="store_true",
                     help="time the training-form block-mask attention (workload train_t2i_4k or train_text)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time every setting of the speed-up switches (cache prompt / cache res / truncate)")
+    ap.add_argument("--ablation-steps", type=int, default=5)
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
                     help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR: write the attention traffic summary")
     args = ap.parse_args()
@@ -386,6 +448,9 @@ def main():
         return
     if args.block_attention:
         block_attention_bench(args)
+        return
+    if args.ablation:
+        ablation_bench(args)
         return
     from masked_discrete_diffusion_amd import _lib as L
     from masked_discrete_diffusion_amd.sampler import SparseStepRunner

@@ -232,6 +232,17 @@ mdm_status mdm_sparse_step_reset(mdm_ctx* ctx);
 /* Current cache length (host bookkeeping), -1 for NULL. */
 int32_t mdm_cache_len(const mdm_ctx* ctx);
 
+/* Shorten the cache to its first new_len slots (page 1, ablation Table 6: the
+ * prompt and the decoded tokens may be recomputed at every step instead of
+ * being kept, so a caller appends them again and drops them after the step).
+ * Host bookkeeping only: nothing is enqueued, and later appends overwrite the
+ * dropped slots.  Unless new_len equals the current length, the queries kept
+ * by the last append are dropped too (a later mdm_step_attention rotates its
+ * D rows itself; mdm_order_step then needs n_new_cached == 0).  MDM_E_ARG if
+ * new_len < 0 or new_len > the current length; MDM_E_UNSUPPORTED with upper
+ * layers attached (their caches are not shortened). */
+mdm_status mdm_cache_rewind(mdm_ctx* ctx, int32_t new_len);
+
 /* Synchronise the stream, read and clear the kernels' sticky range-check flag.
  * MDM_E_DEVICE if any kernel met an out-of-range token id or position. */
 mdm_status mdm_device_status(mdm_ctx* ctx);

@@ -97,6 +97,7 @@ _SIGS = {
     "mdm_order_step": (_I32, [_P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "mdm_sparse_step_reset": (_I32, [_P]),
     "mdm_cache_len": (_I32, [_P]),
+    "mdm_cache_rewind": (_I32, [_P, _I32]),
     "mdm_device_status": (_I32, [_P]),
     "mdm_set_decision_trace": (_I32, [_P, _P]),
     "mdm_decision_counts": (_I32, [_P, ctypes.POINTER(_I64)]),
@@ -206,6 +207,10 @@ def mdm_sparse_step_reset(ctx):
 
 def mdm_cache_len(ctx) -> int:
     return load().mdm_cache_len(ctx)
+
+
+def mdm_cache_rewind(ctx, new_len: int):
+    _check(load().mdm_cache_rewind(ctx, new_len), ctx)
 
 
 def mdm_device_status(ctx):

@@ -641,6 +641,16 @@ mdm_status mdm_layer_attention(mdm_ctx* ctx, int32_t layer, int32_t n_new_cached
 
 int32_t mdm_cache_len(const mdm_ctx* ctx) { return ctx ? ctx->len : -1; }
 
+mdm_status mdm_cache_rewind(mdm_ctx* ctx, int32_t new_len) {
+  if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
+  if (ctx->has_upper) return fail(ctx, MDM_E_UNSUPPORTED, "rewind with upper layers attached");
+  if (new_len < 0 || new_len > ctx->len)
+    return fail(ctx, MDM_E_ARG, "new length %d outside [0, cache length %d]", new_len, ctx->len);
+  if (new_len != ctx->len) ctx->q_rows = -1;
+  ctx->len = new_len;
+  return MDM_OK;
+}
+
 mdm_status mdm_set_decision_trace(mdm_ctx* ctx, float* trace) {
   if (!ctx) return fail(nullptr, MDM_E_ARG, "ctx is NULL");
   if (reinterpret_cast<uintptr_t>(trace) % 16) return fail(ctx, MDM_E_ARG, "trace must be 16-byte aligned");

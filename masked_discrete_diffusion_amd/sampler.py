@@ -82,7 +82,11 @@ class SparseStepRunner:
     """Device state of one workload: tables, caches, workspace, loop buffers."""
 
     def __init__(self, wl, device: str = "cuda", accurate_conf: Optional[bool] = None,
-                 precision: Optional[str] = None, fused: bool = True):
+                 precision: Optional[str] = None, fused: bool = True, n_registers: Optional[int] = None,
+                 max_decode: Optional[int] = None, out_rows: Optional[int] = None, n_out: Optional[int] = None):
+        """n_registers, max_decode, out_rows (query rows per sequence of the
+        output buffers) and n_out (number of output buffers) override the
+        values the workload's plan implies (the ablation loops use them)."""
         cfg = wl.cfg
         self.wl, self.cfg = wl, cfg
         self.device = torch.device(device)
@@ -92,11 +96,13 @@ class SparseStepRunner:
         if accurate_conf is None:
             accurate_conf = cfg.schedule == "semi_ar"
         self.plan = make_plan(wl)
-        max_decode = max(p.n_c for p in self.plan)
+        if max_decode is None:
+            max_decode = max(p.n_c for p in self.plan)
         max_sel = max(p.n_sel for p in self.plan)
+        self.n_registers = cfg.n_registers if n_registers is None else n_registers
         self.mc = L.MdmConfig(batch=cfg.batch, n_heads=cfg.n_heads, n_kv_heads=cfg.n_kv_heads,
                               head_dim=cfg.head_dim, vocab=cfg.vocab, seq_len=cfg.seq_len,
-                              n_registers=cfg.n_registers, max_decode=max_decode,
+                              n_registers=self.n_registers, max_decode=max_decode,
                               precision=L.MDM_BF16 if self.precision == "bf16" else L.MDM_FP32,
                               accurate_conf=int(bool(accurate_conf)), rope_theta=cfg.rope_theta)
         dev = self.device
@@ -128,8 +134,9 @@ class SparseStepRunner:
         self.order = (torch.from_numpy(wl.order.astype(np.int32)).to(dev) if wl.order is not None
                       else torch.zeros(B, 1, **i32))
         self.block_pos = torch.from_numpy(np.ascontiguousarray(wl.gen_pos, dtype=np.int32)).to(dev)
-        self.d_tok = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
-        self.d_pos = [torch.zeros(B * max_sel, **i32) for _ in range(2)]
+        self.max_decode = max_decode
+        self.d_tok = [torch.zeros(B * max(max_sel, max_decode), **i32) for _ in range(2)]
+        self.d_pos = [torch.zeros(B * max(max_sel, max_decode), **i32) for _ in range(2)]
         self.rem = [torch.zeros(B * max_decode, **i32) for _ in range(2)]
         self.layers = cfg.layers
         # A pre-generated order on one bf16 layer runs each step as one fused
@@ -140,9 +147,10 @@ class SparseStepRunner:
         rows = max(p.n_d + p.n_c for p in self.plan)
         if self.layers > 1:
             rows = max(rows, cfg.prompt_len)          # the prefill's first-layer rows feed layer 2
-        self.n_q_max = rows + cfg.n_registers
+        self.n_q_max = rows + self.n_registers if out_rows is None else out_rows
         # layer outputs: layer l writes outs[(l - 1) % 2]; the logits read the last one
-        n_out = 1 if self.layers == 1 else 2
+        if n_out is None:
+            n_out = 1 if self.layers == 1 else 2
         self.outs = [torch.zeros(B * self.n_q_max * cfg.hidden, dtype=torch.float32, device=dev)
                      for _ in range(n_out)]
         self.out = self.outs[(self.layers - 1) % n_out]

@@ -39,7 +39,7 @@ import numpy as np
 from . import rope
 from .attention import attend
 from .logits import decide, subset_logits, top_two
-from .masks import step_mask
+from .masks import CACHED, DECODE, NEW, inference_mask, step_mask
 from .numerics import round_bf16, round_storage, table_values
 from .select import select_all, select_by_confidence
 
@@ -201,6 +201,48 @@ class SequenceOracle:
         o = outs[-1]
         return StepOut(o=o, h=o[n_d:n_d + n_c], o_layers=outs)
 
+    def forward_untruncated(self, d_tok, d_pos, c_pos, m_pos) -> StepOut:
+        """The step with truncation switched off (page 1, ablation Table 6:
+        "truncate res" off).  Every still-masked position m_pos (a superset of
+        c_pos) is present as the mask token and there are no registers, which
+        stand in only for truncated tokens (page 3, section 7.2: with every
+        masked position present the parameterization is the standard MDM's).
+        The step-causal rule still holds: D rows see the cache and D; the
+        decoded rows C see everything present.  Returns rows [D | C] (the
+        masked rows outside C enter only as keys; their own outputs never reach
+        a decision).  One layer: a second would need every masked row's
+        first-layer output."""
+        if self.layers != 1:
+            raise NotImplementedError("the untruncated step is modelled for one layer")
+        m = self.m
+        d_tok = np.asarray(d_tok, dtype=np.int64)
+        d_pos = np.asarray(d_pos, dtype=np.int64)
+        c_pos = np.asarray(c_pos, dtype=np.int64)
+        m_pos = np.asarray(m_pos, dtype=np.int64)
+        if not np.isin(c_pos, m_pos).all():
+            raise ValueError("decoded positions must be masked")
+        n_d, n_c, n_m = d_tok.size, c_pos.size, m_pos.size
+        q_ids = np.concatenate([d_tok, np.full(n_c, m.mask_id, np.int64)])
+        q_pos = np.concatenate([d_pos, c_pos])
+        q, _, _ = m.qkv_layer1(q_ids, q_pos)
+        _, k_dm, v_dm = m.qkv_layer1(np.concatenate([d_tok, np.full(n_m, m.mask_id, np.int64)]),
+                                     np.concatenate([d_pos, m_pos]))
+        n_cache = self.n
+        vis = inference_mask([NEW] * n_d + [DECODE] * n_c,
+                             [CACHED] * n_cache + [NEW] * n_d + [DECODE] * n_m)
+        keys_k = np.concatenate([self.k[0][:n_cache], k_dm])
+        keys_v = np.concatenate([self.v[0][:n_cache], v_dm])
+        o = attend(q, keys_k, keys_v, vis).reshape(n_d + n_c, m.hidden)
+        self._commit(0, k_dm[:n_d], v_dm[:n_d])
+        self.n += n_d
+        self.cache_tok.extend(d_tok.tolist())
+        self.cache_pos.extend(d_pos.tolist())
+        return StepOut(o=o, h=o[n_d:], o_layers=[o])
+
+    def masked_positions(self) -> np.ndarray:
+        """Positions still holding the mask token, ascending."""
+        return np.flatnonzero(self.x == self.m.mask_id).astype(np.int64)
+
     def write_tokens(self, pos, tok):
         self.x[np.asarray(pos, dtype=np.int64)] = tok
 
@@ -245,8 +287,11 @@ def step_candidates(wl, k, b, remaining):
 
 
 def run_workload(wl, batches=None, n_steps: Optional[int] = None, keep_steps=(),
-                 precision: Optional[str] = None, model: Optional[Model] = None) -> RunResult:
-    """Run the sparse sampler on sequences `batches` of workload `wl`."""
+                 precision: Optional[str] = None, model: Optional[Model] = None,
+                 truncate: bool = True) -> RunResult:
+    """Run the sparse sampler on sequences `batches` of workload `wl`.
+    truncate=False runs every step with all masked positions present and no
+    registers (SequenceOracle.forward_untruncated)."""
     cfg = wl.cfg
     batches = list(range(cfg.batch)) if batches is None else list(batches)
     model = model or Model.from_workload(wl, precision=precision)
@@ -263,7 +308,11 @@ def run_workload(wl, batches=None, n_steps: Optional[int] = None, keep_steps=(),
         for i, b in enumerate(batches):
             c_pos = step_candidates(wl, k, b, remaining)
             c_list.append(c_pos)
-            outs.append(seqs[i].forward(d_state[i][0], d_state[i][1], c_pos))
+            if truncate:
+                outs.append(seqs[i].forward(d_state[i][0], d_state[i][1], c_pos))
+            else:
+                outs.append(seqs[i].forward_untruncated(d_state[i][0], d_state[i][1], c_pos,
+                                                        seqs[i].masked_positions()))
         h = np.concatenate([o.h for o in outs])
         z = subset_logits(h, model.w)
         token, conf32, conf64, margin = decide(z)

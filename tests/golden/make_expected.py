@@ -1,6 +1,6 @@
 """Write the oracle's expected results for the five workloads.
 
-    python tests/golden/make_expected.py [config ...]
+    python tests/golden/make_expected.py [--untruncated] [config ...]
 
 Calls only ``oracle`` (and the shared input generator ``mdm_inputs``); the
 HIP path plays no part.  For each workload it stores, in
@@ -21,6 +21,11 @@ HIP path plays no part.  For each workload it stores, in
             sequence 0) whose h is stored
   h_vals    [len(o_steps)][3][hidden] those rows' h (float64): the tests form
             the exact logits h W^T and the bf16 screen's h_bf16 W^T from them
+
+With --untruncated the loop runs with truncation switched off (every masked
+position present, no registers; oracle.step.SequenceOracle.forward_untruncated)
+and writes ``expected_untruncated_<name>.npz`` with the same fields (query rows
+[D | C], no register rows).
 """
 
 from __future__ import annotations
@@ -49,11 +54,11 @@ def o_steps_of(cfg):
     return sorted({1, n // 2, n - 1})
 
 
-def expected(cfg):
+def expected(cfg, truncate=True):
     wl = make_workload(cfg)
     steps = o_steps_of(cfg)
     t = time.time()
-    res = run_workload(wl, keep_steps=steps)
+    res = run_workload(wl, keep_steps=steps, truncate=truncate)
     dt = time.time() - t
     B = cfg.batch
     sel_pos = [np.concatenate([r.c_pos[b][r.selected[b]] for r in res.records]) for b in range(B)]
@@ -67,7 +72,7 @@ def expected(cfg):
     for k in steps:
         r = res.records[k]
         n_d, n_c = r.d_pos[0].size, r.c_pos[0].size
-        rows = sample_rows(n_d, n_c, cfg.n_registers)
+        rows = sample_rows(n_d, n_c, cfg.n_registers if truncate else 0)
         rows = (rows + [rows[-1]] * 6)[:6]
         o_rows.append(rows)
         o_vals.append(r.o[0][rows].astype(np.float32))
@@ -83,11 +88,14 @@ def expected(cfg):
     return out, dt
 
 
-def main(names):
+def main(args):
+    truncate = "--untruncated" not in args
+    names = [a for a in args if a != "--untruncated"]
     cfgs = [get_config(n) for n in names] if names else list(CONFIGS)
     for cfg in cfgs:
-        out, dt = expected(cfg)
-        path = os.path.join(HERE, f"expected_{cfg.name}.npz")
+        out, dt = expected(cfg, truncate)
+        stem = "expected_" if truncate else "expected_untruncated_"
+        path = os.path.join(HERE, f"{stem}{cfg.name}.npz")
         np.savez_compressed(path, **out)
         print(f"{cfg.name}: oracle {dt:.1f}s, min margin {out['margin'].min():.3g}, "
               f"min conf gap {np.nanmin(out['conf_gap']) if np.isfinite(out['conf_gap']).any() else float('nan'):.3g}"

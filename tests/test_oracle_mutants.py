@@ -166,3 +166,35 @@ def test_mutant_layer2_query_block_transposed(monkeypatch):
     monkeypatch.setattr(step_mod, "split_layer2", split)
     with pytest.raises(AssertionError):
         T_two.test_two_layer_step_matches_bruteforce()
+
+
+# ---- untruncated step: each planted mistake must break one of its pins -----
+import test_oracle_untruncated as T_unt
+
+
+def test_mutant_untruncated_keeps_only_the_decoded_masks(monkeypatch):
+    orig = step_mod.SequenceOracle.forward_untruncated
+    monkeypatch.setattr(step_mod.SequenceOracle, "forward_untruncated",
+                        lambda self, dt, dp, c, m: orig(self, dt, dp, c, c))
+    with pytest.raises(AssertionError):
+        T_unt.test_untruncated_matches_training_form_forward(T_unt.tiny_bf16)
+    with pytest.raises(AssertionError):
+        T_unt.test_untruncated_step_matches_bruteforce()
+
+
+def test_mutant_untruncated_new_rows_see_masks(monkeypatch):
+    orig = step_mod.inference_mask
+
+    def inference_mask(qk, kk):
+        return orig([masks_mod.DECODE if q == masks_mod.NEW else q for q in qk], kk)
+    monkeypatch.setattr(step_mod, "inference_mask", inference_mask)
+    with pytest.raises(AssertionError):
+        T_unt.test_untruncated_step_matches_bruteforce()
+
+
+def test_mutant_untruncated_masked_rows_at_wrong_positions(monkeypatch):
+    orig = step_mod.SequenceOracle.masked_positions
+    monkeypatch.setattr(step_mod.SequenceOracle, "masked_positions",
+                        lambda self: np.unique(np.concatenate([orig(self), orig(self) - 1])))
+    with pytest.raises(AssertionError):
+        T_unt.test_untruncated_matches_training_form_forward(T_unt.tiny_bf16)
