@@ -166,6 +166,90 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print(json.dumps(t))
 
 
+def _trace_durations(trace_dir):
+    """{kernel name: [durations in ns in dispatch order]} from a --kernel-trace csv."""
+    import csv
+    import glob
+    out = {}
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            out.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def _short(name):
+    n = name.replace("void ", "").replace("mdm::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def pmc_summary(trace_dir, sq_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload="c3_t2i_4k"):
+    """Per-kernel counter summary of one eager generation (--profile-steps 1
+    runs under rocprofv3 --pmc) with durations from a --kernel-trace run of
+    two generations: MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over every
+    SIMD's cycles of the traced duration at 2.4 GHz), VALU instructions, and
+    HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by a plain copy) against the
+    algorithmic bytes of the same calls."""
+    from mdm_inputs import get_config, make_workload
+    from masked_discrete_diffusion_amd.sampler import make_plan
+    cfg = get_config(workload)
+    wl = make_workload(cfg, tables=False)
+    plan = make_plan(wl)
+    a_flops, a_bytes = attention_work(cfg, plan)
+    l_flops, l_bytes = logits_work(cfg, plan)
+
+    def largest(d, counter):
+        vals = [v for per in _pmc_dispatches(d, counter).values() for v in per.values()]
+        return max(vals)
+    f_scale = COPY_BYTES / 1024.0 / largest(copy_fetch_dir, "FETCH_SIZE")
+    w_scale = COPY_BYTES / 1024.0 / largest(copy_write_dir, "WRITE_SIZE")
+    groups = {"step attention (k_attn_bf16, all variants)": "k_attn_bf16",
+              "vocabulary screen (k_screen_bf16, all variants)": "k_screen_bf16",
+              "screen split reduce (k_screen_reduce)": "k_screen_reduce",
+              "decision (k_decide)": "k_decide"}
+    dur = _trace_durations(trace_dir)
+    tabs = {c: _pmc_dispatches(d, c) for c, d in (("SQ_VALU_MFMA_BUSY_CYCLES", sq_dir), ("SQ_INSTS_VALU", sq_dir),
+                                                  ("SQ_WAVES", sq_dir), ("FETCH_SIZE", fetch_dir),
+                                                  ("WRITE_SIZE", write_dir))}
+    lines = []
+    for label, key in groups.items():
+        ds = [v for n, vs in dur.items() if key in n for v in vs]
+        n_calls = len(ds) // 2                       # two generations traced
+        if not n_calls:
+            continue
+        mean_ns = sum(ds) / len(ds)
+        per = {}
+        for c, tab in tabs.items():
+            vals = [v for n, pv in tab.items() if key in n for v in pv.values()]
+            per[c] = sum(vals) / max(len(vals), 1)
+        mfma = per["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * mean_ns * 2.4)
+        hbm = per["FETCH_SIZE"] * f_scale * 1024 + per["WRITE_SIZE"] * w_scale * 1024
+        if key == "k_attn_bf16":
+            alg, fl = a_bytes.mean(), a_flops.mean()
+        elif key == "k_screen_bf16":
+            alg, fl = l_bytes.mean(), l_flops.mean()
+        else:
+            alg, fl = float("nan"), float("nan")
+        variants = sorted({_short(n) for n in dur if key in n})
+        lines.append(f"{label}\n"
+                     f"  variants                 {', '.join(variants)}\n"
+                     f"  calls per generation     {n_calls}\n"
+                     f"  mean duration            {mean_ns / 1e3:.2f} us (kernel trace)\n"
+                     f"  MFMA busy                {mfma:.3f} of all SIMD cycles\n"
+                     f"  VALU instructions        {per['SQ_INSTS_VALU']:.4g} per call ({per['SQ_WAVES']:.0f} waves)\n"
+                     f"  HBM fetch + write        {hbm / 1e6:.2f} MB per call (FETCH_SIZE x{f_scale:.3f}, "
+                     f"WRITE_SIZE x{w_scale:.3f})\n"
+                     + (f"  algorithmic bytes        {alg / 1e6:.2f} MB per call (measured / algorithmic "
+                        f"{hbm / alg:.2f})\n"
+                        f"  algorithmic FLOP         {fl / 1e9:.2f} GFLOP per call = "
+                        f"{fl / (mean_ns * 1e-9) / 1e12:.1f} TFLOP/s, {fl / (mean_ns * 1e-9) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.3f}"
+                        f" of the bf16 peak; {alg / (mean_ns * 1e-9) / 1e9:.0f} GB/s, "
+                        f"{alg / (mean_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s\n" if alg == alg else ""))
+    text = "\n".join(lines)
+    print(text)
+    return text
+
+
 def cpu_threads(n):
     """Context that caps the BLAS thread pools at n threads (n <= 0: no cap)."""
     import contextlib
@@ -425,11 +509,16 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="time every setting of the speed-up switches (cache prompt / cache res / truncate)")
     ap.add_argument("--ablation-steps", type=int, default=5)
+    ap.add_argument("--pmc-summary", nargs=6, metavar="DIR",
+                    help="TRACE SQ FETCH WRITE COPY_FETCH COPY_WRITE: per-kernel counter summary (stdout)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
                     help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR: write the attention traffic summary")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, workload=args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
