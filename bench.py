@@ -659,6 +659,18 @@ def main():
                     "calls": n * n_up, "avg_call_us": round(proj_ms.mean() / n_up * 1e3, 2),
                     "algorithmic_flops_per_call": round(float(p_flops.mean() / n_up), 0),
                     "first_layer_attention": roofline}
+    # the logits call (screen, split reduce, decision): per step, the time the
+    # roofline allows is the larger of its W + h stream at the HBM peak and its
+    # product at the bf16 MFMA peak
+    l_roof_s = np.maximum(l_bytes / (HBM_PEAK_GBS * 1e9), l_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    l_s = log_ms.sum() / 1e3
+    logits_roofline = {"bound": "hbm below ~300 rows per step, mfma above (per step: the larger)",
+                       "frac": round(float(l_roof_s.sum() / l_s), 4),
+                       "roofline_ms": round(float(l_roof_s.sum() * 1e3), 4), "measured_ms": round(l_s * 1e3, 4),
+                       "achieved_tflops": round(float(l_flops.sum() / l_s / 1e12), 2),
+                       "achieved_gbs": round(float(l_bytes.sum() / l_s / 1e9), 1),
+                       "avg_call_us": round(float(log_ms.mean() * 1e3), 2),
+                       "kernel": "mdm_subset_logits_confidence: k_screen_bf16 (+ k_screen_reduce) + k_decide"}
     both_s = att_s + log_ms.sum() / 1e3
     step_frac = (a_flops.sum() + l_flops.sum()) / both_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
 
@@ -681,6 +693,7 @@ def main():
                    "vocab": cfg.vocab, "schedule": cfg.schedule, "order": cfg.order, "layers": cfg.layers,
                    "parallelism": "none"},
         "roofline": roofline,
+        "logits_roofline": logits_roofline,
         "step_attn_logits_mfma_frac": round(step_frac, 4),
         "kernel_ms_per_generation": {"attention": round(att_ms.sum(), 4), "logits": round(log_ms.sum(), 4),
                                      **({"upper_projection": round(proj_ms.sum(), 4),

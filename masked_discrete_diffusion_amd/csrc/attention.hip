@@ -415,13 +415,15 @@ __device__ inline floatx16 s_half(const uint16_t* kb, const bf16x8* qf, int hk, 
   floatx16 sv;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sv[e] = 0.f;
+  // all eight K operands are read before the MFMA chain: read one by one in
+  // front of their MFMAs, every MFMA waited a full LDS latency (same-box C3:
+  // attention -2 %)
+  bf16x8 kf[NKS];
 #pragma unroll
-  for (int t = 0; t < NKS; ++t) {
-    // at most four K operands in flight: the scheduler would otherwise hoist
-    // all eight LDS reads (32 VGPRs) above the MFMA chain
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
-    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv, 0, 0, 0);
-  }
+  for (int t = 0; t < NKS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kbase + (2 * t) * 8);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[t], sv, 0, 0, 0);
   return sv;
 }
 

@@ -276,18 +276,26 @@ __global__ __launch_bounds__(4 * NG * kWave) void k_screen_bf16(Geometry g, Voca
     if (nxt < n_chunks)
       screen_dma<S>(wrow + nxt * kKChunk, hrow + nxt * kKChunk, lrow + nxt * kKChunk, wave, off, kind,
                     ring_lds + (nxt % S::NST) * (S::ELEMS * 2));
+    // the stage's operands are all read before its MFMAs (one LDS latency per
+    // stage instead of one per MFMA)
     const uint16_t* st = ring[ci % S::NST];
+    bf16x8 wf[kKChunk / 16], hf[kKChunk / 16][RBW], lf[kKChunk / 16][RBW];
 #pragma unroll
     for (int t = 0; t < kKChunk / 16; ++t) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + woff[t]);
+      wf[t] = *reinterpret_cast<const bf16x8*>(st + woff[t]);
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
-        const bf16x8 hf = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff[t] + rb * 32 * S::RU * 8);
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hf, acc[rb], 0, 0, 0);
-        if (kLo) {
-          const bf16x8 lf = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff[t] + rb * 32 * S::RU * 8);
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lf, acc[rb], 0, 0, 0);
-        }
+        hf[t][rb] = *reinterpret_cast<const bf16x8*>(st + S::H_OFF + hoff[t] + rb * 32 * S::RU * 8);
+        if (kLo) lf[t][rb] = *reinterpret_cast<const bf16x8*>(st + S::L_OFF + hoff[t] + rb * 32 * S::RU * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kKChunk / 16; ++t) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], hf[t][rb], acc[rb], 0, 0, 0);
+        if (kLo) acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], lf[t][rb], acc[rb], 0, 0, 0);
       }
     }
   }
