@@ -607,18 +607,30 @@ __device__ inline void tile_loop_quarter(const AttnArgs& a, const Geometry& g, c
                                          int half, int l32, float sc, bool& over) {
   const int tp = q >> 1, hf = q & 1;
   if (FAST && n_comp > 0) {
+    // A half-tile's scores are computed in its own ring step and its softmax
+    // and PV in the next one (its V stays in its ring slot: kStages >= kAhead
+    // + 2), so that every step gives each SIMD part of the fifth chunk (done
+    // in one step, the two SIMDs of that parity carried it alone and the
+    // others waited at the barrier: same-box C3, attention -2 %).
     bool have_ref = false;
+    floatx16 sv;
+    int pend = -1;                        // ring slot of the half-tile whose scores are in sv
     for (int i = 0; i < n_comp; ++i) {
       ring_step<D>(a, g, src, ord, T0, T1, off, ks, vs, i, wave, lane);
+      if (pend >= 0) {
+        finish_half_fixed<D>(sv, vs[pend], hf, acc, m_ref, l_run, half, l32, sc);
+        pend = -1;
+      }
       if ((i & 1) != tp) continue;
       const int cur = i % kStages;
-      floatx16 sv = s_half<D>(ks[cur], qf, hf, krow, half);
+      sv = s_half<D>(ks[cur], qf, hf, krow, half);
       if (!have_ref) {
         m_ref = half_max<false>(sv, 32 * hf, kKeyTile, half, sc);
         have_ref = true;
       }
-      finish_half_fixed<D>(sv, vs[cur], hf, acc, m_ref, l_run, half, l32, sc);
+      pend = cur;
     }
+    if (pend >= 0) finish_half_fixed<D>(sv, vs[pend], hf, acc, m_ref, l_run, half, l32, sc);
     over = !(l_run < 0x1p50f);
   }
   if (!FAST && n_comp > 0) {
