@@ -1099,15 +1099,18 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
 
   // 3. the bound on every column left out, and the re-scoring it may call for
   float dmax = bestv[kCand];
+  int ctile[kCand];                         // each candidate's tile (one division each, not one per pair)
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) ctile[k] = besti[k] / tw;
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
     int same = 0;
 #pragma unroll
-    for (int q = 0; q < kCand; ++q) same += (besti[q] / tw == besti[k] / tw) ? 1 : 0;
+    for (int q = 0; q < kCand; ++q) same += (ctile[q] == ctile[k]) ? 1 : 0;
     // a tile with all three entries among the candidates: its other columns rank after its third
     bool last = true;
 #pragma unroll
-    for (int q = k + 1; q < kCand; ++q) last = last && (besti[q] / tw != besti[k] / tw);
+    for (int q = k + 1; q < kCand; ++q) last = last && (ctile[q] != ctile[k]);
     if (same == 3 && last && besti[k] != 0x7fffffff) dmax = fmaxf(dmax, bestv[k]);
   }
   const bool rescan = dmax != kNegInf && dmax + eps_s >= zbest - eps_e;   // uniform over the block

@@ -153,3 +153,44 @@ def test_switches_full_size_decisions(name):
         err = np.abs(conf.astype(np.float64) - e["conf"].astype(np.float64))
         assert np.all(err <= atol + rtol * np.abs(e["conf"])), f"{sw.name}: confidence error {err.max():.3g}"
         print(f"  {sw.name}: {dec_tok.size} decisions identical, max conf err {err.max():.3g}", flush=True)
+
+
+def test_cache_rewind_bookkeeping_and_errors():
+    """mdm_cache_rewind: shortens the host cache length, refuses lengths
+    outside [0, length] and contexts with upper layers, and drops the queries
+    the last append kept (the fused order step then refuses a non-zero
+    n_new_cached)."""
+    from masked_discrete_diffusion_amd import _lib as L
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    from small_workloads import gpu_two_layer
+    cfg = gpu_small_d128()
+    run = SparseStepRunner(workload(cfg), device="cuda", fused=False)
+    try:
+        run.prefill()
+        P = cfg.prompt_len
+        assert L.mdm_cache_len(run.ctx) == P
+        for bad in (P + 1, -1):
+            with pytest.raises(L.MdmError) as e:
+                L.mdm_cache_rewind(run.ctx, bad)
+            assert e.value.status == L.MDM_E_ARG
+        L.mdm_cache_rewind(run.ctx, P)                      # no-op
+        assert L.mdm_cache_len(run.ctx) == P
+        n = 4
+        L.mdm_kv_append(run.ctx, run.prompt_tok, run.prompt_pos, P, n)   # queries kept for these n rows
+        L.mdm_cache_rewind(run.ctx, P + n - 1)
+        assert L.mdm_cache_len(run.ctx) == P + n - 1
+        with pytest.raises(L.MdmError) as e:
+            L.mdm_order_step(run.ctx, n - 1, run.order, cfg.gen_len, 1, 0, run.outs[0], run.conf, run.token,
+                             None, None)
+        assert e.value.status == L.MDM_E_ARG
+        L.mdm_device_status(run.ctx)
+    finally:
+        run.close()
+    cfg2 = gpu_two_layer()
+    run2 = SparseStepRunner(workload(cfg2), device="cuda")
+    try:
+        with pytest.raises(L.MdmError) as e:
+            L.mdm_cache_rewind(run2.ctx, 0)
+        assert e.value.status == L.MDM_E_UNSUPPORTED
+    finally:
+        run2.close()
