@@ -116,7 +116,7 @@ struct VocabArgs {
   int emit;                 // nonzero: the screen writes the raw product to zpart [M][v_pad] and stops
   int prepacked;            // nonzero: hhi (and hlo) already hold rows 0..M-1 (no k_pack); rows
                             // M..m_pad-1 hold finite values that only reach their own logits
-  // Fused unmasking in a pre-generated order (k_merge): with cand_pos != NULL,
+  // Fused unmasking in a pre-generated order (k_decide): with cand_pos != NULL,
   // row m = (b, c) is unmasked at position cand_pos[b*cand_stride + c]:
   // seq_tokens[b][pos] = its token (when seq_tokens != NULL).
   const int32_t* cand_pos;

@@ -668,7 +668,7 @@ __global__ __launch_bounds__(256) void k_screen_f32(Geometry g, VocabArgs a, int
 }
 
 // ---------------------------------------------------- decide (merge) --
-// One wavefront per row (four rows per block).  The decision is the argmax of
+// One 256-thread block per row.  The decision is the argmax of
 // the exact fp32 logits z = h W^T over the whole vocabulary, which the screen
 // only approximates; the kernel makes that exact as follows.
 //
