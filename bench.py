@@ -205,6 +205,7 @@ def pmc_summary(trace_dir, sq_dir, fetch_dir, write_dir, copy_fetch_dir, copy_wr
     w_scale = COPY_BYTES / 1024.0 / largest(copy_write_dir, "WRITE_SIZE")
     groups = {"step attention (k_attn_bf16, all variants)": "k_attn_bf16",
               "vocabulary screen (k_screen_bf16, all variants)": "k_screen_bf16",
+              "wide vocabulary screen (k_screen_wide, all variants)": "k_screen_wide",
               "screen split reduce (k_screen_reduce)": "k_screen_reduce",
               "decision (k_decide)": "k_decide"}
     dur = _trace_durations(trace_dir)
@@ -226,7 +227,7 @@ def pmc_summary(trace_dir, sq_dir, fetch_dir, write_dir, copy_fetch_dir, copy_wr
         hbm = per["FETCH_SIZE"] * f_scale * 1024 + per["WRITE_SIZE"] * w_scale * 1024
         if key == "k_attn_bf16":
             alg, fl = a_bytes.mean(), a_flops.mean()
-        elif key == "k_screen_bf16":
+        elif key in ("k_screen_bf16", "k_screen_wide"):
             alg, fl = l_bytes.mean(), l_flops.mean()
         else:
             alg, fl = float("nan"), float("nan")
