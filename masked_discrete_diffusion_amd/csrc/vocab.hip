@@ -438,13 +438,14 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
     }
   }
   const uint32_t ring_lds = lds_addr(&ring[0][0]);
-  // Each 512-column tile walks the hidden dimension from its own starting
-  // chunk (both row tiles of a column tile alike, so that they still stream
-  // the same W rows together): at any moment the blocks read W at different
+  // With one row tile, each 512-column tile walks the hidden dimension from
+  // its own starting chunk: at any moment the blocks read W at different
   // offsets within its 8 KB rows instead of all at the same one, which
-  // spreads the stream over more HBM channels (measured: -1.6 % per
-  // generation at 128k columns).  Only the order of the hidden sum changes.
-  const int rot = (int)(((unsigned)vw * 37u) % (unsigned)n_chunks);
+  // spreads the stream over more HBM channels (measured at 128k columns:
+  // 64-row steps 253 -> 218 us).  With two row tiles the pair that shares a
+  // column tile keeps the plain order (measured faster: their W reads meet
+  // in the cache).  Only the order of the hidden sum changes.
+  const int rot = n_m == 1 ? (int)(((unsigned)vw * 37u) % (unsigned)n_chunks) : 0;
   auto issue = [&](int c, uint32_t stage) {
     const int cr = c + rot < n_chunks ? c + rot : c + rot - n_chunks;
 #pragma unroll
@@ -847,13 +848,55 @@ __device__ __attribute__((always_inline)) inline float wave_dot(const float (&hr
   return group_sum<6>(acc);
 }
 
+// Best and runner-up (rank order) of the exact logits seen, updated by value.
+struct Best2 {
+  float zb;
+  int ib;
+  float zr;
+  int ir;
+};
+__device__ __attribute__((always_inline)) inline Best2 best2_take(Best2 t, float z, int col) {
+  const bool first = ranks_before(z, col, t.zb, t.ib);
+  const bool second = !first && ranks_before(z, col, t.zr, t.ir);
+  Best2 o;
+  o.zr = first ? t.zb : (second ? z : t.zr);
+  o.ir = first ? t.ib : (second ? col : t.ir);
+  o.zb = first ? z : t.zb;
+  o.ib = first ? col : t.ib;
+  return o;
+}
+
+// Two columns at once (both rows' loads in flight together), each summed
+// exactly as wave_dot sums it.
+template <typename WT, int NIT>
+__device__ __attribute__((always_inline)) inline void wave_dot2(const float (&hr)[NIT][8], const WT* w, int c0, int c1,
+                                                                int lane, int hidden, float& z0, float& z1) {
+  const WT* row0 = w + (int64_t)c0 * hidden;
+  const WT* row1 = w + (int64_t)c1 * hidden;
+  Raw8<WT> raw0[NIT], raw1[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    raw0[j] = raw8_load(row0 + min(8 * lane + 512 * j, hidden - 8));
+    raw1[j] = raw8_load(row1 + min(8 * lane + 512 * j, hidden - 8));
+  }
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NIT; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a0 = fmaf(hr[j][e], raw8_at(raw0[j], e), a0);
+      a1 = fmaf(hr[j][e], raw8_at(raw1[j], e), a1);
+    }
+  z0 = group_sum<6>(a0);
+  z1 = group_sum<6>(a1);
+}
+
 template <typename WT, int NIT, bool kLo>
 __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) {
   constexpr bool kF32 = sizeof(WT) == 4;
-  constexpr int NB = (NIT + 3) / 4;         // 8-element pieces of h per thread (block layout)
   __shared__ float s_lse[4][2];
   __shared__ Cand s_c[4][kCand + 1];
-  __shared__ float s_red[4][kCand + 2];
+  __shared__ float s_red[4][2];
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int m = blockIdx.x;
@@ -865,20 +908,11 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   const float* hrow = a.h + (int64_t)b * a.h_stride + (int64_t)cc * g.hidden;
   const float wmax = *a.wmax;               // loaded early: used after the re-score
 
-  // thread t's piece j of h: elements [8t + 2048 j, +8) (block layout); loaded
-  // first, its latency overlaps the fold; addresses clamped, zero past the row
-  float hb[NB][8];
-  {
-    Raw8<float> raw[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) raw[j] = raw8_load(hrow + min(8 * tid + 2048 * j, g.hidden - 8));
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const bool ok = 8 * tid + 2048 * j < g.hidden;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hb[j][e] = ok ? raw8_at(raw[j], e) : 0.f;
-    }
-  }
+  // lane l's slice of h, elements [8l + 512 j, +8) in every wavefront (the
+  // layout of every exact re-score below); loaded first, its latency overlaps
+  // the fold
+  float hr[NIT][8];
+  load_h_slice<NIT>(hrow, lane, g.hidden, hr);
 
   // 1. fold the tiles: (max, sum of exp) and the kCand + 1 best entries
   __shared__ Cand s_best[kCand + 1];
@@ -1027,24 +1061,23 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   for (int k = 0; k <= kCand; ++k) { bestv[k] = s_best[k].v; besti[k] = s_best[k].i; }
   const float lm = s_m, lse = s_se;
 
-  // 2. exact fp32 logits of the candidates: every thread loads its pieces of
-  //    the kCand rows at once, then a fixed-order sum (lanes, then wavefronts)
-  float dot[kCand], hh = 0.f, dd = 0.f;
+  // 2. exact fp32 logits of the candidates: wavefront w re-scores candidates
+  //    2w and 2w + 1 (both rows' loads in flight together), in the one
+  //    summation order every exact re-score of this kernel uses, so that equal
+  //    W rows give bit-identical logits and exact ties go to the lowest index;
+  //    every wavefront also forms |h|^2 and |h - h_screen|^2 over its slices
+  static_assert(kCand == 8, "two candidates per wavefront");
+  float hh = 0.f, dd = 0.f;
   {
-    Raw8<WT> raw[NB][kCand];
+    const int ca = besti[2 * wave], cb = besti[2 * wave + 1];
+    float za, zb2;
+    wave_dot2<WT, NIT>(hr, w, (ca >= 0 && ca < g.V) ? ca : 0, (cb >= 0 && cb < g.V) ? cb : 0, lane, g.hidden, za,
+                       zb2);
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) {
-      const WT* crow = w + (int64_t)((besti[k] >= 0 && besti[k] < g.V) ? besti[k] : 0) * g.hidden;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) raw[j][k] = raw8_load(crow + min(8 * tid + 2048 * j, g.hidden - 8));
-    }
-#pragma unroll
-    for (int k = 0; k < kCand; ++k) dot[k] = 0.f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NIT; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = hb[j][e];
+        const float x = hr[j][e];
         hh = fmaf(x, x, hh);
         if constexpr (!kF32) {
           const float hi = bf16_to_f32(f32_to_bf16(x));
@@ -1052,19 +1085,13 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
           if constexpr (kLo) r -= bf16_to_f32(f32_to_bf16(r));
           dd = fmaf(r, r, dd);
         }
-#pragma unroll
-        for (int k = 0; k < kCand; ++k) dot[k] = fmaf(x, raw8_at(raw[j][k], e), dot[k]);
       }
-  }
-#pragma unroll
-  for (int k = 0; k < kCand; ++k) dot[k] = group_sum<6>(dot[k]);
-  hh = group_sum<6>(hh);
-  dd = group_sum<6>(dd);
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < kCand; ++k) s_red[wave][k] = dot[k];
-    s_red[wave][kCand] = hh;
-    s_red[wave][kCand + 1] = dd;
+    hh = group_sum<6>(hh);                   // the same in every wavefront
+    dd = group_sum<6>(dd);
+    if (lane == 0) {
+      s_red[wave][0] = za;
+      s_red[wave][1] = zb2;
+    }
   }
   __shared__ int s_rescan;
   __syncthreads();
@@ -1077,12 +1104,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   // the exact logits and bounds (the same values in every wavefront that gets here)
   float ze[kCand];
 #pragma unroll
-  for (int k = 0; k < kCand; ++k) {
-    const float z = (s_red[0][k] + s_red[1][k]) + (s_red[2][k] + s_red[3][k]);
-    ze[k] = (besti[k] >= 0 && besti[k] < g.V) ? z : kNegInf;
-  }
-  hh = (s_red[0][kCand] + s_red[1][kCand]) + (s_red[2][kCand] + s_red[3][kCand]);
-  dd = (s_red[0][kCand + 1] + s_red[1][kCand + 1]) + (s_red[2][kCand + 1] + s_red[3][kCand + 1]);
+  for (int k = 0; k < kCand; ++k) ze[k] = (besti[k] >= 0 && besti[k] < g.V) ? s_red[k / 2][k % 2] : kNegInf;
   // error bounds (rounded up by a small factor for the fp32 evaluation of the norms)
   const float hn = sqrtf(hh) * 1.0001f;
   // accumulation depth of a screened logit: sequential fp32 FMAs (fp32 screen);
@@ -1092,11 +1114,8 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   const float n_s = kF32 ? (float)g.hidden + 8.f
                          : 2.f * ((float)(g.hidden / 16) * 17.f * (kLo ? 2.f : 1.f) + 8.f + (float)a.n_split);
   const float eps_s = (sqrtf(dd) * 1.0001f + gamma_f32(n_s) * hn * 1.01f) * wmax;
-  // the re-scores: candidates and single entries take at most max(8 NB, 8 NIT)
-  // sequential FMAs per thread and 8 tree levels; whole tiles hidden / 2 FMAs
-  // per thread and one addition
-  const float eps_e = gamma_f32((float)max(8 * NB, 8 * NIT) + 8.f) * hn * wmax;
-  const float eps_f = gamma_f32((float)(g.hidden / 2) + 1.f) * hn * wmax;
+  // every re-score: 8 NIT sequential FMAs per lane and 6 tree levels (counted as 8)
+  const float eps_e = gamma_f32(8.f * NIT + 8.f) * hn * wmax;
 
   int tb = 0;                        // tracked by value: no indexing by tb
   float zbest = ze[0];
@@ -1148,17 +1167,24 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   }
 
   if (rescan) {
-    // Rare.  Every wavefront scans the tiles in order (the same values in each);
-    // wavefront 0 re-scores the single entries at or above tau one by one
-    // (wavefront dots, lane l taking elements [8l + 512j, +8)); a tile whose
-    // third entry reaches tau is re-scored whole by the block, two threads per
-    // column (elements [0, hidden/2) and [hidden/2, hidden), added in that order).
-    __shared__ Cand s_ft[4][2];
+    // Rare.  Every wavefront scans the tile records in order (the same values
+    // in each) and takes its turn at the work: the single entries at or above
+    // tau go to the wavefronts in turn (entry e to wavefront e mod 4), and the
+    // columns of a tile whose third entry reaches tau (its unseen columns may)
+    // are shared out two at a time (columns 2w, 2w + 1, 2w + 8, ... to
+    // wavefront w).  Every re-score is a wavefront dot (lane l taking elements
+    // [8l + 512j, +8), the candidates' order, so eps_e bounds it).  Each
+    // wavefront keeps its own best, runner-up and sum of exact-minus-screened
+    // terms; wavefront 0 merges them in wavefront order.
+    __shared__ Cand s_rb[4][2];
+    __shared__ double s_rx[4];
     flags |= 1;
-    float hr[NIT][8];
-    load_h_slice<NIT>(hrow, lane, g.hidden, hr);
     const float tau = zbest - eps_e - eps_s;
     float dafter = kNegInf;
+    // this wavefront's tallies: wavefront 0 starts from the candidates'
+    Best2 t2 = wave == 0 ? Best2{zbest, ibest, zrun, irun} : Best2{kNegInf, 0x7fffffff, kNegInf, 0x7fffffff};
+    double ex = wave == 0 ? extra : 0.0;
+    int turn = 0;                              // single entries seen so far (uniform)
     for (int t0 = 0; t0 < n_vt; t0 += kWave) {
       const int t = t0 + lane;
       float v[3] = {kNegInf, kNegInf, kNegInf};
@@ -1179,83 +1205,61 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
         for (int k = 0; k < kCand; ++k) is_cand = is_cand || (besti[k] == ix[q]);
         const bool want = v[q] >= tau && !is_cand && ix[q] >= 0 && ix[q] < g.V;
         if (!want && !is_cand) dafter = fmaxf(dafter, v[q]);
-        uint64_t mask = wave == 0 ? __ballot(want) : 0ull;
+        uint64_t mask = __ballot(want);       // the same in every wavefront
         while (mask) {
           const int src = __builtin_ctzll(mask);
           mask &= mask - 1;
           const int col = __shfl(ix[q], src);
           const float scr = __shfl(v[q], src);
-          const float z = wave_dot<WT, NIT>(hr, w, col, lane, g.hidden);
-          extra += exp((double)z - (double)lm) - exp((double)scr - (double)lm);
-          if (ranks_before(z, col, zbest, ibest)) {
-            zrun = zbest; irun = ibest; zbest = z; ibest = col;
-          } else if (ranks_before(z, col, zrun, irun)) {
-            zrun = z; irun = col;
+          if ((turn & 3) == wave) {
+            const float z = wave_dot<WT, NIT>(hr, w, col, lane, g.hidden);
+            ex += exp((double)z - (double)lm) - exp((double)scr - (double)lm);
+            t2 = best2_take(t2, z, col);
           }
+          ++turn;
         }
       }
-      uint64_t fmask = __ballot(full);      // the same in every wavefront
+      uint64_t fmask = __ballot(full);        // the same in every wavefront
       while (fmask) {
         flags |= 2;
-        const int tile = t0 + __builtin_ctzll(fmask);
+        const int src = __builtin_ctzll(fmask);
         fmask &= fmask - 1;
-        // block re-score of the tile's columns (their screened terms stay in
-        // the conf sum: only the decision uses them)
-        const int col = tile * tw + (tid >> 1), hf = tid & 1;
-        bool ok = (tid >> 1) < tw && col < g.V;
+        const int tile = t0 + src;
+        // the tile's three entries were re-scored above (all reach tau) or are
+        // candidates; its other columns are re-scored here, their screened
+        // terms staying in the conf sum (only the decision uses them)
+        const int e0 = __shfl(ix[0], src), e1 = __shfl(ix[1], src), e2 = __shfl(ix[2], src);
+        for (int j = 2 * wave; j < tw; j += 8) {
+          const int c0 = tile * tw + j, c1 = c0 + 1;
+          float z0, z1;
+          wave_dot2<WT, NIT>(hr, w, min(c0, g.V - 1), min(c1, g.V - 1), lane, g.hidden, z0, z1);
+          bool ok0 = c0 < g.V && c0 != e0 && c0 != e1 && c0 != e2;
+          bool ok1 = j + 1 < tw && c1 < g.V && c1 != e0 && c1 != e1 && c1 != e2;
 #pragma unroll
-        for (int k = 0; k < kCand; ++k) ok = ok && besti[k] != col;
-        float acc = 0.f;
-        if ((tid >> 1) < tw) {
-          const int half_len = g.hidden / 2;
-          const float* hp = hrow + hf * half_len;
-          const WT* wp = w + (int64_t)min(col, g.V - 1) * g.hidden + hf * half_len;
-          for (int e0 = 0; e0 < half_len; e0 += 8) {
-            Raw8<float> hx;
-            Raw8<WT> wx;
-            hx = raw8_load(hp + e0);
-            wx = raw8_load(wp + e0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(raw8_at(hx, e), raw8_at(wx, e), acc);
-          }
+          for (int k = 0; k < kCand; ++k) { ok0 = ok0 && besti[k] != c0; ok1 = ok1 && besti[k] != c1; }
+          if (ok0) t2 = best2_take(t2, z0, c0);
+          if (ok1) t2 = best2_take(t2, z1, c1);
         }
-        const float other = __shfl_xor(acc, 1);
-        float z = hf == 0 ? acc + other : other + acc;
-        float bv = ok ? z : kNegInf;
-        int bi = ok ? col : 0x7fffffff;
-        // the block's two best columns of the tile
-        float b1 = bv;
-        int i1 = bi;
-        group_argmax<6>(b1, i1);
-        const bool pop = bi == i1;
-        float b2 = pop ? kNegInf : bv;
-        int i2 = pop ? 0x7fffffff : bi;
-        group_argmax<6>(b2, i2);
-        if (lane == 0) { s_ft[wave][0] = Cand{b1, i1}; s_ft[wave][1] = Cand{b2, i2}; }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-              const float zc = s_ft[q][r].v;
-              const int cc2 = s_ft[q][r].i;
-              if (cc2 == 0x7fffffff) continue;
-              if (ranks_before(zc, cc2, zbest, ibest)) {
-                zrun = zbest; irun = ibest; zbest = zc; ibest = cc2;
-              } else if (ranks_before(zc, cc2, zrun, irun)) {
-                zrun = zc; irun = cc2;
-              }
-            }
-        }
-        __syncthreads();
       }
     }
+    if (lane == 0) {
+      s_rb[wave][0] = Cand{t2.zb, t2.ib};
+      s_rb[wave][1] = Cand{t2.zr, t2.ir};
+      s_rx[wave] = ex;
+    }
+    __syncthreads();
     if (wave != 0) return;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (s_rb[q][r].i != 0x7fffffff) t2 = best2_take(t2, s_rb[q][r].v, s_rb[q][r].i);
+      ex += s_rx[q];
+    }
+    zbest = t2.zb; ibest = t2.ib; zrun = t2.zr; irun = t2.ir; extra = ex;
     dmax = wave_max(dafter);
   }
-  const float eps_r = (flags & 2) ? fmaxf(eps_e, eps_f) : eps_e;
-  if (zrun != kNegInf && zbest - zrun <= 2.f * eps_r) flags |= 4;
+  if (zrun != kNegInf && zbest - zrun <= 2.f * eps_e) flags |= 4;
   if (dmax == kNegInf || dmax + eps_s < zbest - eps_e) flags |= 8;
 
   // 4. confidence = exp(z* - lm) / (sum of exp(z - lm)): screened terms with

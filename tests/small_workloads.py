@@ -158,3 +158,14 @@ def gpu_screen_regimes(index=120, **kw):
                 schedule="cosine", order="random", precision="bf16")
     base.update(kw)
     return Config(**base)
+
+
+# The production decision kernel's shape (hidden 4096 = 32 heads x 128) with a
+# 2048-column vocabulary (16 tiles of 128) and 32 decoded rows per step; the
+# decision tests rewrite its head so that columns tie.
+def gpu_decide_dup(index=121, **kw):
+    base = dict(name="gpu_decide_dup", index=index, batch=2, n_heads=32, n_kv_heads=8, head_dim=128,
+                vocab=2048, prompt_len=20, gen_len=48, n_registers=4, n_steps=3,
+                schedule="fixed", per_step=16, order="random", precision="bf16")
+    base.update(kw)
+    return Config(**base)

@@ -178,6 +178,7 @@ def _check_generation(cfg, wl, run):
     assert np.array_equal(seq, res.tokens), "final sequences differ"
     _say(f"  {compared} steps compared, worst abs errors: {worst}; decision counters "
          f"(re-scored beyond the candidates, whole tiles, fp32 ties): {counts}")
+    return counts
 
 
 def test_screen_regimes_match_oracle():
@@ -190,6 +191,44 @@ def test_screen_regimes_match_oracle():
     _say(f"screen regimes: {cfg.name}")
     wl, run = _runner(cfg)
     _check_generation(cfg, wl, run)
+
+
+def _tied_head(wl, kind):
+    """Rewrite the workload's bf16 vocabulary head so that exact ties defeat
+    the screen's candidates: 'whole_tiles' repeats 12 distinct rows over the
+    whole vocabulary (every 128-column tile holds ten or more copies of each,
+    so a tile's third entry ties its first); 'single_entries' copies one row,
+    scaled by 4 (exact in bf16), to column 5 of every tile (16 tied columns,
+    one per tile).  Tied columns have bit-identical exact logits on both
+    sides, so the argmax must take the lowest of their indices."""
+    w = wl.w_vocab
+    V = w.shape[0]
+    if kind == "whole_tiles":
+        w[:] = w[np.arange(V) % 12]
+    else:
+        f = (w[7].astype(np.uint32) << 16).view(np.float32) * np.float32(4.0)
+        w[5::128] = (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["whole_tiles", "single_entries"])
+def test_decision_rescans_on_tied_columns(kind):
+    """Both re-scoring paths of the decision kernel (the single entries beyond
+    the candidates, shared over the wavefronts, and whole tiles), forced by
+    tied vocabulary columns: the generation must match the oracle's, every
+    decision carrying the kernel's proof, and the kernel's counters must show
+    the path taken."""
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    from small_workloads import gpu_decide_dup
+    cfg = gpu_decide_dup()
+    _say(f"decision re-scoring on tied columns: {kind}")
+    wl = make_workload(cfg)
+    _tied_head(wl, kind)
+    run = SparseStepRunner(wl, device="cuda")
+    counts = _check_generation(cfg, wl, run)
+    if kind == "whole_tiles":
+        assert counts[1] > 0, f"no whole-tile re-scoring: {counts}"
+    else:
+        assert counts[0] > 0, f"no re-scoring beyond the candidates: {counts}"
 
 
 @pytest.mark.parametrize("cfgfn", [gpu_wide_semi_ar, gpu_wide_fixed], ids=["wide_semi_ar", "wide_fixed"])
