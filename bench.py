@@ -437,6 +437,56 @@ def block_attention_cpu_baseline(inp, budget_s):
                       f"({cfg.n_rows} rows each) in {dt:.1f} s, float64 NumPy"}
 
 
+def library_gemm_bench(args):
+    """Context for the vocabulary screen: the vendor GEMM (torch.matmul on
+    bf16 operands, bf16 out) of the workload's logits products h W^T at the
+    step sizes of its schedule, timed beside this library's whole logits call
+    (screen + split reduce + proven decision) at the same row counts, both
+    over 20 back-to-back calls between HIP events.  Not part of the product
+    path; h is seeded N(0, 1)."""
+    import torch
+    from masked_discrete_diffusion_amd import _lib as L
+    from masked_discrete_diffusion_amd.sampler import SparseStepRunner
+    from mdm_inputs import get_config, make_workload
+
+    cfg = get_config(args.workload)
+    wl = make_workload(cfg)
+    run = SparseStepRunner(wl, device="cuda:0")
+    ns = sorted({st.n_c for st in run.plan if st.n_c})
+    picks = sorted({ns[0], ns[len(ns) // 4], ns[len(ns) // 2], ns[(3 * len(ns)) // 4], ns[-1]})
+    w = torch.from_numpy(wl.w_vocab.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+    reps = 20
+
+    def timed(fn, stream):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    print(f"# {cfg.name}: logits products [M x {cfg.hidden}] x [{cfg.vocab} x {cfg.hidden}]^T")
+    print("#    M  vendor GEMM (us)  TFLOP/s   this library's logits call (us)  TFLOP/s")
+    for n_c in picks:
+        M = cfg.batch * n_c
+        h = torch.randn(M * cfg.hidden, generator=gen, device="cuda:0", dtype=torch.float32)
+        hb = h.view(M, cfg.hidden).to(torch.bfloat16)
+        t_lib = timed(lambda: torch.matmul(hb, w.t()), torch.cuda.current_stream())
+        t_own = timed(lambda: L.mdm_subset_logits_confidence(run.ctx, h, n_c * cfg.hidden, n_c, run.conf, run.token,
+                                                             None), run.stream)
+        fl = 2.0 * M * cfg.hidden * cfg.vocab
+        print(f"  {M:5d}  {t_lib:16.1f}  {fl / t_lib / 1e6:7.0f}   {t_own:31.1f}  {fl / t_own / 1e6:7.0f}",
+              flush=True)
+    L.mdm_device_status(run.ctx)
+    run.close()
+
+
 def ablation_bench(args):
     """Every setting of the speed-up switches on the workload, each timed as
     whole generations replayed from a HIP graph."""
@@ -510,6 +560,8 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="time every setting of the speed-up switches (cache prompt / cache res / truncate)")
     ap.add_argument("--ablation-steps", type=int, default=5)
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor GEMM on the workload's logits products beside the logits call")
     ap.add_argument("--pmc-summary", nargs=6, metavar="DIR",
                     help="TRACE SQ FETCH WRITE COPY_FETCH COPY_WRITE: per-kernel counter summary (stdout)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
@@ -538,6 +590,9 @@ def main():
         return
     if args.block_attention:
         block_attention_bench(args)
+        return
+    if args.library_gemm:
+        library_gemm_bench(args)
         return
     if args.ablation:
         ablation_bench(args)
