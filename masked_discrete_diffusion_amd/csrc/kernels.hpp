@@ -105,7 +105,7 @@ struct VocabArgs {
   int n_c;                  // rows per sequence
   uint16_t* hhi;            // [m_pad][hidden] bf16 workspace (bf16 mode)
   uint16_t* hlo;            // [m_pad][hidden] bf16 workspace (accurate mode), or NULL
-  float* partials;          // [m_pad][ceil(V / tile_w)][8], tile_w >= 32
+  float* partials;          // [m_pad][ceil(V / 128)][8]: one record per 128-column tile
   float* zpart;             // split partial logits [n_split][M][v_pad] (bf16 path)
   int64_t zpart_bytes;
   int v_pad;                // V rounded up to the vocab tile
@@ -132,7 +132,6 @@ struct VocabArgs {
   float* trace;
   unsigned* stats;
   int n_split;              // set by the launcher: hidden splits summed before the epilogue
-  int tile_w;               // set by the launcher: vocabulary columns per partial record
 };
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
 // max_v ||W_v||_2 of the vocabulary head, rounded up, into *out (which must hold 0)

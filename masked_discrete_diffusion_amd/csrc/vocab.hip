@@ -27,7 +27,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kKChunk = 64;        // hidden elements per LDS stage
 constexpr int kScreenTargetBlocks = 256;   // split hidden until about this many blocks
 constexpr int kSplitMaxRows = 1 << 20;     // split hidden only for steps of at most this many rows
-constexpr bool kFoldSplitsInDecide = false; // split sums: in the decision kernel, else a reduce launch
 
 // Per (row, vocabulary tile) summary of screened logits: the maximum, the sum
 // of exp(z - max) and the three best (value, index) pairs in rank order
@@ -900,7 +899,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int m = blockIdx.x;
-  const int tw = a.tile_w;                  // vocabulary columns per partial record
+  constexpr int tw = kVocabTile;            // vocabulary columns per partial record
   const int n_vt = (g.V + tw - 1) / tw;
   const float* part = a.partials + (int64_t)m * n_vt * 8;
   const WT* w = static_cast<const WT*>(a.w);
@@ -917,8 +916,7 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
   // 1. fold the tiles: (max, sum of exp) and the kCand + 1 best entries
   __shared__ Cand s_best[kCand + 1];
   __shared__ float s_m, s_se;
-  const bool fold = a.n_split > 1 && a.zpart != nullptr;   // split partial logits, not tile records
-  if (n_vt <= kWave && !fold) {
+  if (n_vt <= kWave) {
     // one tile per lane of wavefront 0: its three entries are already in rank order
     if (wave == 0) {
       const int t = min(lane, n_vt - 1);
@@ -944,54 +942,12 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
       if (lane == 0) { s_m = lm; s_se = lse; }
     }
   } else {
-    // several tiles per thread (large vocabularies), or the hidden dimension
-    // split over screen blocks: sorted insertion, then a block merge of the
-    // wavefronts' top-(kCand + 1)
+    // several tiles per thread (large vocabularies): sorted insertion, then a
+    // block merge of the wavefronts' top-(kCand + 1)
     float lm = kNegInf, lse = 0.f;
     CandList cl;
 #pragma unroll
     for (int k = 0; k < kCand; ++k) { cl.c[k].v = kNegInf; cl.c[k].i = 0x7fffffff; }
-    if (fold) {
-      // the screen's per-split partial logits of this row are summed here in
-      // split order (up to 4 splits): thread t takes 32 consecutive columns
-      // per pass, every split's loads issued before any sum; the four threads
-      // of a 128-column tile then merge their (max, sum of exp, top-3)
-      for (int c0 = 32 * tid; c0 < g.V; c0 += 32 * 256) {
-        floatx4 zp[4][8];
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
-          const floatx4* zr = reinterpret_cast<const floatx4*>(
-              a.zpart + ((int64_t)min(sp, a.n_split - 1) * M + m) * a.v_pad + c0);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) zp[sp][q] = zr[q];
-        }
-        float vals[32];
-        int idx[32];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float z = zp[0][q][e];
-#pragma unroll
-            for (int sp = 1; sp < 4; ++sp) z = sp < a.n_split ? z + zp[sp][q][e] : z;
-            const int col = c0 + 4 * q + e;
-            idx[4 * q + e] = col;
-            vals[4 * q + e] = col < g.V ? z : kNegInf;
-            if (a.logits && col < g.V) a.logits[(int64_t)m * g.V + col] = z;
-          }
-        Top3 t = summarize<32>(vals, idx);
-        t = top3_merge(t, top3_shfl_xor(t, 1));
-        t = top3_merge(t, top3_shfl_xor(t, 2));
-        if ((tid & 3) == 0) {
-          // the tile's record, for the rare re-scoring pass below
-          if (c0 < g.V) store_partial(a.partials + ((int64_t)m * n_vt + c0 / tw) * 8, t);
-          lse_merge(lm, lse, t.m, t.se);
-          cl = cand_insert(cl, t.v1, t.i1);
-          cl = cand_insert(cl, t.v2, t.i2);
-          cl = cand_insert(cl, t.v3, t.i3);
-        }
-      }
-    } else {
     // four tiles per thread and pass, every load issued before any is used
     for (int t0 = 0; t0 < n_vt; t0 += 1024) {
       floatx4 p0[4], p1[4];
@@ -1010,7 +966,6 @@ __global__ __launch_bounds__(256) void k_decide(Geometry g, VocabArgs a, int M) 
           cl = cand_insert(cl, p1[u][2], __float_as_int(p1[u][3]));
         }
       }
-    }
     }
     wave_lse(lm, lse);
 #pragma unroll
@@ -1333,7 +1288,6 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     VocabArgs da = a;
     da.n_split = 1;
-    da.tile_w = kVocabTile;
     return launch_decide<float>(g, da, M, s);
   }
   const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
@@ -1363,7 +1317,6 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     ew = hipGetLastError();
     if (ew != hipSuccess) return ew;
     pa.n_split = 1;
-    pa.tile_w = kVocabTile;
     return launch_decide<uint16_t>(g, pa, M, s);
   }
   int n_split = 1;
@@ -1391,20 +1344,17 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
 #undef MDM_SCREEN
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // split partial logits are summed in split order, by the reduce launch
-  // (whose grid spreads the sums over the vocabulary tiles) or by the
-  // decision kernel itself
-  if (n_split > 1 && !kFoldSplitsInDecide) {
+  // split partial logits are summed in split order by the reduce launch,
+  // whose grid spreads the sums over the vocabulary tiles
+  if (n_split > 1) {
     hipLaunchKernelGGL(k_screen_reduce, dim3(n_vt, (M + 31) / 32), dim3(256), 0, s, g, pa, M, n_split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     pa.n_split = n_split;              // the accumulation depth of the screened values
     pa.zpart = nullptr;                // the decision reads the reduced tile records
-    pa.tile_w = kVocabTile;
     return launch_decide<uint16_t>(g, pa, M, s);
   }
   pa.n_split = n_split;
-  pa.tile_w = kVocabTile;
   return launch_decide<uint16_t>(g, pa, M, s);
 }
 
