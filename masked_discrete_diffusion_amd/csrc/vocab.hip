@@ -27,6 +27,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kKChunk = 64;        // hidden elements per LDS stage
 constexpr int kScreenTargetBlocks = 256;   // split hidden until about this many blocks
 constexpr int kSplitMaxRows = 1 << 20;     // split hidden only for steps of at most this many rows
+constexpr int kProjWideBlocks = 192;     // projection blocks from which the wide tiles are used
 
 // Per (row, vocabulary tile) summary of screened logits: the maximum, the sum
 // of exp(z - max) and the three best (value, index) pairs in rank order
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(512) void k_screen_wide(Geometry g, VocabArgs a, in
 
   // lane holds z for row m0 + 32(rb0 + rb) + l32 and vocab v0 + 128 vg + 32 vb + 8jj + 4half + ii
   const int vt = vw * (kWideTile / kVocabTile) + vg;      // 128-column tile index
-  if (n_split > 1) {
+  if (n_split > 1 || a.emit) {
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
@@ -1389,6 +1390,19 @@ hipError_t launch_project(const Geometry& g, const ProjArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_pack, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gp, va, M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Large steps take the 512-column tiles of the wide screen (each h operand
+  // read from LDS feeds four MFMA blocks instead of one) once they alone give
+  // at least kProjWideBlocks blocks; below that the 128-column tiles keep
+  // every compute unit busy.  Same-box two-layer C3 generations: 26.1 against
+  // 26.9 ms at 192 blocks, 26.2 at 128, 27.7 at 64.
+  const int n_wide = gp.V / kWideTile;
+  if (rb == 4 && gp.V % kWideTile == 0 && n_wide * m_tiles >= kProjWideBlocks) {
+    hipLaunchKernelGGL((k_screen_wide<4, true>), dim3((unsigned)(((n_wide + 7) / 8) * 8 * m_tiles)), dim3(512), 0, s,
+                       gp, va, M, 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_rope_scatter(g, p, M, s);
+  }
   dim3 grid(p.n_pad / kVocabTile, m_tiles, 1);
   if (rb == 1) hipLaunchKernelGGL((k_screen_bf16<1, 1, true>), grid, dim3(ScreenStage<1, 1, true>::THREADS), 0, s, gp, va, M, 1);
   else if (rb == 2) hipLaunchKernelGGL((k_screen_bf16<2, 2, true>), grid, dim3(ScreenStage<2, 2, true>::THREADS), 0, s, gp, va, M, 1);

@@ -149,6 +149,18 @@ def gpu_two_layer_semi_ar(index=119, **kw):
     return gpu_small_semi_ar(index=index, **base)
 
 
+# Two layers at the production head shape (32 heads x 128, so 12288
+# projection rows = 24 tiles of 512 columns) with a 1100-token prompt: the
+# prefill projection of 1116 rows takes the projection's wide tiles (9 row
+# tiles x 24 = 216 blocks), the decode steps the 128-column tiles.
+def gpu_two_layer_wide(index=122, **kw):
+    base = dict(name="gpu_two_layer_wide", index=index, batch=1, n_heads=32, n_kv_heads=32, head_dim=128,
+                vocab=1000, prompt_len=1100, gen_len=96, n_registers=16, n_steps=3,
+                schedule="fixed", per_step=32, order="random", precision="bf16", layers=2)
+    base.update(kw)
+    return Config(**base)
+
+
 # The bf16 screen's row tilings and hidden splits on one 8192-column
 # vocabulary: a cosine schedule over 600 positions in 8 steps decodes
 # 12..117 rows per sequence, 36..351 rows per step over 3 sequences.

@@ -22,7 +22,8 @@ from mdm_inputs import make_workload
 from oracle.numerics import round_bf16, table_values
 from oracle.step import Model, SequenceOracle, run_workload
 from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_text_infill,
-                             gpu_two_layer, gpu_two_layer_semi_ar, gpu_wide_fixed, gpu_wide_semi_ar)
+                             gpu_two_layer, gpu_two_layer_semi_ar, gpu_two_layer_wide, gpu_wide_fixed,
+                             gpu_wide_semi_ar)
 from mdm_inputs import get_config
 
 pytestmark = pytest.mark.gpu
@@ -254,7 +255,8 @@ def test_text_infill_random_block_order_matches_oracle(kw):
     _check_generation(cfg, wl, run)
 
 
-@pytest.mark.parametrize("cfgfn", [gpu_two_layer, gpu_two_layer_semi_ar], ids=["fixed", "semi_ar_gqa"])
+@pytest.mark.parametrize("cfgfn", [gpu_two_layer, gpu_two_layer_semi_ar, gpu_two_layer_wide],
+                         ids=["fixed", "semi_ar_gqa", "wide_projection"])
 def test_two_layer_generation_matches_oracle(cfgfn):
     """Layer 2 projects layer 1's outputs of every query row (RoPE'd q, k and
     v rounded to bf16), keeps its own cache of the decoded rows and attends
