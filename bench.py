@@ -711,7 +711,7 @@ def main():
         p_tflops = p_flops.sum() / p_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(p_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "mdm_layer_project: k_pack + k_screen_bf16 (raw product, h hi + lo) + k_rope_scatter",
+                    "kernel": "mdm_layer_project: k_pack + k_screen_bf16 | k_screen_wide (raw product, h hi + lo) + k_rope_scatter",
                     "calls": n * n_up, "avg_call_us": round(proj_ms.mean() / n_up * 1e3, 2),
                     "algorithmic_flops_per_call": round(float(p_flops.mean() / n_up), 0),
                     "first_layer_attention": roofline}
