@@ -13,14 +13,15 @@ HIP path plays no part.  For each workload it stores, in
   margin    [B][sum n_C] top-1 minus top-2 logit (float64)
   conf_gap  [steps][B] fp32 confidence gap at the top-n cut (semi-AR only)
   o_steps   steps whose attention output rows were sampled
-  o_rows    [len(o_steps)][n_rows] sampled query-row indices (sequence 0)
-  o_vals    [len(o_steps)][n_rows][hidden] attention output (float32)
+  o_rows    [len(o_steps)][B][6] sampled query-row indices of every sequence
+  o_vals    [len(o_steps)][B][6][hidden] attention output (float32)
   top2_idx  [B][sum n_C][2] the two best vocabulary indices of every decision
   top2_val  [B][sum n_C][2] their exact (float64) logits
-  h_rows    [len(o_steps)][3] decoded-row indices (within the step's C rows of
-            sequence 0) whose h is stored
-  h_vals    [len(o_steps)][3][hidden] those rows' h (float64): the tests form
-            the exact logits h W^T and the bf16 screen's h_bf16 W^T from them
+  h_rows    [len(o_steps)][B][3] decoded-row indices (within the step's C rows
+            of every sequence) whose h is stored
+  h_vals    [len(o_steps)][B][3][hidden] those rows' h (float64): the tests
+            form the exact logits h W^T and the bf16 screen's h_bf16 W^T from
+            them
 
 With --untruncated the loop runs with truncation switched off (every masked
 position present, no registers; oracle.step.SequenceOracle.forward_untruncated)
@@ -71,14 +72,20 @@ def expected(cfg, truncate=True):
     o_rows, o_vals, h_rows, h_vals = [], [], [], []
     for k in steps:
         r = res.records[k]
-        n_d, n_c = r.d_pos[0].size, r.c_pos[0].size
-        rows = sample_rows(n_d, n_c, cfg.n_registers if truncate else 0)
-        rows = (rows + [rows[-1]] * 6)[:6]
-        o_rows.append(rows)
-        o_vals.append(r.o[0][rows].astype(np.float32))
-        hr = [0, n_c // 2, n_c - 1]
-        h_rows.append(hr)
-        h_vals.append(r.o[0][[n_d + i for i in hr]])
+        orow, oval, hrow, hval = [], [], [], []
+        for b in range(B):
+            n_d, n_c = r.d_pos[b].size, r.c_pos[b].size
+            rows = sample_rows(n_d, n_c, cfg.n_registers if truncate else 0)
+            rows = (rows + [rows[-1]] * 6)[:6]
+            orow.append(rows)
+            oval.append(r.o[b][rows].astype(np.float32))
+            hr = [0, n_c // 2, n_c - 1]
+            hrow.append(hr)
+            hval.append(r.o[b][[n_d + i for i in hr]])
+        o_rows.append(orow)
+        o_vals.append(np.stack(oval))
+        h_rows.append(hrow)
+        h_vals.append(np.stack(hval))
     out = dict(tokens=res.tokens.astype(np.int32), sel_pos=np.stack(sel_pos).astype(np.int32),
                dec_tok=np.stack(dec_tok).astype(np.int32), conf=np.stack(conf).astype(np.float32),
                margin=np.stack(margin), conf_gap=gaps, o_steps=np.array(steps, dtype=np.int32),

@@ -5,10 +5,12 @@ written by tests/golden/make_expected.py, which calls only the oracle).
 Bars:
 * every decoded token, every unmasked position and the unmask order are
   bit-exact;
-* confidences and the sampled attention-output rows are within 2e-2 relative
+* confidences and the sampled attention-output rows (six per sequence at three
+  steps) are within 2e-2 relative
   + 1e-2 absolute (bf16 path) or 1e-5 (fp32 path), and the attention rows also
   within a tight relative bound;
-* screened logits of sampled decoded rows, over the whole vocabulary, within
+* screened logits of sampled decoded rows (three per sequence at the same
+  steps), over the whole vocabulary, within
   the same bars against the oracle's logits of the same rows: the exact h W^T
   where the screen multiplies h split into bf16 hi + lo (and in fp32), else the
   product the bf16 screen approximates, bf16(h) W^T, with one bf16 ulp of room
@@ -90,32 +92,35 @@ def test_full_config_matches_oracle(cfg):
     err = np.abs(conf.astype(np.float64) - exp["conf"].astype(np.float64))
     assert np.all(err <= atol + rtol * np.abs(exp["conf"])), f"confidence error {err.max():.3g}"
 
-    # attention outputs of the sampled rows
+    # attention outputs of the sampled rows of every sequence
     worst_rel = 0.0
     for i, k in enumerate(o_steps):
-        rows = exp["o_rows"][i]
-        got = recs[k]["o"][0][rows]
-        ref = exp["o_vals"][i].astype(np.float64)
-        e = np.abs(got - ref)
-        assert np.all(e <= atol + rtol * np.abs(ref)), f"attention output at step {k}: {e.max():.3g}"
-        worst_rel = max(worst_rel, float(e.max() / np.abs(ref).max()))
+        for b in range(cfg.batch):
+            rows = exp["o_rows"][i][b]
+            got = recs[k]["o"][b][rows]
+            ref = exp["o_vals"][i][b].astype(np.float64)
+            e = np.abs(got - ref)
+            assert np.all(e <= atol + rtol * np.abs(ref)), f"attention output at step {k} seq {b}: {e.max():.3g}"
+            worst_rel = max(worst_rel, float(e.max() / np.abs(ref).max()))
     assert worst_rel <= TIGHT[cfg.precision], f"attention output relative error {worst_rel:.3g}"
 
-    # screened logits of sampled decoded rows over the whole vocabulary
+    # screened logits of sampled decoded rows of every sequence over the whole vocabulary
     worst_z = 0.0
     for i, k in enumerate(o_steps):
-        h = exp["h_vals"][i]
-        got = recs[k]["logits"][0][exp["h_rows"][i]].astype(np.float64)
-        if cfg.precision == "fp32" or accurate:
-            ref, z_atol = chunked_logits(h, wl.w_vocab), atol
-        else:
-            ref = chunked_logits(round_bf16(h), wl.w_vocab)
-            eps = TIGHT[cfg.precision] * float(np.abs(recs[k]["o"][0]).max())
-            z_atol = atol + abs_w_dot(bf16_flip_room(h, eps), wl.w_vocab)
-        e = np.abs(got - ref)
-        bad = ~(e <= z_atol + rtol * np.abs(ref))
-        assert not bad.any(), f"logits at step {k}: {int(bad.sum())} of {bad.size} outside, max {e.max():.3g}"
-        worst_z = max(worst_z, float(e.max()))
+        for b in range(cfg.batch):
+            h = exp["h_vals"][i][b]
+            got = recs[k]["logits"][b][exp["h_rows"][i][b]].astype(np.float64)
+            if cfg.precision == "fp32" or accurate:
+                ref, z_atol = chunked_logits(h, wl.w_vocab), atol
+            else:
+                ref = chunked_logits(round_bf16(h), wl.w_vocab)
+                eps = TIGHT[cfg.precision] * float(np.abs(recs[k]["o"][b]).max())
+                z_atol = atol + abs_w_dot(bf16_flip_room(h, eps), wl.w_vocab)
+            e = np.abs(got - ref)
+            bad = ~(e <= z_atol + rtol * np.abs(ref))
+            assert not bad.any(), (f"logits at step {k} seq {b}: {int(bad.sum())} of {bad.size} outside, "
+                                   f"max {e.max():.3g}")
+            worst_z = max(worst_z, float(e.max()))
 
     # per-decision certificate
     trace = np.concatenate([r["trace"] for r in recs], axis=1)            # [B][sum n_C][8]
