@@ -103,7 +103,8 @@ size_t mdm_cache_slots(const mdm_config* cfg);
 
 /* Bytes of workspace the context needs (RoPE table, the key/query/value tables of
  * the mask token and the registers, the appended rows' queries, packed h,
- * partial results).  0 if invalid. */
+ * partial results; bf16 with vocab >= 32768: a copy of w_vocab tiled for the
+ * vocabulary screen, V rounded up to 512 rows x H*d x 2 bytes).  0 if invalid. */
 size_t mdm_workspace_bytes(const mdm_config* cfg);
 
 /* Bytes per element of tables, caches and the vocab head (2 or 4).  0 if invalid. */
@@ -115,8 +116,10 @@ size_t mdm_element_bytes(const mdm_config* cfg);
  * rounded to fp32) on the host and uploads it to the workspace, clears the
  * device error flag, builds in the workspace the rows every step reuses (bf16:
  * the RoPE'd keys and queries of the mask token at every position and of the
- * registers, and their values in the layout the attention tiles read), and
- * computes the largest row norm of w_vocab (for the decisions' error bound),
+ * registers, and their values in the layout the attention tiles read; for
+ * vocab >= 32768 a copy of w_vocab in 128-row x 64-column runs, which the
+ * vocabulary screen streams), and computes the largest row norm of w_vocab
+ * (for the decisions' error bound),
  * and synchronises the stream once.  The tables tq/tk/tv and w_vocab are read
  * here and by later calls, so they must hold their final contents before init
  * and not change while the context lives.  `stream` is a hipStream_t (NULL = the default

@@ -28,11 +28,12 @@ thread_local std::string g_last_error;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-  size_t err, rope_cos, rope_sin, ktab, qtab, qbuf, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart,
+  size_t err, rope_cos, rope_sin, ktab, qtab, qbuf, mvt, rvt, apart_o, apart_ml, hhi, hlo, partials, zpart, wt,
       total;
   int ktab_rows, r_pad;
   size_t zpart_bytes;
   int m_pad, n_vt, v_pad;
+  bool wt_on;               // the tiled copy of W is kept (bf16, large vocabularies)
 };
 
 bool config_ok(const mdm_config* c, std::string* why) {
@@ -101,6 +102,9 @@ Layout layout_of(const mdm_config* c) {
   const size_t zfull = 8 * (size_t)c->batch * c->max_decode * L.v_pad * sizeof(float);
   L.zpart_bytes = bf16 ? std::min(zfull, (size_t)32 << 20) : 0;
   L.zpart = off; off = align_up(off + L.zpart_bytes, kAlign);
+  // bf16: the vocabulary head tiled for the screens' operand stream (built at init)
+  L.wt_on = bf16 && c->vocab >= kTiledWMinVocab;
+  L.wt = off; off = align_up(off + (L.wt_on ? tiled_w_elems(c->vocab, hidden) * sizeof(uint16_t) : 0), kAlign);
   L.total = off;
   return L;
 }
@@ -258,6 +262,9 @@ mdm_status mdm_sparse_step_init(mdm_ctx** out, const mdm_config* cfg, const mdm_
                                        hipMemcpyHostToDevice, ctx->stream), "upload RoPE table");
   if (st == MDM_OK) st = hip_check(ctx, launch_fill_i32(err_word(ctx), 0, 64, ctx->stream), "clear error flag");
   if (st == MDM_OK) st = hip_check(ctx, launch_row_norm_max(g, buf->w_vocab, wmax_word(ctx), ctx->stream), "vocab row norms");
+  if (st == MDM_OK && L.wt_on)
+    st = hip_check(ctx, launch_tile_w(g, buf->w_vocab, reinterpret_cast<uint16_t*>(ctx->ws() + L.wt), ctx->stream),
+                   "tiled vocabulary head");
   // The packed logits rows start at zero: rows past a step's count are read
   // by the screen (their logits are never used) and must hold finite values.
   const size_t hwords = g.fp32 ? 0 : (size_t)L.m_pad * g.hidden / 2;
@@ -382,6 +389,7 @@ VocabArgs logits_args(mdm_ctx* ctx, const float* h, int64_t h_batch_stride, int3
   a.logits = logits_or_null; a.conf = conf; a.token = token; a.m_pad = ctx->L.m_pad;
   a.zpart = reinterpret_cast<float*>(ctx->ws() + ctx->L.zpart); a.zpart_bytes = (int64_t)ctx->L.zpart_bytes;
   a.v_pad = ctx->L.v_pad;
+  if (ctx->L.wt_on) a.wt = reinterpret_cast<const uint16_t*>(ctx->ws() + ctx->L.wt);
   a.wmax = wmax_word(ctx);
   a.stats = decision_stats(ctx);
   a.trace = ctx->trace;

@@ -100,6 +100,11 @@ hipError_t launch_attention(const Geometry& g, const AttnArgs& a, hipStream_t s)
 
 struct VocabArgs {
   const void* w;            // [V][hidden] elem
+  // Optional tiled copy of a bf16 W for the wide screen's operand stream (or
+  // NULL): wt[rt][c][h][r][e] = W[128 rt + r][64 c + 32 h + e], zero past V,
+  // for rt < align_up(V, 512) / 128, so a 128-row x 32-column piece of a
+  // stage is one contiguous 8 KB run.  Every other reader uses w.
+  const uint16_t* wt;
   const float* h;           // fp32 rows: row m = (b, c) at h + b*h_stride + c*hidden
   int64_t h_stride;
   int n_c;                  // rows per sequence
@@ -136,6 +141,12 @@ struct VocabArgs {
 hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s);
 // max_v ||W_v||_2 of the vocabulary head, rounded up, into *out (which must hold 0)
 hipError_t launch_row_norm_max(const Geometry& g, const void* w, float* out, hipStream_t s);
+// The tiled copy of a bf16 W described at VocabArgs::wt (built at init).
+hipError_t launch_tile_w(const Geometry& g, const void* w, uint16_t* wt, hipStream_t s);
+inline size_t tiled_w_elems(int V, int hidden) { return ((size_t)(V + 511) / 512) * 512 * (size_t)hidden; }
+// Vocabularies from which the tiled copy is kept: where the wide screen runs
+// with a single row tile (W, not h, is the stream that bounds it).
+constexpr int kTiledWMinVocab = 32768;
 
 // Upper layers: y = h_prev W^T for every query row (h_prev fp32, split into
 // bf16 hi + lo; W bf16 [N][hidden] with N = (H + 2 H_kv) d, rows q | k | v),
