@@ -1317,10 +1317,15 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
     da.n_split = 1;
     return launch_decide<float>(g, da, M, s);
   }
-  const int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  const int n_wide = (g.V + kWideTile - 1) / kWideTile;
+  int rb = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  // hi + lo steps of 129-192 rows on a large vocabulary: three 64-row tiles
+  // (768 blocks) instead of two 128-row tiles padded to 256 rows (C5 55.9 ->
+  // 54.9 ms per generation; 64-row tiles for the 65-128 or 193-256-row steps
+  // measured slower)
+  if (a.hlo && M > 128 && M <= 192 && n_wide >= 128) rb = 2;
   const int mt_rows = 32 * rb;
   const int m_tiles = (M + mt_rows - 1) / mt_rows;
-  const int n_wide = (g.V + kWideTile - 1) / kWideTile;
   // wide vocabulary tiles when they alone give (nearly) a block per compute unit
   const bool wide = (rb == 4 || (rb == 2 && a.hlo)) && n_wide * m_tiles >= kScreenTargetBlocks * 7 / 8;
   VocabArgs pa = a;

@@ -79,6 +79,16 @@ def gpu_wide_semi_ar(index=115, **kw):
     return Config(**base)
 
 
+# Semi-AR blocks of 24 decoded 6 at a time over 8 sequences: steps of 192
+# and 144 rows take three and three 64-row tiles of the wide screen (hi + lo).
+def gpu_wide_semi_ar_192(index=123, **kw):
+    base = dict(name="gpu_wide_semi_ar_192", index=index, batch=8, n_heads=2, n_kv_heads=1, head_dim=128,
+                vocab=120000, prompt_len=24, gen_len=48, n_registers=4, n_steps=8,
+                schedule="semi_ar", block=24, steps_per_block=4, order="confidence", precision="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
 def gpu_wide_fixed(index=116, **kw):
     base = dict(name="gpu_wide_fixed", index=index, batch=8, n_heads=2, n_kv_heads=2, head_dim=128,
                 vocab=115000, prompt_len=30, gen_len=32, n_registers=4, n_steps=2,

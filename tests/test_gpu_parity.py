@@ -23,7 +23,7 @@ from oracle.numerics import round_bf16, table_values
 from oracle.step import Model, SequenceOracle, run_workload
 from small_workloads import (gpu_small_bf16, gpu_small_d128, gpu_small_fp32, gpu_small_semi_ar, gpu_text_infill,
                              gpu_two_layer, gpu_two_layer_semi_ar, gpu_two_layer_wide, gpu_wide_fixed,
-                             gpu_wide_semi_ar)
+                             gpu_wide_semi_ar, gpu_wide_semi_ar_192)
 from mdm_inputs import get_config
 
 pytestmark = pytest.mark.gpu
@@ -232,11 +232,13 @@ def test_decision_rescans_on_tied_columns(kind):
         assert counts[0] > 0, f"no re-scoring beyond the candidates: {counts}"
 
 
-@pytest.mark.parametrize("cfgfn", [gpu_wide_semi_ar, gpu_wide_fixed], ids=["wide_semi_ar", "wide_fixed"])
+@pytest.mark.parametrize("cfgfn", [gpu_wide_semi_ar, gpu_wide_semi_ar_192, gpu_wide_fixed],
+                         ids=["wide_semi_ar", "wide_semi_ar_192", "wide_fixed"])
 def test_wide_vocab_tiles_match_oracle(cfgfn):
     """Vocabularies of 115k-120k take the 512-column screen tiles (with and
-    without the hi/lo split of h, 64- and 128-row tiles); the generation must
-    match the oracle like the small workloads."""
+    without the hi/lo split of h, 64- and 128-row tiles, three 64-row tiles
+    for the 144- and 192-row hi/lo steps) streamed from the tiled copy of the
+    head; the generation must match the oracle like the small workloads."""
     cfg = cfgfn()
     _say(f"wide vocab parity: {cfg.name}")
     wl, run = _runner(cfg)
