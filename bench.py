@@ -107,8 +107,14 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """Counter-derived HBM bytes per attention call, if measured on these sources."""
+TRAFFIC_WORKLOAD = "c3_t2i_4k"     # the workload the committed counter runs measured
+
+
+def load_traffic(workload):
+    """Counter-derived HBM bytes per attention call, if measured on this
+    workload and these sources (None otherwise)."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -693,7 +699,7 @@ def main():
     mfma_tflops = a_flops.sum() / att_s / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(),
+                "traffic": None if args.layers != 1 else load_traffic(cfg.name),
                 "kernel": "mdm_step_attention: k_attn_bf16<128, pair | lag | quad> (+ k_attn_combine<128> on key-split steps)",
                 "calls": n,
                 "launches_per_event_pair": ATT_REPEAT,
@@ -726,7 +732,7 @@ def main():
                        "achieved_tflops": round(float(l_flops.sum() / l_s / 1e12), 2),
                        "achieved_gbs": round(float(l_bytes.sum() / l_s / 1e9), 1),
                        "avg_call_us": round(float(log_ms.mean() * 1e3), 2),
-                       "kernel": "mdm_subset_logits_confidence: k_screen_bf16 (+ k_screen_reduce) + k_decide"}
+                       "kernel": "mdm_subset_logits_confidence: k_screen_bf16 | k_screen_wide (+ k_screen_reduce) + k_decide"}
     both_s = att_s + log_ms.sum() / 1e3
     step_frac = (a_flops.sum() + l_flops.sum()) / both_s / 1e12 / MFMA_BF16_PEAK_TFLOPS
 
