@@ -1324,13 +1324,15 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   // 54.9 ms per generation; 64-row tiles for the 65-128 or 193-256-row steps
   // measured slower)
   if (a.hlo && M > 128 && M <= 192 && n_wide >= 128) rb = 2;
-  // bf16(h) steps of 129-256 rows below the wide regime: 64-row tiles (192-256
-  // blocks) without a hidden split, so no split-reduce launch (same box: C3
-  // 7.62 -> 7.57 and 7.90 -> 7.75, C4 6.86 -> 6.77 and 7.10 -> 6.84 ms per
-  // generation; the 65-128-row steps keep the split 128-row tiles, and
-  // extending the range to 320 or 384 rows measured slower on C3)
-  const bool tile64 = !a.hlo && M > 128 && M <= 256 && n_wide * ((M + 127) / 128) < kScreenTargetBlocks * 7 / 8;
-  if (tile64) rb = 2;
+  // bf16(h) steps of 65-256 rows below the wide regime: 32-row tiles for
+  // 65-128 rows and 64-row tiles for 129-256 rows (192-256 blocks either way)
+  // without a hidden split, so no split-reduce launch.  Same box, per
+  // generation: 129-256 rows C3 7.62 -> 7.57 and 7.90 -> 7.75, C4 6.86 ->
+  // 6.77 and 7.10 -> 6.84 ms; 65-128 rows on top C3 7.77 -> 7.73, C4 6.89 ->
+  // 6.83 ms (64-row tiles there gained less; 32-row tiles for 33-64 rows, or
+  // 64-row tiles up to 320 or 384 rows, measured no gain or slower).
+  const bool unsplit = !a.hlo && M > 64 && M <= 256 && n_wide * ((M + 127) / 128) < kScreenTargetBlocks * 7 / 8;
+  if (unsplit) rb = M <= 128 ? 1 : 2;
   const int mt_rows = 32 * rb;
   const int m_tiles = (M + mt_rows - 1) / mt_rows;
   // wide vocabulary tiles when they alone give (nearly) a block per compute unit
@@ -1360,7 +1362,7 @@ hipError_t launch_vocab(const Geometry& g, const VocabArgs& a, hipStream_t s) {
   }
   int n_split = 1;
   const int chunks = g.hidden / kKChunk;
-  while (!tile64 && n_split < 4 && M <= kSplitMaxRows && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks &&
+  while (!unsplit && n_split < 4 && M <= kSplitMaxRows && n_vt * m_tiles * n_split * 2 <= kScreenTargetBlocks &&
          chunks % (n_split * 2) == 0 &&
          (int64_t)n_split * 2 * M * pa.v_pad * 4 <= a.zpart_bytes)
     n_split *= 2;
