@@ -99,6 +99,30 @@ def logits_work(cfg, plan):
     return flops, nbytes
 
 
+def device_reference(stream):
+    """Context for the roofline fractions, measured on this device: compute
+    units and name as the runtime reports them, and the bandwidth of a plain
+    1 GiB device copy (bytes read + written over the HIP-event time of 10
+    back-to-back copies), the HBM rate an ordinary stream attains here."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            dst.copy_(src)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        t1.record(stream)
+    t1.synchronize()
+    gbs = 10 * 2 * COPY_BYTES / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    return {"name": props.name, "compute_units": props.multi_processor_count,
+            "copy_gbs": round(gbs, 1), "copy_frac_of_peak": round(gbs / HBM_PEAK_GBS, 3)}
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -761,6 +785,7 @@ def main():
                                      **({"upper_projection": round(proj_ms.sum(), 4),
                                          "upper_attention": round(up_att_ms.sum(), 4)} if cfg.layers > 1 else {})},
     }
+    out["device"] = device_reference(stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         with cpu_threads(args.cpu_threads):
